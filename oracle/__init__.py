@@ -1,0 +1,261 @@
+"""fp64 CPU oracle for attention over a paged KV cache.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import or run anything in this package; the product library never
+does.  It shares no code with the HIP path: no kernels, headers, helpers or
+tables.  It is deliberately plain and slow.
+
+What it computes, and where each step comes from:
+
+* Cache layout, block table and slot arithmetic: "AI Infra入门干货总结：大模型是
+  如何高效推理的" (github QianJinGuo/wiki), section "Paged Attention": one layer
+  is ``[2, num_blocks, block_size, num_kv_heads, head_dim]`` with K at index 0
+  and V at index 1 of the second dimension; ``block_table[r]`` lists request
+  ``r``'s physical blocks; a slot ``s`` names block ``s // block_size`` and
+  offset ``s % block_size`` inside it.
+* Q is ``[query_lens, num_heads, head_dim]``; K/V are read per request as
+  ``[seq_lens, num_kv_heads, head_dim]``; a group of query heads shares one KV
+  head by index (same page, section "LLM 推理全流程", 3. Transformer Block,
+  "Attention (FlashAttention)").
+* ``num_computed_tokens`` counts tokens already in the cache (same page,
+  section "连续批处理"), so the step's query ``i`` sits at absolute position
+  ``num_computed_tokens + i`` and, being causal, sees keys ``0 .. that position``
+  (chunked prefill is a prompt split into pieces run step by step:
+  lpnh.cn/news/2436702, section 2.3).
+* The attention itself is the plain definition printed as the naive
+  ``scaled_dot_product_attention`` in lpnh.cn/news/2669538, section 2.1:
+  ``softmax(q kᵀ · scale + mask) v`` (the page's extraction lost the ``=``
+  signs; the reading is the textbook one).  Tiling, online softmax and
+  split-KV are ways to reach this same value, so the oracle computes the value
+  directly, in float64.
+
+Every function here is pinned by tests (``tests/test_oracle.py``) to facts that
+do not come from the oracle itself: a scalar brute force over independently
+drawn contiguous K/V, PyTorch's fp64 CPU SDPA, closed forms, and hand-worked
+fixtures under ``tests/golden/``.
+"""
+from __future__ import annotations
+
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+
+# ---------------------------------------------------------------------------
+# Storage formats.
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64, exactly.
+
+    A bf16 number is the top 16 bits of an IEEE float32, so shifting the
+    pattern left by 16 gives the float32 with the same value."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_bits_to_f64(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# paged_kv_write: place each new token's K and V at its slot.
+
+def kv_write(pool: np.ndarray, k: np.ndarray, v: np.ndarray,
+             slot_mapping: np.ndarray, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Return a copy of ``pool`` with token ``t``'s K/V stored at ``slot_mapping[t]``.
+
+    ``pool``: ``[2, num_blocks, block_size, Hkv, D]``; ``k``, ``v``:
+    ``[T, Hkv, D]``.  Slot ``-1`` marks a padding token and is skipped.  The
+    stored values are the input bits unchanged (pure copy).  Slot -> (block,
+    offset) follows the page's slot formula (section "Paged Attention")."""
+    out = pool.copy()
+    num_blocks = pool.shape[1]
+    for t in range(int(slot_mapping.shape[0])):
+        s = int(slot_mapping[t])
+        if s == -1:
+            continue
+        if s < 0 or s >= num_blocks * block_size:
+            raise ValueError(f"slot {s} of token {t} is outside the pool")
+        block_idx = s // block_size
+        block_offset = s % block_size
+        out[0, block_idx, block_offset] = k[t]
+        out[1, block_idx, block_offset] = v[t]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Reading one request's K/V through its block table.
+
+def gather_kv(pool: np.ndarray, block_table_row: np.ndarray, seq_len: int,
+              dtype: str, block_size: int = BLOCK_SIZE) -> Tuple[np.ndarray, np.ndarray]:
+    """Logical ``K, V [seq_len, Hkv, D]`` (float64) of one request.
+
+    Logical token ``t`` lives in physical block ``block_table_row[t // block_size]``
+    at offset ``t % block_size`` (section "Paged Attention")."""
+    pos = np.arange(seq_len)
+    blocks = np.asarray(block_table_row)[pos // block_size]
+    offs = pos % block_size
+    K = to_f64(pool[0, blocks, offs], dtype)
+    V = to_f64(pool[1, blocks, offs], dtype)
+    return K, V
+
+
+# ---------------------------------------------------------------------------
+# Attention.
+
+def _softmax_rows(scores: np.ndarray, visible: np.ndarray) -> np.ndarray:
+    """Row softmax of ``scores`` over the ``visible`` entries (others get weight 0)."""
+    s = np.where(visible, scores, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    w = np.where(visible, np.exp(s - m), 0.0)
+    return w / w.sum(axis=-1, keepdims=True)
+
+
+def _check_request(r: int, seq_len: int, computed: int, qlen: int) -> None:
+    if qlen < 0 or seq_len != computed + qlen:
+        raise ValueError(f"request {r}: seq_len {seq_len} != computed {computed} + query {qlen}")
+
+
+def request_weights(q_rows: np.ndarray, K: np.ndarray, computed: int, scale: float,
+                    num_q_heads: int) -> np.ndarray:
+    """Softmax weights ``[ql, Hq, L]`` of one request (float64).
+
+    Query row ``i`` is at absolute position ``computed + i`` and sees keys
+    ``t <= computed + i``.  Query head ``h`` reads KV head ``h // (Hq // Hkv)``."""
+    ql = q_rows.shape[0]
+    L, Hkv, _ = K.shape
+    group = num_q_heads // Hkv
+    kv_of_head = np.arange(num_q_heads) // group
+    Kh = K[:, kv_of_head, :]                                   # [L, Hq, D]
+    scores = np.einsum("ihd,thd->iht", q_rows, Kh) * scale     # [ql, Hq, L]
+    visible = (np.arange(L)[None, :] <= (computed + np.arange(ql))[:, None])[:, None, :]
+    return _softmax_rows(scores, visible)
+
+
+def attention(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
+              seq_lens: np.ndarray, query_start_loc: np.ndarray,
+              num_computed_tokens: np.ndarray, scale: float, dtype: str,
+              requests: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Paged attention for one step, float64 ``out [T, Hq, D]``.
+
+    ``requests`` restricts the work to some requests (other rows stay NaN)."""
+    T, Hq, D = q.shape
+    Hkv = pool.shape[3]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    out = np.full((T, Hq, D), np.nan)
+    R = int(seq_lens.shape[0])
+    for r in (range(R) if requests is None else requests):
+        qs, qe = int(query_start_loc[r]), int(query_start_loc[r + 1])
+        L, c = int(seq_lens[r]), int(num_computed_tokens[r])
+        _check_request(r, L, c, qe - qs)
+        if qe == qs:
+            continue
+        K, V = gather_kv(pool, block_table[r], L, dtype)
+        qf = to_f64(q[qs:qe], dtype)
+        w = request_weights(qf, K, c, scale, Hq)               # [ql, Hq, L]
+        Vh = V[:, np.arange(Hq) // (Hq // Hkv), :]             # [L, Hq, D]
+        out[qs:qe] = np.einsum("iht,thd->ihd", w, Vh)
+    return out
+
+
+def attention_rows(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
+                   seq_lens: np.ndarray, query_start_loc: np.ndarray,
+                   num_computed_tokens: np.ndarray, scale: float, dtype: str,
+                   tokens: Sequence[int]) -> np.ndarray:
+    """``out[t]`` (all heads, float64) for the chosen token rows only."""
+    Hq = q.shape[1]
+    Hkv = pool.shape[3]
+    res = []
+    for t in tokens:
+        r = int(np.searchsorted(query_start_loc, t, side="right") - 1)
+        qs = int(query_start_loc[r])
+        L, c = int(seq_lens[r]), int(num_computed_tokens[r])
+        _check_request(r, L, c, int(query_start_loc[r + 1]) - qs)
+        p = c + (t - qs)                        # absolute position of this query
+        K, V = gather_kv(pool, block_table[r], p + 1, dtype)
+        w = request_weights(to_f64(q[t:t + 1], dtype), K, p, scale, Hq)[0]   # [Hq, p+1]
+        Vh = V[:, np.arange(Hq) // (Hq // Hkv), :]
+        res.append(np.einsum("ht,thd->hd", w, Vh))
+    return np.stack(res) if res else np.zeros((0, Hq, q.shape[2]))
+
+
+# ---------------------------------------------------------------------------
+# Split-KV (Flash-Decoding, named in lpnh.cn/news/2436702 section 6; the pages
+# give no algorithm).  Reading taken: cut the visible keys into partitions,
+# keep for each the running max m, the sum l of exp(s - m) and the
+# un-normalised o = sum exp(s - m) v, then merge with the log-sum-exp rule.
+# Online softmax (section "Attention (FlashAttention)") is what makes the
+# merge exact.
+
+def partition_state(scores: np.ndarray, values: np.ndarray) -> Tuple[float, float, np.ndarray]:
+    """(m, l, o) of one partition: scores ``[n]``, values ``[n, D]``."""
+    m = float(scores.max())
+    e = np.exp(scores - m)
+    return m, float(e.sum()), e @ values
+
+
+def merge_states(states: Sequence[Tuple[float, float, np.ndarray]]) -> np.ndarray:
+    """Attention output from partition states: sum_p e^{m_p-M} o_p / sum_p e^{m_p-M} l_p."""
+    M = max(m for m, _, _ in states)
+    num = sum(np.exp(m - M) * o for m, _, o in states)
+    den = sum(np.exp(m - M) * l for m, l, _ in states)
+    return num / den
+
+
+def split_kv_row(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                 partition: int) -> np.ndarray:
+    """One query head's output computed partition by partition and merged.
+
+    ``q_row [D]``, ``K, V [n, D]`` (the visible keys of that head's KV head)."""
+    n = K.shape[0]
+    scores = (K @ q_row) * scale
+    states = [partition_state(scores[a:a + partition], V[a:a + partition])
+              for a in range(0, n, partition)]
+    return merge_states(states)
+
+
+# ---------------------------------------------------------------------------
+# Dense brute force, for tiny inputs only: contiguous K/V, scalar loops.
+
+def dense_brute_force(q: Sequence, K: Sequence, V: Sequence, scale: float,
+                      computed: int) -> List:
+    """Scalar-loop attention of one request over contiguous K/V.
+
+    ``q[i][h][d]``, ``K[t][g][d]``, ``V[t][g][d]`` as nested sequences of
+    Python floats.  Returns ``out[i][h][d]``."""
+    import math
+    ql, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(K[0])
+    G = Hq // Hkv
+    out = []
+    for i in range(ql):
+        row = []
+        for h in range(Hq):
+            g = h // G
+            last = computed + i
+            s = []
+            for t in range(last + 1):
+                acc = 0.0
+                for d in range(D):
+                    acc += q[i][h][d] * K[t][g][d]
+                s.append(acc * scale)
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            tot = sum(e)
+            o = []
+            for d in range(D):
+                acc = 0.0
+                for t in range(last + 1):
+                    acc += e[t] * V[t][g][d]
+                o.append(acc / tot)
+            row.append(o)
+        out.append(row)
+    return out

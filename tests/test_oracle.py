@@ -1,0 +1,414 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test ties the oracle to something other than itself: hand-worked
+fixtures, a scalar brute force over independently drawn contiguous K/V,
+PyTorch's fp64 SDPA, closed forms and invariants that the definition implies.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers: place contiguous per-request K/V into a scattered pool (test-side
+# construction through the oracle's own write, then pinned separately).
+
+def _scatter_requests(rng, Ks, Vs, ctxs, Hkv, D, dtype, extra_blocks=3):
+    """Ks[r], Vs[r]: [L_r, Hkv, D] storage values. Returns pool, block_table."""
+    nblk = [(len(K) + 15) // 16 for K in Ks]
+    NB = sum(nblk) + extra_blocks
+    perm = rng.permutation(NB)
+    MB = max(nblk) + 1
+    bt = np.full((len(Ks), MB), NB - 1, dtype=np.int32)
+    store = np.uint16 if dtype == "bf16" else np.float32
+    nan = workloads.BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    pool = np.full((2, NB, 16, Hkv, D), nan, dtype=store)
+    pos = 0
+    for r, K in enumerate(Ks):
+        bt[r, : nblk[r]] = perm[pos: pos + nblk[r]]
+        pos += nblk[r]
+        L = len(K)
+        slots = np.array([bt[r, t // 16] * 16 + t % 16 for t in range(L)], dtype=np.int64)
+        pool = oracle.kv_write(pool, K, Vs[r], slots)
+    return pool, bt
+
+
+def _draw(rng, shape, dtype):
+    x = rng.standard_normal(shape).astype(np.float32)
+    return workloads.bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
+def _ragged_case(seed, dtype, Hq, Hkv, D, reqs):
+    """reqs: list of (computed, qlen). Returns dict with contiguous and paged views."""
+    rng = np.random.default_rng(seed)
+    Ks = [_draw(rng, (c + ql, Hkv, D), dtype) for c, ql in reqs]
+    Vs = [_draw(rng, (c + ql, Hkv, D), dtype) for c, ql in reqs]
+    qs = [_draw(rng, (ql, Hq, D), dtype) for c, ql in reqs]
+    pool, bt = _scatter_requests(rng, Ks, Vs, [c for c, _ in reqs], Hkv, D, dtype)
+    qsl = np.zeros(len(reqs) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum([ql for _, ql in reqs])
+    q = np.concatenate(qs) if qs else np.zeros((0, Hq, D), np.float32)
+    return dict(Ks=Ks, Vs=Vs, qs=qs, q=q, pool=pool, bt=bt, qsl=qsl,
+                nct=np.array([c for c, _ in reqs], np.int32),
+                L=np.array([c + ql for c, ql in reqs], np.int32))
+
+
+def _run(case, scale, dtype):
+    return oracle.attention(case["q"], case["pool"], case["bt"], case["L"], case["qsl"],
+                            case["nct"], scale, dtype)
+
+
+# ---------------------------------------------------------------------------
+# storage formats
+
+def test_bf16_decode_matches_torch():
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_generator_bf16_rounding_matches_torch():
+    x = np.random.default_rng(0).standard_normal(200000).astype(np.float32) * 7.0
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0]   # ties to even
+    ours = workloads.bf16_bits_from_f32(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (ours == ref).all()
+
+
+# ---------------------------------------------------------------------------
+# golden fixtures (hand-worked)
+
+def test_golden_slot_arithmetic():
+    g = json.load(open(os.path.join(GOLDEN, "slot_arithmetic.json")))
+    fo = g["flat_offsets"]
+    NB, Hkv, D = fo["num_blocks"], fo["num_kv_heads"], fo["head_dim"]
+    for c in g["slots"]:
+        pool = np.zeros((2, NB, 16, 1, 1), np.float32)
+        k = np.array([[[1.0]]], np.float32)
+        v = np.array([[[2.0]]], np.float32)
+        out = oracle.kv_write(pool, k, v, np.array([c["slot"]], np.int64))
+        assert out[0, c["block"], c["offset"], 0, 0] == 1.0
+        assert out[1, c["block"], c["offset"], 0, 0] == 2.0
+        assert np.count_nonzero(out) == 2
+    for c in fo["cases"]:
+        pool = np.zeros((2, NB, 16, Hkv, D), np.float32)
+        k = np.zeros((1, Hkv, D), np.float32)
+        v = np.zeros((1, Hkv, D), np.float32)
+        (k if c["kv"] == 0 else v)[0, c["head"], c["d"]] = 5.0
+        out = oracle.kv_write(pool, k, v, np.array([c["slot"]], np.int64))
+        assert np.flatnonzero(out.reshape(-1)).tolist() == [c["flat"]]
+
+
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "closed_forms.json")))["cases"],
+                         ids=lambda c: c["name"])
+def test_golden_closed_forms(case):
+    q = np.array(case["q"], np.float64)
+    K = np.array(case["k"], np.float64)
+    V = np.array(case["v"], np.float64)
+    ql, Hq, D = q.shape
+    L, Hkv, _ = K.shape
+    # place the L tokens in scattered blocks 3, 0 (block table [3, 0]) of a 4-block pool
+    pool = np.full((2, 4, 16, Hkv, D), np.nan)
+    bt = np.array([[3, 0]], np.int32)
+    slots = np.array([bt[0, t // 16] * 16 + t % 16 for t in range(L)], np.int64)
+    pool = oracle.kv_write(pool, K, V, slots)
+    out = oracle.attention(q.astype(np.float32), pool.astype(np.float32), bt,
+                           np.array([L], np.int32), np.array([0, ql], np.int32),
+                           np.array([case["computed"]], np.int32), case["scale"], "f32")
+    # inputs are float32-rounded, so compare at float32 input precision
+    np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=2e-6)
+    # exact fp64 check through the scalar brute force on the same values
+    bf = oracle.dense_brute_force(q.tolist(), K.tolist(), V.tolist(), case["scale"], case["computed"])
+    np.testing.assert_allclose(np.array(bf), np.array(case["out"]), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P1: dense brute force and torch SDPA
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (3, 3), (4, 1)])
+def test_matches_scalar_brute_force(dtype, Hq, Hkv):
+    reqs = [(0, 1), (5, 1), (17, 3), (0, 20), (31, 2)]
+    case = _ragged_case(11, dtype, Hq, Hkv, 8, reqs)
+    scale = 0.37
+    out = _run(case, scale, dtype)
+    for r, (c, ql) in enumerate(reqs):
+        q = oracle.to_f64(case["qs"][r], dtype).tolist()
+        K = oracle.to_f64(case["Ks"][r], dtype).tolist()
+        V = oracle.to_f64(case["Vs"][r], dtype).tolist()
+        bf = np.array(oracle.dense_brute_force(q, K, V, scale, c))
+        np.testing.assert_allclose(out[case["qsl"][r]: case["qsl"][r + 1]], bf, rtol=0, atol=1e-12)
+
+
+def test_matches_torch_sdpa_fp64():
+    reqs = [(7, 1), (0, 33), (40, 9), (100, 1)]
+    Hq, Hkv, D = 8, 2, 16
+    case = _ragged_case(5, "f32", Hq, Hkv, D, reqs)
+    scale = 1 / math.sqrt(D)
+    out = _run(case, scale, "f32")
+    for r, (c, ql) in enumerate(reqs):
+        q = torch.from_numpy(case["qs"][r].astype(np.float64)).permute(1, 0, 2)     # [Hq, ql, D]
+        K = torch.from_numpy(case["Ks"][r].astype(np.float64)).permute(1, 0, 2)     # [Hkv, L, D]
+        V = torch.from_numpy(case["Vs"][r].astype(np.float64)).permute(1, 0, 2)
+        K = K.repeat_interleave(Hq // Hkv, dim=0).contiguous()
+        V = V.repeat_interleave(Hq // Hkv, dim=0).contiguous()
+        L = c + ql
+        mask = torch.arange(L)[None, :] <= (c + torch.arange(ql))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(out[case["qsl"][r]: case["qsl"][r + 1]],
+                                   ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P2: physical block permutation invariance
+
+def test_block_permutation_invariance():
+    wl = workloads.build(workloads.small_spec("perm", 3, "bf16", 4, 2, 16,
+                                               [(40, 1), (0, 25), (70, 3)]))
+    pool = oracle.kv_write(wl.pool, wl.k_new, wl.v_new, wl.slot_mapping)
+    out = oracle.attention(wl.q, pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
+                           wl.num_computed_tokens, wl.scale, "bf16")
+    NB = pool.shape[1]
+    perm = np.random.default_rng(9).permutation(NB)
+    pool2 = np.empty_like(pool)
+    pool2[:, perm] = pool
+    bt2 = perm[wl.block_table].astype(np.int32)
+    out2 = oracle.attention(wl.q, pool2, bt2, wl.seq_lens, wl.query_start_loc,
+                            wl.num_computed_tokens, wl.scale, "bf16")
+    assert np.array_equal(out, out2)
+
+
+# ---------------------------------------------------------------------------
+# P3: softmax rows sum to one; V == 1 gives 1
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((6, 4, 8))
+    K = rng.standard_normal((30, 2, 8)) * 3
+    w = oracle.request_weights(q, K, 24, 0.9, 4)
+    np.testing.assert_allclose(w.sum(-1), 1.0, rtol=0, atol=1e-12)
+    # row i sees exactly 24 + i + 1 keys
+    for i in range(6):
+        assert np.all(w[i, :, 24 + i + 1:] == 0) and np.all(w[i, :, : 24 + i + 1] > 0)
+
+
+def test_constant_v_gives_constant_out():
+    case = _ragged_case(4, "f32", 4, 2, 8, [(9, 1), (0, 12)])
+    pool = case["pool"].copy()
+    finite = np.isfinite(pool[1])
+    pool[1][finite] = 1.0
+    case["pool"] = pool
+    out = _run(case, 0.5, "f32")
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# P4, P5: single-token context returns V; zero query averages visible V
+
+def test_single_token_context_returns_v():
+    case = _ragged_case(6, "bf16", 4, 2, 8, [(0, 1), (0, 1)])
+    out = _run(case, 0.125, "bf16")
+    for r in range(2):
+        v0 = oracle.to_f64(case["Vs"][r][0], "bf16")          # [Hkv, D]
+        assert np.array_equal(out[r], v0[np.arange(4) // 2])
+
+
+def test_zero_query_is_mean_of_visible_v():
+    reqs = [(10, 4), (3, 1)]
+    case = _ragged_case(7, "f32", 4, 2, 8, reqs)
+    case["q"] = np.zeros_like(case["q"])
+    out = _run(case, 1.0, "f32")
+    for r, (c, ql) in enumerate(reqs):
+        V = case["Vs"][r].astype(np.float64)
+        for i in range(ql):
+            mean = V[: c + i + 1].mean(axis=0)                  # [Hkv, D]
+            np.testing.assert_allclose(out[case["qsl"][r] + i], mean[np.arange(4) // 2],
+                                       rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P6, P7: decode == last prefill row; chunk-split invariance
+
+def test_decode_equals_last_prefill_row_and_chunk_invariance():
+    rng = np.random.default_rng(8)
+    Hq, Hkv, D, n = 4, 2, 8, 37
+    K = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    V = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    q = rng.standard_normal((n, Hq, D)).astype(np.float32)
+    pool, bt = _scatter_requests(rng, [K], [V], [0], Hkv, D, "f32")
+    L = np.array([n], np.int32)
+
+    def run(c, ql):
+        return oracle.attention(q[c: c + ql], pool, bt, np.array([c + ql], np.int32),
+                                np.array([0, ql], np.int32), np.array([c], np.int32), 0.3, "f32")
+
+    full = run(0, n)                       # one prefill of all n tokens
+    dec = run(n - 1, 1)                    # decode of the last token
+    np.testing.assert_allclose(dec[0], full[-1], rtol=0, atol=1e-13)
+    for k in (1, 16, 20, 36):              # split into [0,k) and [k,n)
+        a = run(0, k)
+        b = run(k, n - k)
+        np.testing.assert_allclose(np.concatenate([a, b]), full, rtol=0, atol=1e-13)
+    del L
+
+
+# ---------------------------------------------------------------------------
+# P8: split-KV merge equals the direct softmax
+
+@pytest.mark.parametrize("partition", [1, 5, 16, 512, 10000])
+def test_split_kv_merge(partition):
+    rng = np.random.default_rng(partition)
+    n, D = 1500, 16
+    K = rng.standard_normal((n, D)) * 2
+    V = rng.standard_normal((n, D))
+    q = rng.standard_normal(D)
+    s = K @ q * 0.25
+    w = np.exp(s - s.max())
+    direct = (w / w.sum()) @ V
+    got = oracle.split_kv_row(q, K, V, 0.25, partition)
+    np.testing.assert_allclose(got, direct, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P9: write round trip, sentinels untouched
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_write_round_trip(dtype):
+    wl = workloads.build(workloads.small_spec("rt", 12, dtype, 4, 2, 16,
+                                               [(0, 20), (33, 1), (5, 7), (15, 2)]))
+    pool = oracle.kv_write(wl.pool, wl.k_new, wl.v_new, wl.slot_mapping)
+    touched = np.zeros(pool.shape[1:3], bool)
+    for t, s in enumerate(wl.slot_mapping):
+        b, o = divmod(int(s), 16)
+        touched[b, o] = True
+        assert pool[0, b, o].tobytes() == wl.k_new[t].tobytes()
+        assert pool[1, b, o].tobytes() == wl.v_new[t].tobytes()
+    assert pool[:, ~touched].tobytes() == wl.pool[:, ~touched].tobytes()
+    # -1 padding tokens are skipped
+    sm = wl.slot_mapping.copy()
+    sm[::2] = -1
+    p2 = oracle.kv_write(wl.pool, wl.k_new, wl.v_new, sm)
+    for t in range(0, len(sm), 2):
+        b, o = divmod(int(wl.slot_mapping[t]), 16)
+        assert p2[:, b, o].tobytes() == wl.pool[:, b, o].tobytes()
+
+
+def test_write_rejects_out_of_pool_slot():
+    pool = np.zeros((2, 2, 16, 1, 1), np.float32)
+    kv = np.zeros((1, 1, 1), np.float32)
+    for bad in (32, -2):
+        with pytest.raises(ValueError):
+            oracle.kv_write(pool, kv, kv, np.array([bad], np.int64))
+
+
+# ---------------------------------------------------------------------------
+# P10: MHA and MQA reduce to textbook per-head attention
+
+@pytest.mark.parametrize("Hkv", [4, 1])
+def test_mha_and_mqa(Hkv):
+    Hq, D, c, ql = 4, 8, 6, 3
+    case = _ragged_case(13, "f32", Hq, Hkv, D, [(c, ql)])
+    out = _run(case, 0.5, "f32")
+    K = case["Ks"][0].astype(np.float64)
+    V = case["Vs"][0].astype(np.float64)
+    q = case["qs"][0].astype(np.float64)
+    for h in range(Hq):
+        g = h if Hkv == Hq else 0
+        S = q[:, h] @ K[:, g].T * 0.5                                    # [ql, L]
+        S = S + np.where(np.arange(c + ql)[None] <= (c + np.arange(ql))[:, None], 0, -np.inf)
+        P = np.exp(S - S.max(1, keepdims=True))
+        P /= P.sum(1, keepdims=True)
+        np.testing.assert_allclose(out[:, h], P @ V[:, g], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P11: request order invariance; empty requests
+
+def test_request_order_invariance_and_empty_requests():
+    reqs = [(3, 2), (0, 1), (20, 5), (8, 0), (47, 1)]
+    case = _ragged_case(14, "f32", 4, 2, 8, reqs)
+    out = _run(case, 0.4, "f32")
+    order = [4, 3, 0, 2, 1]
+    qs = [case["qs"][r] for r in order]
+    qsl = np.zeros(len(order) + 1, np.int32)
+    qsl[1:] = np.cumsum([reqs[r][1] for r in order])
+    out2 = oracle.attention(np.concatenate(qs), case["pool"], case["bt"][order],
+                            case["L"][order], qsl, case["nct"][order], 0.4, "f32")
+    for j, r in enumerate(order):
+        assert np.array_equal(out2[qsl[j]: qsl[j + 1]],
+                              out[case["qsl"][r]: case["qsl"][r + 1]])
+
+
+def test_rejects_inconsistent_metadata():
+    case = _ragged_case(15, "f32", 2, 1, 4, [(3, 2)])
+    with pytest.raises(ValueError):
+        oracle.attention(case["q"], case["pool"], case["bt"], case["L"] + 1, case["qsl"],
+                         case["nct"], 1.0, "f32")
+
+
+def test_rows_agree_with_full():
+    wl = workloads.build(workloads.small_spec("rows", 16, "bf16", 8, 2, 16,
+                                               [(30, 1), (0, 18), (50, 6)]))
+    pool = oracle.kv_write(wl.pool, wl.k_new, wl.v_new, wl.slot_mapping)
+    args = (wl.q, pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
+            wl.num_computed_tokens, wl.scale, "bf16")
+    full = oracle.attention(*args)
+    rows = [0, 1, 5, 18, 19, 24]
+    np.testing.assert_allclose(oracle.attention_rows(*args, tokens=rows), full[rows],
+                               rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes in a copy of the oracle are caught by the pins above.
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    reqs = [(5, 1), (0, 6)]
+    case = _ragged_case(17, "f32", 4, 2, 8, reqs)
+
+    def brute(r):
+        return np.array(oracle.dense_brute_force(
+            case["qs"][r].astype(np.float64).tolist(), case["Ks"][r].astype(np.float64).tolist(),
+            case["Vs"][r].astype(np.float64).tolist(), 0.5, reqs[r][0]))
+
+    good = _run(case, 0.5, "f32")
+    np.testing.assert_allclose(good[1:7], brute(1), atol=1e-12)
+
+    # (a) GQA mapping by modulo instead of by group
+    orig = oracle.request_weights
+
+    def wrong_gqa(q_rows, K, computed, scale, num_q_heads):
+        return orig(q_rows, K[:, ::-1], computed, scale, num_q_heads)
+    monkeypatch.setattr(oracle, "request_weights", wrong_gqa)
+    bad = _run(case, 0.5, "f32")
+    assert not np.allclose(bad[1:7], brute(1), atol=1e-6)
+    monkeypatch.undo()
+
+    # (b) causal window off by one
+    def wrong_mask(q_rows, K, computed, scale, num_q_heads):
+        return orig(q_rows, K, computed - 1, scale, num_q_heads)
+    monkeypatch.setattr(oracle, "request_weights", wrong_mask)
+    with np.errstate(invalid="ignore"):
+        bad = _run(case, 0.5, "f32")
+    assert not np.allclose(bad[1:7], brute(1), atol=1e-6, equal_nan=False)
+    monkeypatch.undo()
+
+    # (c) block offset taken from the wrong end of the slot
+    orig_gather = oracle.gather_kv
+
+    def wrong_gather(pool, row, L, dtype, block_size=16):
+        K, V = orig_gather(pool, row, L, dtype, block_size)
+        return K, V[::-1].copy()
+    monkeypatch.setattr(oracle, "gather_kv", wrong_gather)
+    bad = _run(case, 0.5, "f32")
+    assert not np.allclose(bad[1:7], brute(1), atol=1e-6)
