@@ -1,0 +1,218 @@
+/*
+ * paged_kv.h — C ABI of libpagedkv: attention over a paged KV cache for one
+ * continuous-batching step, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what the calls compute (cited by page title and section):
+ *  - "AI Infra入门干货总结：大模型是如何高效推理的", section "Paged Attention":
+ *    the cache layout [num_layers, 2, num_blocks, block_size, num_kv_heads,
+ *    head_dim], the per-request block_table [max_num_reqs,
+ *    max_num_blocks_per_req] of physical block ids, and slot_mapping, which
+ *    tells the kernel where to store each new token's K/V, with
+ *    slot = block * block_size + offset.
+ *  - Same page, section "连续批处理 (Continuous Batching)": num_computed_tokens
+ *    counts the tokens of a request already in the cache.
+ *  - Same page, section "LLM 推理全流程", "Attention (FlashAttention)": Q is
+ *    [query_lens, num_heads, head_dim], K/V are read from the paged cache as
+ *    [seq_lens, num_kv_heads, head_dim], and a group of query heads shares one
+ *    KV head by index (GQA); attention is computed tile by tile with an online
+ *    softmax.
+ *  - lpnh.cn/news/2669538, section 2.1: attention is
+ *    softmax(q k^T * scale + mask) v.
+ *
+ * Conventions shared by every call:
+ *  - block_size is fixed at 16 tokens.
+ *  - Element types: PKV_F32 (IEEE float32) or PKV_BF16 (bfloat16). q, k, v,
+ *    the cache and out all use the same type.
+ *  - One layer of the cache is passed: kv_cache_layer points at
+ *    [2][num_blocks][16][num_kv_heads][head_dim] elements (K at index 0, V at
+ *    index 1), row-major, contiguous.
+ *  - All array arguments are DEVICE pointers owned by the caller, except where
+ *    a call says "host".  Tensors must be contiguous; q, k, v, out and the
+ *    cache must be 16-byte aligned.
+ *  - head_dim must be 64 or 128; num_q_heads must be a multiple of
+ *    num_kv_heads with num_q_heads / num_kv_heads <= 16.
+ *  - stream is a hipStream_t (NULL = the legacy default stream).  Work is only
+ *    enqueued: the calls return before the GPU finishes, never synchronise,
+ *    never allocate and never free.  The caller keeps every buffer alive until
+ *    the stream reaches that point.
+ *  - The calls keep no global mutable state and may be made from several host
+ *    threads at once.  Two calls that share a workspace must be ordered on one
+ *    stream.
+ *  - Errors are returned as a pkv_status, never thrown.  Argument errors are
+ *    detected on the host before anything is enqueued.  Bad *contents* of
+ *    device metadata (inconsistent lengths, out-of-range block ids or slots)
+ *    are detected on the device: the affected output rows are written as NaN
+ *    (cache writes are skipped) and a bit is set in a device error word that
+ *    pkv_read_device_error() returns.
+ */
+#ifndef PAGED_KV_H_
+#define PAGED_KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_SIZE 16
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,       /* a required pointer is NULL */
+  PKV_ERR_DIMS = 2,       /* a size is negative, zero where it may not be, or unsupported */
+  PKV_ERR_DTYPE = 3,      /* dtype is not a pkv_dtype */
+  PKV_ERR_WORKSPACE = 4,  /* workspace smaller than paged_attention_workspace_size() */
+  PKV_ERR_LAUNCH = 5,     /* the HIP runtime refused a launch (see pkv_last_error_detail) */
+  PKV_ERR_METADATA = 6,   /* host validator: metadata contents are inconsistent */
+  PKV_ERR_ALIGN = 7       /* a pointer is not 16-byte aligned */
+} pkv_status;
+
+/* Bits of the device error word. */
+#define PKV_DEVERR_SEQ_LEN     0x1  /* seq_lens[r] != num_computed_tokens[r] + query_len, or a length < 0 */
+#define PKV_DEVERR_LIMITS      0x2  /* query_len > max_query_len, seq_len > max_seq_len, or
+                                       seq_len > 16 * max_blocks_per_req */
+#define PKV_DEVERR_QSL         0x4  /* query_start_loc not non-decreasing from 0, or past num_tokens */
+#define PKV_DEVERR_BLOCK_ID    0x8  /* a block_table entry read is outside [0, num_blocks) */
+#define PKV_DEVERR_SLOT        0x10 /* a slot_mapping entry is < -1 or >= 16 * num_blocks */
+#define PKV_DEVERR_CAPACITY    0x20 /* the workspace was too small for this step's split-KV partials */
+
+/*
+ * paged_kv_write — store the step's new K/V in the cache (a "slot_mapping"
+ * scatter: "AI Infra入门干货总结", section "Paged Attention").
+ *
+ *   k, v            device, [num_tokens][num_kv_heads][head_dim], dtype.
+ *   slot_mapping    device, int64 [num_tokens].  Token t goes to block
+ *                   slot / 16, offset slot % 16.  -1 marks a padding token,
+ *                   which is skipped.  Any other value outside
+ *                   [0, 16 * num_blocks) is skipped and sets PKV_DEVERR_SLOT.
+ *                   Two tokens must not share a slot (the result would be
+ *                   either token's data).
+ *   kv_cache_layer  device, [2][num_blocks][16][num_kv_heads][head_dim], dtype.
+ *                   Only the addressed slots change; the bits are copied
+ *                   unchanged.
+ *   device_error    device int32, or NULL.  When non-NULL, PKV_DEVERR_SLOT is
+ *                   OR-ed into it on a bad slot.
+ *   num_tokens      >= 0 (0 enqueues nothing).
+ * Returns PKV_OK or an argument error.
+ */
+int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+                   void* kv_cache_layer, int64_t num_tokens, int32_t num_blocks,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   int32_t* device_error, void* stream);
+
+/*
+ * paged_attention — attention of one step's query tokens over the paged cache.
+ *
+ * Request r owns query rows [query_start_loc[r], query_start_loc[r+1]) of q
+ * and out.  Its query_len = query_start_loc[r+1] - query_start_loc[r] may be
+ * 0 (nothing is computed), 1 (a decode) or more (a prefill chunk).  Its
+ * seq_len must equal num_computed_tokens[r] + query_len: the step's new
+ * tokens are already in the cache (paged_kv_write runs first on the same
+ * stream).  Query row i of the request sits at absolute position
+ * num_computed_tokens[r] + i and attends to the request's cached tokens
+ * 0 .. that position (causal within the chunk, full over the cached prefix).
+ * Token t of the request is read from physical block block_table[r][t / 16],
+ * offset t % 16.  Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ *   out                  device, [num_tokens][num_q_heads][head_dim], dtype (written).
+ *                        Rows past query_start_loc[num_reqs] are not written.
+ *   q                    device, [num_tokens][num_q_heads][head_dim], dtype.
+ *   kv_cache_layer       device, [2][num_blocks][16][num_kv_heads][head_dim], dtype.
+ *   block_table          device, int32 [num_reqs][max_blocks_per_req].  Only the
+ *                        first ceil(seq_len / 16) entries of a row are read.
+ *   seq_lens             device, int32 [num_reqs].
+ *   query_start_loc      device, int32 [num_reqs + 1], non-decreasing, [0] == 0,
+ *                        [num_reqs] <= num_tokens.
+ *   num_computed_tokens  device, int32 [num_reqs].
+ *   scale                multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
+ *   max_query_len        host bound on every query_len (sizes the prefill grid).
+ *   max_seq_len          host bound on every seq_len (sizes the split-KV grid).
+ *   workspace            device scratch of workspace_bytes >=
+ *                        paged_attention_workspace_size(...) bytes, 256-byte
+ *                        aligned.  Holds the device error word (cleared by each
+ *                        call), work lists and split-KV partials.
+ * Slots of the cache that no request reads (the tail of a request's last
+ * block, unused blocks) may hold anything, NaN included; they never reach out.
+ * Results are deterministic: the same inputs give the same bits, whatever the
+ * other requests of the batch and their order.
+ * Returns PKV_OK or an argument error.
+ */
+int paged_attention(void* out, const void* q, const void* kv_cache_layer,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                    float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                    int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_profiled — paged_attention, plus hipEvent_t records around
+ * each internal phase, for measurement tools that time a kernel on the
+ * library's own stream.  phase_events points at 2 * PKV_NUM_PHASES event
+ * handles (hipEvent_t, created by the caller; any entry may be NULL):
+ * entry 2*p is recorded just before phase p is enqueued and 2*p+1 just after.
+ * A phase that has no work for the step still records both events.  The
+ * computation and its results are exactly those of paged_attention.
+ */
+#define PKV_PHASE_PLAN 0     /* metadata checks and work lists */
+#define PKV_PHASE_PREFILL 1  /* causal chunked prefill (bf16 MFMA) */
+#define PKV_PHASE_ROWS 2     /* decode rows and split-KV partitions */
+#define PKV_PHASE_REDUCE 3   /* split-KV merge */
+#define PKV_NUM_PHASES 4
+int paged_attention_profiled(void* out, const void* q, const void* kv_cache_layer,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                             float scale, int32_t num_reqs, int64_t num_tokens,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t num_blocks, int32_t max_blocks_per_req,
+                             int32_t max_query_len, int32_t max_seq_len, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* phase_events);
+
+/*
+ * paged_attention_workspace_size — bytes of workspace paged_attention needs
+ * for these bounds (same meaning as its arguments).  Returns 0 for invalid
+ * sizes.  Pure host function.
+ */
+size_t paged_attention_workspace_size(int32_t num_reqs, int64_t num_tokens,
+                                      int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_query_len, int32_t max_seq_len);
+
+/*
+ * pkv_read_device_error — wait for `stream`, then return the device error word
+ * of the last paged_attention call that used `workspace` (0 = no error, else
+ * PKV_DEVERR_* bits), or -1 if the copy failed.  This call synchronises.
+ */
+int32_t pkv_read_device_error(const void* workspace, void* stream);
+
+/*
+ * pkv_validate_metadata_host — check a step's metadata on the host, with no
+ * HIP call.  All pointers are HOST arrays with the shapes paged_attention
+ * uses; slot_mapping (int64 [num_tokens]) may be NULL.  Checks the
+ * query_start_loc, seq_len and limit rules, that every block id a request
+ * reads is in [0, num_blocks), that every slot is -1 or in
+ * [0, 16 * num_blocks), and that no two tokens share a slot.
+ * Returns PKV_OK or PKV_ERR_METADATA / PKV_ERR_NULL / PKV_ERR_DIMS
+ * (pkv_last_error_detail() says which request or token).
+ */
+int pkv_validate_metadata_host(const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* query_start_loc,
+                               const int32_t* num_computed_tokens, const int64_t* slot_mapping,
+                               int32_t num_reqs, int64_t num_tokens, int32_t num_blocks,
+                               int32_t max_blocks_per_req, int32_t max_query_len,
+                               int32_t max_seq_len);
+
+/* Static text of a pkv_status. */
+const char* pkv_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* pkv_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H_ */

@@ -1,0 +1,58 @@
+// paged_kv_write: store each new token's K and V rows at its slot.
+//
+// "AI Infra入门干货总结：大模型是如何高效推理的", section "Paged Attention":
+// slot_mapping tells the kernel which slot a new token's K/V goes to, and a
+// slot names block slot / block_size, offset slot % block_size.  Inside a
+// block the layout is [block_size][num_kv_heads][head_dim], so the slot
+// index, taken as a row number of the [num_blocks * 16] row array of one
+// half (K or V), addresses the token's whole [num_kv_heads][head_dim] row.
+//
+// One thread moves one 16-byte chunk; consecutive threads move consecutive
+// chunks of a token row, so both the read of k/v and the write into the
+// cache are fully coalesced.  The copy is bit-exact.
+#include "pkv_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+__global__ __launch_bounds__(256) void kv_write_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    const int64_t* __restrict__ slot_mapping, u32x4* __restrict__ cache,
+    int64_t num_tokens, int64_t num_slots, int32_t chunks_per_row,
+    int32_t* __restrict__ device_error) {
+  const int64_t per_token = 2 * (int64_t)chunks_per_row;
+  const int64_t total = num_tokens * per_token;
+  const int64_t half = num_slots * chunks_per_row;  // chunks in the K half
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / per_token;
+    const int32_t rem = (int32_t)(i - t * per_token);
+    const int32_t kv = rem >= chunks_per_row;
+    const int32_t ch = rem - kv * chunks_per_row;
+    const int64_t slot = slot_mapping[t];
+    if (slot == -1) continue;  // padding token
+    if (slot < 0 || slot >= num_slots) {
+      if (device_error != nullptr && ch == 0 && kv == 0) atomicOr(device_error, PKV_DEVERR_SLOT);
+      continue;
+    }
+    const u32x4* src = kv ? v : k;
+    cache[kv * half + slot * chunks_per_row + ch] = src[t * chunks_per_row + ch];
+  }
+}
+
+int launch_kv_write(const void* k, const void* v, const int64_t* slot_mapping, void* cache,
+                    int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
+                    hipStream_t stream) {
+  if (num_tokens == 0) return 0;
+  const int32_t chunks = num_kv_heads * head_dim * elem_bytes / 16;
+  const int64_t total = num_tokens * 2 * chunks;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)cache,
+                     num_tokens, (int64_t)num_blocks * kBlock, chunks, device_error);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace pkv

@@ -1,0 +1,344 @@
+// Host side of libpagedkv: the extern "C" entry points declared in
+// include/paged_kv.h.  Arguments are checked here before anything is
+// enqueued; the kernels are launched on the caller's stream with no
+// allocation and no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "pkv_common.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int status, const char* fmt, long long a = 0, long long b = 0, long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), fmt, a, b, c);
+  g_detail = buf;
+  return status;
+}
+
+int ok() {
+  g_detail.clear();
+  return PKV_OK;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : dtype == PKV_F32 ? 4 : 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Compute units of the current device, cached per device id.
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool prefill_on_mfma(int32_t dtype) { return false && dtype == PKV_BF16; }
+
+int64_t tile_rows_for(int32_t dtype, int32_t group) {
+  return prefill_on_mfma(dtype) ? pkv::prefill_tile_rows(group) : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null pointer argument";
+    case PKV_ERR_DIMS: return "invalid or unsupported size";
+    case PKV_ERR_DTYPE: return "unsupported dtype";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_METADATA: return "inconsistent metadata";
+    case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_last_error_detail(void) { return g_detail.c_str(); }
+
+int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+                   void* kv_cache_layer, int64_t num_tokens, int32_t num_blocks,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   int32_t* device_error, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
+  if (num_tokens < 0) return fail(PKV_ERR_DIMS, "num_tokens %lld < 0", num_tokens);
+  if (num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_DIMS, "num_blocks %lld, num_kv_heads %lld", num_blocks, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_DIMS, "head_dim %lld not 64/128", head_dim);
+  if (kv_cache_layer == nullptr) return fail(PKV_ERR_NULL, "kv_cache_layer is NULL");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping) return fail(PKV_ERR_NULL, "k, v or slot_mapping is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kv_cache_layer, 16) || !aligned(slot_mapping, 8))
+    return fail(PKV_ERR_ALIGN, "k, v, cache must be 16-byte aligned, slot_mapping 8-byte");
+  if (pkv::launch_kv_write(k, v, slot_mapping, kv_cache_layer, num_tokens, num_blocks, num_kv_heads,
+                           head_dim, eb, device_error, (hipStream_t)stream))
+    return fail(PKV_ERR_LAUNCH, "kv_write launch: %lld", (long long)hipGetLastError());
+  return ok();
+}
+
+static size_t workspace_size_tiles(int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                                         int32_t head_dim, int32_t max_query_len,
+                                         int32_t max_seq_len, int64_t tile_rows) {
+  if (num_reqs < 0 || num_tokens < 0 || num_q_heads <= 0 || head_dim <= 0 || max_query_len < 0 ||
+      max_seq_len < 0)
+    return 0;
+  return pkv::ws_layout(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len, max_seq_len,
+                        tile_rows)
+      .total;
+}
+
+size_t paged_attention_workspace_size(int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                                      int32_t head_dim, int32_t max_query_len,
+                                      int32_t max_seq_len) {
+  // Tile count bound with one-row tiles covers every prefill tiling.
+  return workspace_size_tiles(num_reqs, num_tokens, num_q_heads, head_dim,
+                                           max_query_len, max_seq_len, 1);
+}
+
+static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                          float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                          int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                          int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* phase_events) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
+  if (num_reqs < 0 || num_tokens < 0)
+    return fail(PKV_ERR_DIMS, "num_reqs %lld, num_tokens %lld", num_reqs, num_tokens);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      num_q_heads / num_kv_heads > 16)
+    return fail(PKV_ERR_DIMS, "num_q_heads %lld / num_kv_heads %lld", num_q_heads, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_DIMS, "head_dim %lld not 64/128", head_dim);
+  if (num_blocks <= 0 || max_blocks_per_req <= 0 || max_query_len < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_DIMS, "num_blocks %lld, max_blocks_per_req %lld, limits", num_blocks,
+                max_blocks_per_req);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_DIMS, "scale is not finite");
+  if (!out && num_tokens > 0) return fail(PKV_ERR_NULL, "out is NULL");
+  if (!q && num_tokens > 0) return fail(PKV_ERR_NULL, "q is NULL");
+  if (!kv_cache_layer || !workspace || !query_start_loc)
+    return fail(PKV_ERR_NULL, "kv_cache_layer, workspace or query_start_loc is NULL");
+  if (num_reqs > 0 && (!block_table || !seq_lens || !num_computed_tokens))
+    return fail(PKV_ERR_NULL, "block_table, seq_lens or num_computed_tokens is NULL");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(kv_cache_layer, 16) ||
+      !aligned(workspace, 256))
+    return fail(PKV_ERR_ALIGN, "out, q, cache need 16-byte alignment, workspace 256-byte");
+  if ((int64_t)num_blocks * pkv::kBlock * num_kv_heads * head_dim * eb > (int64_t)1 << 46)
+    return fail(PKV_ERR_DIMS, "cache too large");
+
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t tile_rows = tile_rows_for(dtype, group);
+  const pkv::WsLayout ws =
+      pkv::ws_layout(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len, max_seq_len, tile_rows);
+  if (workspace_bytes < ws.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace %lld bytes < %lld needed", (long long)workspace_bytes,
+                (long long)ws.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int phase, int end) {
+    if (phase_events && phase_events[2 * phase + end])
+      (void)hipEventRecord((hipEvent_t)phase_events[2 * phase + end], s);
+  };
+  char* wsb = (char*)workspace;
+  int32_t* hdr = (int32_t*)wsb;
+
+  pkv::PlanParams pp{};
+  pp.qsl = query_start_loc;
+  pp.seq_lens = seq_lens;
+  pp.nct = num_computed_tokens;
+  pp.num_reqs = num_reqs;
+  pp.num_tokens = num_tokens;
+  pp.max_query_len = max_query_len;
+  pp.max_seq_len = max_seq_len;
+  pp.max_blocks_per_req = max_blocks_per_req;
+  pp.split_decode = 1;
+  pp.mfma_prefill = prefill_on_mfma(dtype) ? 1 : 0;
+  pp.prefill_tile_rows = (int32_t)tile_rows;
+  pp.hdr = hdr;
+  pp.row_items = (int4*)(wsb + ws.row_items);
+  pp.prefill_items = (int4*)(wsb + ws.prefill_items);
+  pp.reduce_items = (int4*)(wsb + ws.reduce_items);
+  pp.cap_row_items = ws.cap_row_items;
+  pp.cap_prefill_items = ws.cap_prefill_items;
+  pp.cap_reduce = ws.cap_reduce;
+  pp.cap_slots = ws.cap_slots;
+  mark(PKV_PHASE_PLAN, 0);
+  if (pkv::launch_plan(pp, s)) return fail(PKV_ERR_LAUNCH, "plan launch failed");
+  mark(PKV_PHASE_PLAN, 1);
+
+  const int cus = num_cus();
+  const float scale_log2 = scale * 1.4426950408889634f;
+  mark(PKV_PHASE_PREFILL, 0);
+  if (pp.mfma_prefill && max_query_len > 1) {
+    pkv::PrefillParams fp{};
+    fp.out = out;
+    fp.q = q;
+    fp.cache = kv_cache_layer;
+    fp.block_table = block_table;
+    fp.qsl = query_start_loc;
+    fp.nct = num_computed_tokens;
+    fp.items = pp.prefill_items;
+    fp.hdr = hdr;
+    fp.err = hdr + pkv::kHdrError;
+    fp.scale_log2 = scale_log2;
+    fp.num_q_heads = num_q_heads;
+    fp.num_kv_heads = num_kv_heads;
+    fp.group = group;
+    fp.num_blocks = num_blocks;
+    fp.max_blocks_per_req = max_blocks_per_req;
+    const int64_t bound = ws.cap_prefill_items * num_kv_heads;
+    const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 16);
+    if (pkv::launch_prefill(fp, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "prefill launch failed");
+  }
+
+  mark(PKV_PHASE_PREFILL, 1);
+  pkv::RowParams rp{};
+  rp.out = out;
+  rp.q = q;
+  rp.cache = kv_cache_layer;
+  rp.block_table = block_table;
+  rp.qsl = query_start_loc;
+  rp.nct = num_computed_tokens;
+  rp.items = pp.row_items;
+  rp.hdr = hdr;
+  rp.part_o = (float*)(wsb + ws.part_o);
+  rp.part_ml = (float2*)(wsb + ws.part_ml);
+  rp.err = hdr + pkv::kHdrError;
+  rp.scale_log2 = scale_log2;
+  rp.num_q_heads = num_q_heads;
+  rp.num_kv_heads = num_kv_heads;
+  rp.group = group;
+  rp.head_groups = (group + pkv::kMaxGroupRegs - 1) / pkv::kMaxGroupRegs;
+  rp.num_blocks = num_blocks;
+  rp.max_blocks_per_req = max_blocks_per_req;
+  {
+    const int64_t bound = ws.cap_row_items * num_kv_heads * rp.head_groups;
+    const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 8);
+    mark(PKV_PHASE_ROWS, 0);
+    if (pkv::launch_rows(rp, dtype, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "row launch failed");
+    mark(PKV_PHASE_ROWS, 1);
+  }
+  mark(PKV_PHASE_REDUCE, 0);
+  if (max_seq_len > pkv::kSplitTokens) {
+    pkv::ReduceParams rd{};
+    rd.out = out;
+    rd.items = pp.reduce_items;
+    rd.hdr = hdr;
+    rd.part_o = rp.part_o;
+    rd.part_ml = rp.part_ml;
+    rd.num_q_heads = num_q_heads;
+    const int64_t bound = (ws.cap_reduce * num_q_heads + 3) / 4;
+    const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 8);
+    if (pkv::launch_reduce(rd, dtype, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "reduce launch failed");
+  }
+  mark(PKV_PHASE_REDUCE, 1);
+  return ok();
+}
+
+int paged_attention(void* out, const void* q, const void* kv_cache_layer,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                    float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                    int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(out, q, kv_cache_layer, block_table, seq_lens, query_start_loc,
+                        num_computed_tokens, scale, num_reqs, num_tokens, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, max_blocks_per_req, max_query_len, max_seq_len, dtype,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int paged_attention_profiled(void* out, const void* q, const void* kv_cache_layer,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                             float scale, int32_t num_reqs, int64_t num_tokens,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t num_blocks, int32_t max_blocks_per_req,
+                             int32_t max_query_len, int32_t max_seq_len, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* phase_events) {
+  return attention_impl(out, q, kv_cache_layer, block_table, seq_lens, query_start_loc,
+                        num_computed_tokens, scale, num_reqs, num_tokens, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, max_blocks_per_req, max_query_len, max_seq_len, dtype,
+                        workspace, workspace_bytes, stream, phase_events);
+}
+
+int32_t pkv_read_device_error(const void* workspace, void* stream) {
+  if (!workspace) return -1;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return -1;
+  int32_t e = 0;
+  if (hipMemcpy(&e, workspace, sizeof(e), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  return e;
+}
+
+int pkv_validate_metadata_host(const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* query_start_loc,
+                               const int32_t* num_computed_tokens, const int64_t* slot_mapping,
+                               int32_t num_reqs, int64_t num_tokens, int32_t num_blocks,
+                               int32_t max_blocks_per_req, int32_t max_query_len,
+                               int32_t max_seq_len) {
+  if (num_reqs < 0 || num_tokens < 0 || num_blocks <= 0 || max_blocks_per_req <= 0)
+    return fail(PKV_ERR_DIMS, "num_reqs %lld, num_tokens %lld, num_blocks %lld", num_reqs,
+                num_tokens, num_blocks);
+  if (!query_start_loc) return fail(PKV_ERR_NULL, "query_start_loc is NULL");
+  if (num_reqs > 0 && (!block_table || !seq_lens || !num_computed_tokens))
+    return fail(PKV_ERR_NULL, "block_table, seq_lens or num_computed_tokens is NULL");
+  if (query_start_loc[0] != 0) return fail(PKV_ERR_METADATA, "query_start_loc[0] = %lld", query_start_loc[0]);
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    const int64_t qs = query_start_loc[r], qe = query_start_loc[r + 1];
+    const int64_t ql = qe - qs, L = seq_lens[r], c = num_computed_tokens[r];
+    if (ql < 0 || qe > num_tokens)
+      return fail(PKV_ERR_METADATA, "request %lld: query_start_loc %lld..%lld", r, qs, qe);
+    if (c < 0 || L != c + ql)
+      return fail(PKV_ERR_METADATA, "request %lld: seq_len %lld != computed + query_len (%lld)", r, L,
+                  c + ql);
+    if (ql > max_query_len || L > max_seq_len || L > (int64_t)max_blocks_per_req * pkv::kBlock)
+      return fail(PKV_ERR_METADATA, "request %lld: query_len %lld / seq_len %lld over the limits", r,
+                  ql, L);
+    const int64_t nb = (L + pkv::kBlock - 1) / pkv::kBlock;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t b = block_table[(int64_t)r * max_blocks_per_req + j];
+      if (b < 0 || b >= num_blocks)
+        return fail(PKV_ERR_METADATA, "request %lld: block_table[%lld] = %lld out of range", r, j, b);
+    }
+  }
+  if (slot_mapping) {
+    std::vector<int64_t> used;
+    used.reserve((size_t)num_tokens);
+    for (int64_t t = 0; t < num_tokens; ++t) {
+      const int64_t s = slot_mapping[t];
+      if (s == -1) continue;
+      if (s < 0 || s >= (int64_t)num_blocks * pkv::kBlock)
+        return fail(PKV_ERR_METADATA, "token %lld: slot %lld outside the pool", t, s);
+      used.push_back(s);
+    }
+    std::sort(used.begin(), used.end());
+    for (size_t i = 1; i < used.size(); ++i)
+      if (used[i] == used[i - 1]) return fail(PKV_ERR_METADATA, "slot %lld used twice", used[i]);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Device-side helpers and the workspace layout shared by the kernels and the
+// host entry points of libpagedkv (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlock = 16;        // tokens per cache block (fixed)
+constexpr int kWave = 64;         // CDNA wavefront width
+constexpr int kSplitTokens = 512; // split-KV partition length of a decode row
+constexpr int kSplitBlocks = kSplitTokens / kBlock;
+constexpr int kMaxGroupRegs = 8;  // query heads per kv head handled in one pass
+
+// Header words at the start of the workspace (int32).
+enum HdrWord {
+  kHdrError = 0,
+  kHdrRowItems = 1,
+  kHdrPrefillItems = 2,
+  kHdrReduceItems = 3,
+  kHdrSlots = 4,
+};
+constexpr size_t kHdrBytes = 256;
+
+// Row item (int4): x = query row, y = request, z = partition (kWholeRow: all
+// visible keys, kNanRow: metadata was bad, write NaN), w = first partial slot
+// of the row (or -1 when the item writes `out` directly).
+constexpr int kWholeRow = -1;
+constexpr int kNanRow = -2;
+
+// Prefill item (int4): x = request, y = first query row of the tile
+// (relative to the request), z = rows in the tile, w = unused.
+
+struct WsLayout {
+  size_t row_items, prefill_items, reduce_items, part_ml, part_o, total;
+  int64_t cap_row_items, cap_prefill_items, cap_reduce, cap_slots;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Capacities are upper bounds that hold for any metadata that passes the
+// device checks (query_len <= max_query_len, seq_len <= max_seq_len).
+inline WsLayout ws_layout(int64_t num_reqs, int64_t num_tokens, int64_t num_q_heads,
+                          int64_t head_dim, int64_t max_query_len, int64_t max_seq_len,
+                          int64_t prefill_tile_rows) {
+  WsLayout w{};
+  const int64_t dec_rows = num_reqs < num_tokens ? num_reqs : num_tokens;
+  const int64_t max_parts = (max_seq_len + kSplitTokens - 1) / kSplitTokens;
+  w.cap_row_items = dec_rows * (max_parts > 1 ? max_parts : 1) + num_tokens + 1;
+  w.cap_prefill_items = num_tokens / (prefill_tile_rows > 0 ? prefill_tile_rows : 1) + num_reqs + 1;
+  w.cap_reduce = dec_rows + 1;
+  w.cap_slots = (max_parts > 1 ? dec_rows * max_parts : 0) + 1;
+  (void)max_query_len;
+  size_t off = kHdrBytes;
+  w.row_items = off;      off = align_up(off + sizeof(int32_t) * 4 * w.cap_row_items, 256);
+  w.prefill_items = off;  off = align_up(off + sizeof(int32_t) * 4 * w.cap_prefill_items, 256);
+  w.reduce_items = off;   off = align_up(off + sizeof(int32_t) * 4 * w.cap_reduce, 256);
+  w.part_ml = off;        off = align_up(off + sizeof(float) * 2 * w.cap_slots * num_q_heads, 256);
+  w.part_o = off;         off = align_up(off + sizeof(float) * w.cap_slots * num_q_heads * head_dim, 256);
+  w.total = off;
+  return w;
+}
+
+#ifdef __HIP_DEVICE_COMPILE__
+#define PKV_DEV __device__ __forceinline__
+#else
+#define PKV_DEV __device__ inline
+#endif
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 is stored as its 16-bit pattern; a bf16 value is the top half of the
+// float32 with the same value.
+PKV_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+PKV_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+PKV_DEV uint16_t f32_to_bf16(float f) {  // round to nearest even; NaN stays NaN
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c, bf16 products accumulated in fp32.
+PKV_DEV float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane moves (all rows and banks enabled).
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;   // rotate right by 4 inside each row of 16 lanes
+constexpr int kDppRowRor8 = 0x128;
+
+template <int CTRL>
+PKV_DEV float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+PKV_DEV float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+PKV_DEV float wave_sum(float x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+PKV_DEV float wave_max(float x) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// Buffer resource over [p, p + bytes); loads past the end return 0.
+constexpr int kRsrcWord3 = 0x00020000;
+PKV_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+}  // namespace pkv

@@ -1,0 +1,80 @@
+// Internal launch interface between the host entry points (pkv_api.cpp) and
+// the kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/paged_kv.h"
+
+namespace pkv {
+
+struct PlanParams {
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* nct;
+  int32_t num_reqs;
+  int64_t num_tokens;
+  int32_t max_query_len, max_seq_len, max_blocks_per_req;
+  int32_t split_decode;      // decode rows may be split into partitions
+  int32_t mfma_prefill;      // query_len > 1 requests go to the prefill kernel
+  int32_t prefill_tile_rows; // query rows per prefill tile
+  int32_t* hdr;
+  int4* row_items;
+  int4* prefill_items;
+  int4* reduce_items;
+  int64_t cap_row_items, cap_prefill_items, cap_reduce, cap_slots;
+};
+
+struct RowParams {
+  void* out;
+  const void* q;
+  const void* cache;  // layer base: K half then V half
+  const int32_t* block_table;
+  const int32_t* qsl;
+  const int32_t* nct;
+  const int4* items;
+  const int32_t* hdr;
+  float* part_o;
+  float2* part_ml;
+  int32_t* err;
+  float scale_log2;  // scale * log2(e)
+  int32_t num_q_heads, num_kv_heads, group, head_groups, num_blocks, max_blocks_per_req;
+};
+
+struct ReduceParams {
+  void* out;
+  const int4* items;
+  const int32_t* hdr;
+  const float* part_o;
+  const float2* part_ml;
+  int32_t num_q_heads;
+};
+
+struct PrefillParams {
+  void* out;
+  const void* q;
+  const void* cache;
+  const int32_t* block_table;
+  const int32_t* qsl;
+  const int32_t* nct;
+  const int4* items;
+  const int32_t* hdr;
+  int32_t* err;
+  float scale_log2;
+  int32_t num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_req;
+};
+
+int launch_kv_write(const void* k, const void* v, const int64_t* slot_mapping, void* cache,
+                    int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
+                    hipStream_t stream);
+int launch_plan(const PlanParams& p, hipStream_t stream);
+int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t grid,
+                hipStream_t stream);
+int launch_reduce(const ReduceParams& p, int32_t dtype, int32_t head_dim, int64_t grid,
+                  hipStream_t stream);
+int prefill_tile_rows(int32_t group);
+int launch_prefill(const PrefillParams& p, int32_t head_dim, int64_t grid, hipStream_t stream);
+
+}  // namespace pkv

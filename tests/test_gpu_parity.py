@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Cache writes must be bit-exact; attention outputs within
+1e-5 (fp32) or 2e-2 (bf16) max abs error."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (TOL, assert_close, device_error, from_dev, oracle_out, oracle_pool,
+                      out_f64, run_attention, run_write, to_dev, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_61_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _check_pool(s, ref_pool, what):
+    got = from_dev(s.pool)
+    same = got.tobytes() == ref_pool.tobytes()
+    if not same:
+        diff = np.nonzero(got.reshape(-1).view(np.uint8) != ref_pool.reshape(-1).view(np.uint8))[0]
+        raise AssertionError(f"{what}: cache differs from the oracle write at {diff.size} bytes")
+
+
+def _full_step(wl, what):
+    print(f"[case] {what}", flush=True)
+    s = upload(wl)
+    run_write(s)
+    run_attention(s)
+    torch.cuda.synchronize()
+    assert device_error(s) == 0
+    ref_pool = oracle_pool(wl)
+    _check_pool(s, ref_pool, what)
+    ref = oracle_out(wl, ref_pool)
+    assert_close(out_f64(s.out), ref, wl.dtype, what)
+    return s, ref
+
+
+# ---------------------------------------------------------------------------
+# small ragged batches: decode rows, split-KV rows, prefill chunks
+
+SMALL = [
+    ("f32", 64, 8, 2), ("f32", 128, 4, 4), ("bf16", 64, 8, 2), ("bf16", 128, 4, 1),
+    ("bf16", 128, 32, 8), ("bf16", 128, 12, 4), ("bf16", 64, 16, 1), ("f32", 64, 6, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", SMALL)
+def test_small_ragged_batch(dtype, D, Hq, Hkv):
+    spec = workloads.random_spec(f"ragged-{dtype}-{D}-{Hq}-{Hkv}", 100 + D + Hq, dtype, Hq, Hkv,
+                                 D, num_reqs=9, max_ctx=1400, max_ql=40)
+    _full_step(workloads.build(spec), spec.name)
+
+
+def test_edge_lengths():
+    # context lengths around block and partition edges, one empty request
+    reqs = [(0, 1), (14, 1), (15, 1), (16, 1), (511, 1), (512, 1), (1023, 1), (1024, 1),
+            (7, 0), (0, 17), (5, 16), (31, 33)]
+    for dtype in ("f32", "bf16"):
+        wl = workloads.build(workloads.small_spec(f"edges-{dtype}", 7, dtype, 8, 2, 128, reqs))
+        _full_step(wl, f"edges-{dtype}")
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5])
+def test_config_full(n):
+    wl = workloads.build(workloads.CONFIGS[n])
+    _full_step(wl, f"config {n}: {wl.spec.name}")
+
+
+def test_config4_mixed_step_sampled():
+    wl = workloads.build(workloads.CONFIGS[4])
+    what = "config 4 mixed step"
+    print(f"[case] {what}", flush=True)
+    s = upload(wl)
+    run_write(s)
+    run_attention(s)
+    torch.cuda.synchronize()
+    assert device_error(s) == 0
+    ref_pool = oracle_pool(wl)
+    expect = to_dev(ref_pool, wl.dtype)
+    assert torch.equal(s.pool.view(torch.int16) if wl.dtype == "bf16" else s.pool.view(torch.int32),
+                       expect.view(torch.int16) if wl.dtype == "bf16" else expect.view(torch.int32))
+    del expect
+    rng = np.random.default_rng(44)
+    qsl = wl.query_start_loc
+    rows = []
+    for r in range(3):  # prefill chunks: first, last and random rows
+        rows += [int(qsl[r]), int(qsl[r + 1]) - 1] + rng.integers(qsl[r], qsl[r + 1], 14).tolist()
+    rows += rng.integers(qsl[3], qsl[-1], 64).tolist()
+    rows = sorted(set(rows))
+    ref = oracle_out(wl, ref_pool, tokens=rows)
+    got = out_f64(s.out)[rows]
+    assert_close(got, ref, wl.dtype, what)
+    # every row is finite
+    assert torch.isfinite(s.out.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+
+def _bits(t):
+    return from_dev(t).tobytes()
+
+
+def test_block_permutation_bit_exact():
+    spec = workloads.random_spec("perm", 21, "bf16", 8, 2, 128, num_reqs=6, max_ctx=1500, max_ql=20)
+    wl = workloads.build(spec)
+    s = upload(wl)
+    run_write(s)
+    a = _bits(run_attention(s))
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(wl.num_blocks)).cuda()
+    pool2 = torch.empty_like(s.pool)
+    pool2[:, perm] = s.pool
+    s.pool = pool2
+    s.block_table = perm[s.block_table.long()].to(torch.int32).contiguous()
+    b = _bits(run_attention(s, out=torch.empty_like(s.q)))
+    assert a == b
+
+
+def test_determinism_and_batch_invariance():
+    reqs = [(700, 1), (30, 1), (2000, 1), (100, 9), (0, 25), (1300, 1)]
+    wl = workloads.build(workloads.small_spec("batch", 22, "bf16", 16, 4, 128, reqs))
+    s = upload(wl)
+    run_write(s)
+    a = _bits(run_attention(s))
+    b = _bits(run_attention(s, out=torch.empty_like(s.q)))
+    assert a == b
+    full = from_dev(s.out)
+    # each request alone (same pool, one-row metadata) gives the same bits
+    import paged_kv_cache_61_amd as pkv
+    for r in range(len(reqs)):
+        qs, qe = int(wl.query_start_loc[r]), int(wl.query_start_loc[r + 1])
+        i32 = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")
+        out = pkv.paged_attention(s.q[qs:qe].contiguous(), s.pool, s.block_table[r:r + 1].contiguous(),
+                                  i32([wl.seq_lens[r]]), i32([0, qe - qs]),
+                                  i32([wl.num_computed_tokens[r]]), wl.scale,
+                                  max_query_len=qe - qs, max_seq_len=int(wl.seq_lens[r]))
+        assert from_dev(out).tobytes() == full[qs:qe].tobytes(), f"request {r}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_constant_v_gives_one(dtype):
+    reqs = [(0, 1), (37, 1), (900, 1), (0, 30), (64, 5)]
+    wl = workloads.build(workloads.small_spec("ones", 23, dtype, 8, 2, 64, reqs))
+    one = np.float32(1.0)
+    if dtype == "bf16":
+        live = wl.pool[1] != workloads.BF16_NAN
+        wl.pool[1][live] = workloads.bf16_bits_from_f32(np.array([one]))[0]
+        wl.v_new[:] = workloads.bf16_bits_from_f32(np.array([one]))[0]
+    else:
+        live = np.isfinite(wl.pool[1])
+        wl.pool[1][live] = one
+        wl.v_new[:] = one
+    s = upload(wl)
+    run_write(s)
+    got = out_f64(run_attention(s))
+    if dtype == "bf16":
+        assert (got == 1.0).all()
+    else:
+        assert np.abs(got - 1.0).max() <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_context_returns_v(dtype):
+    wl = workloads.build(workloads.small_spec("one", 24, dtype, 8, 2, 128, [(0, 1), (0, 1), (0, 1)]))
+    s = upload(wl)
+    run_write(s)
+    got = from_dev(run_attention(s))
+    G = 4
+    for t in range(3):
+        for h in range(8):
+            assert got[t, h].tobytes() == wl.v_new[t, h // G].tobytes()
+
+
+# ---------------------------------------------------------------------------
+# bad metadata is reported, never faults, and poisons only its own rows
+
+def test_bad_metadata_sets_error_and_nan_rows():
+    import paged_kv_cache_61_amd as pkv
+    reqs = [(40, 1), (10, 3), (100, 1)]
+    wl = workloads.build(workloads.small_spec("bad", 25, "f32", 4, 2, 64, reqs))
+    s = upload(wl)
+    run_write(s)
+    good = out_f64(run_attention(s))
+    # request 1: seq_len inconsistent with computed + query_len
+    sl = s.seq_lens.clone()
+    sl[1] += 1
+    s2 = upload(wl)
+    run_write(s2)
+    s2.seq_lens = sl
+    out = out_f64(run_attention(s2))
+    err = device_error(s2)
+    assert err & pkv.DEVERR_SEQ_LEN
+    assert np.isnan(out[1:4]).all()
+    assert np.array_equal(out[[0, 4]], good[[0, 4]])
+    # request 2: a block id outside the pool
+    s3 = upload(wl)
+    run_write(s3)
+    bt = s3.block_table.clone()
+    bt[2, 3] = wl.num_blocks + 5
+    s3.block_table = bt
+    out = out_f64(run_attention(s3))
+    assert device_error(s3) & pkv.DEVERR_BLOCK_ID
+    assert np.isnan(out[4]).all()
+    assert np.array_equal(out[:4], good[:4])
+
+
+def test_write_skips_padding_and_bad_slots():
+    import paged_kv_cache_61_amd as pkv
+    wl = workloads.build(workloads.small_spec("w", 26, "bf16", 8, 2, 128, [(5, 6), (0, 3)]))
+    s = upload(wl)
+    sm = wl.slot_mapping.copy()
+    sm[1] = -1
+    sm[4] = 16 * wl.num_blocks      # outside the pool: skipped and reported
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.paged_kv_write(s.k_new, s.v_new, torch.from_numpy(sm).cuda(), s.pool, device_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & pkv.DEVERR_SLOT
+    sm_ok = sm.copy()
+    sm_ok[4] = -1
+    ref = oracle.kv_write(wl.pool, wl.k_new, wl.v_new, sm_ok)
+    assert from_dev(s.pool).tobytes() == ref.tobytes()
+
+
+def test_empty_step():
+    import paged_kv_cache_61_amd as pkv
+    wl = workloads.build(workloads.small_spec("e", 27, "bf16", 8, 2, 64, [(3, 0), (9, 0)]))
+    s = upload(wl)
+    out = run_attention(s)
+    torch.cuda.synchronize()
+    assert device_error(s) == 0
+    assert out.shape[0] == 0
