@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of one continuous-batching step of attention over a paged KV cache.
+
+A step is the whole hot path over one batch: ``paged_kv_write`` of the step's
+new tokens, then ``paged_attention`` (device-side planning, prefill chunks on
+MFMA, decode rows with split-KV partitions, the split-KV merge, the output).
+Inputs are seeded synthetic tensors already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+
+Default workload: Llama-7B-shaped single-layer decode, bf16 (64 sequences,
+32 q / 32 kv heads, head_dim 128, contexts uniform in [512, 4096]).
+Prints ONE JSON line.  Only one GPU is supported: ``--gpus`` above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+METRIC = "paged decode KV-read GB/s (% HBM peak); prefill attn TFLOPS (% MFMA)"
+WORKLOAD_NAMES = {
+    1: "tiny paged decode fp32",
+    2: "Llama-7B-shaped single-layer decode bf16",
+    3: "GQA decode at high concurrency bf16",
+    4: "mixed continuous-batching step bf16",
+    5: "long-context split-KV decode bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0,
+                    help="CPU seconds the oracle baseline may spend on its sample")
+    return ap.parse_args()
+
+
+def accounting(wl):
+    """Algorithmic work of one step (what the method must move / compute)."""
+    import numpy as np
+    s = 2 if wl.dtype == "bf16" else 4
+    Hq, Hkv, D = wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    ql = wl.query_lens.astype(np.int64)
+    L = wl.seq_lens.astype(np.int64)
+    c = wl.num_computed_tokens.astype(np.int64)
+    dec = ql == 1
+    pre = ql > 1
+    kv_token_bytes = 2 * Hkv * D * s
+    a = {}
+    a["decode_rows"] = int(dec.sum())
+    a["decode_kv_tokens"] = int(L[dec].sum())
+    a["decode_kv_bytes"] = int(L[dec].sum()) * kv_token_bytes
+    a["decode_io_bytes"] = 2 * int(dec.sum()) * Hq * D * s            # q read + out written
+    a["decode_table_bytes"] = int(((L[dec] + 15) // 16).sum()) * 4
+    a["decode_bytes"] = a["decode_kv_bytes"] + a["decode_io_bytes"] + a["decode_table_bytes"]
+    a["prefill_pairs_per_head"] = int((ql[pre] * c[pre] + ql[pre] * (ql[pre] + 1) // 2).sum())
+    a["prefill_flops"] = 4 * D * Hq * a["prefill_pairs_per_head"]
+    a["prefill_bytes"] = int(L[pre].sum()) * kv_token_bytes + 2 * int(ql[pre].sum()) * Hq * D * s
+    T = wl.num_tokens
+    a["write_bytes"] = 2 * (2 * T * Hkv * D * s) + 8 * T
+    a["step_bytes"] = a["decode_bytes"] + a["prefill_bytes"] + a["write_bytes"]
+    return a
+
+
+def cpu_baseline(wl, acct, budget_s):
+    """Time the fp64 oracle on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    order = np.random.default_rng(1234).permutation(wl.num_reqs)
+    ql = wl.query_lens
+    s = 2 if wl.dtype == "bf16" else 4
+    kv_token_bytes = 2 * wl.num_kv_heads * wl.head_dim * s
+    t0 = time.perf_counter()
+    pool = oracle.kv_write(wl.pool, wl.k_new, wl.v_new, wl.slot_mapping)
+    done_bytes = 0
+    done_flops = 0
+    n = 0
+    rows = 0
+    for r in order:
+        if ql[r] == 0:
+            continue
+        if ql[r] == 1:
+            oracle.attention(wl.q, pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
+                             wl.num_computed_tokens, wl.scale, wl.dtype, requests=[int(r)])
+            done_bytes += int(wl.seq_lens[r]) * kv_token_bytes
+            rows += 1
+        else:  # a prefill chunk: sample 8 of its rows
+            qs = int(wl.query_start_loc[r])
+            pick = np.linspace(qs, qs + int(ql[r]) - 1, 8).astype(int).tolist()
+            oracle.attention_rows(wl.q, pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
+                                  wl.num_computed_tokens, wl.scale, wl.dtype, tokens=pick)
+            c = int(wl.num_computed_tokens[r])
+            done_flops += sum(4 * wl.head_dim * wl.num_q_heads * (c + t - qs + 1) for t in pick)
+            rows += len(pick)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if acct["decode_rows"] > 0:
+        value, unit = done_bytes / dt / 1e9, "GB/s"
+    else:
+        value, unit = done_flops / dt / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {wl.num_reqs} requests ({rows} query rows) in seeded random order, "
+                      f"cache write included, {dt:.1f} s single-threaded numpy fp64",
+            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_61_amd as pkv
+    import workloads
+
+    t_gen = time.perf_counter()
+    wl = workloads.build(workloads.CONFIGS[args.workload])
+    gen_s = time.perf_counter() - t_gen
+    acct = accounting(wl)
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    q, pool = up(wl.q), up(wl.pool)
+    k_new, v_new = up(wl.k_new), up(wl.v_new)
+    slot_mapping = torch.from_numpy(wl.slot_mapping).to(dev)
+    bt, sl, qsl, nct = (i32(wl.block_table), i32(wl.seq_lens), i32(wl.query_start_loc),
+                        i32(wl.num_computed_tokens))
+    ws = torch.empty(max(256, pkv.paged_attention_workspace_size(
+        wl.num_reqs, wl.num_tokens, wl.num_q_heads, wl.head_dim, wl.max_query_len,
+        wl.max_seq_len)), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    nph = pkv.NUM_PHASES
+    step_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nph)]
+                   for _ in range(args.steps)]
+    for evs in step_events:          # create the underlying hipEvents
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        pkv.paged_kv_write(k_new, v_new, slot_mapping, pool)
+        pkv.paged_attention(q, pool, bt, sl, qsl, nct, wl.scale, max_query_len=wl.max_query_len,
+                            max_seq_len=wl.max_seq_len, out=out, workspace=ws, phase_events=evs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    err = pkv.pkv_read_device_error(ws)
+    if err != 0:
+        raise SystemExit(f"device error word {err:#x}")
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(step_events[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    names = ["plan", "prefill", "rows", "reduce"]
+    phase_ms = {}
+    for p, nm in enumerate(names):
+        phase_ms[nm] = float(np.mean([evs[2 * p].elapsed_time(evs[2 * p + 1]) for evs in step_events]))
+
+    value = acct["step_bytes"] / (ms_per_step * 1e-3) / 1e9
+    rows_gbs = acct["decode_bytes"] / (phase_ms["rows"] * 1e-3) / 1e9 if phase_ms["rows"] > 0 else 0.0
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, shuffled block pool, NaN-poisoned unused slots)",
+        "config": {
+            "workload": f"{WORKLOAD_NAMES[args.workload]}: {wl.spec.name}",
+            "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
+            "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "block_size": 16, "num_blocks": wl.num_blocks,
+            "decode_kv_tokens": acct["decode_kv_tokens"], "max_seq_len": wl.max_seq_len,
+        },
+        "roofline": {
+            "kernel": "row_attn_kernel (decode rows + split-KV partitions)",
+            "bound": "hbm",
+            "achieved": round(rows_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": acct["decode_bytes"],
+            "avg_launch_ms": round(phase_ms["rows"], 5),
+        },
+        "phases_ms": {k: round(v, 5) for k, v in phase_ms.items()},
+        "step_algorithmic_bytes": acct["step_bytes"],
+        "wall_s_timed": round(wall_s, 4),
+        "input_gen_s": round(gen_s, 2),
+    }
+    if acct["prefill_flops"] > 0 and phase_ms["prefill"] > 0.02:
+        tf = acct["prefill_flops"] / (phase_ms["prefill"] * 1e-3) / 1e12 if phase_ms["prefill"] > 0 else 0.0
+        result["prefill"] = {"flops": acct["prefill_flops"], "tflops": round(tf, 2),
+                             "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if not args.no_cpu_baseline and world == 1:
+        result["cpu_baseline"] = cpu_baseline(wl, acct, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,6 +29,8 @@ __all__ = [
 
 BLOCK_SIZE = 16
 PKV_F32, PKV_BF16 = 0, 1
+PHASE_PLAN, PHASE_PREFILL, PHASE_ROWS, PHASE_REDUCE = 0, 1, 2, 3
+NUM_PHASES = 4
 DEVERR_SEQ_LEN, DEVERR_LIMITS, DEVERR_QSL = 0x1, 0x2, 0x4
 DEVERR_BLOCK_ID, DEVERR_SLOT, DEVERR_CAPACITY = 0x8, 0x10, 0x20
 
@@ -58,6 +60,8 @@ def load_library() -> ctypes.CDLL:
     lib.paged_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i64, i32, i32, i32, i32,
                                     i32, i32, i32, i32, vp, sz, vp]
     lib.paged_attention.restype = ctypes.c_int
+    lib.paged_attention_profiled.argtypes = lib.paged_attention.argtypes + [vp]
+    lib.paged_attention_profiled.restype = ctypes.c_int
     lib.paged_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.paged_attention_workspace_size.restype = sz
     lib.pkv_read_device_error.argtypes = [vp, vp]
@@ -73,7 +77,8 @@ def load_library() -> ctypes.CDLL:
 
 _lib = load_library()
 
-EXPORTED_SYMBOLS = ("paged_kv_write", "paged_attention", "paged_attention_workspace_size",
+EXPORTED_SYMBOLS = ("paged_kv_write", "paged_attention", "paged_attention_profiled",
+                    "paged_attention_workspace_size",
                     "pkv_read_device_error", "pkv_validate_metadata_host", "pkv_status_string",
                     "pkv_last_error_detail")
 
@@ -137,12 +142,15 @@ def paged_attention(q: torch.Tensor, kv_cache_layer: torch.Tensor, block_table: 
                     seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
                     num_computed_tokens: torch.Tensor, scale: float, *, max_query_len: int,
                     max_seq_len: int, out: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    phase_events=None) -> torch.Tensor:
     """Attention of ``q [T, Hq, D]`` over the paged cache; returns ``out [T, Hq, D]``.
 
     ``max_query_len`` / ``max_seq_len`` are host-side bounds on the step's
     query lengths and sequence lengths.  ``workspace`` (uint8, on the device)
-    is allocated when not given."""
+    is allocated when not given.  ``phase_events``: optional sequence of
+    ``2 * NUM_PHASES`` ``torch.cuda.Event`` (or None) recorded around the
+    library's internal phases (``paged_attention_profiled``)."""
     _check_dev("q", q, kv_cache_layer.dtype)
     _check_dev("kv_cache_layer", kv_cache_layer)
     for n, x in (("block_table", block_table), ("seq_lens", seq_lens),
@@ -170,11 +178,18 @@ def paged_attention(q: torch.Tensor, kv_cache_layer: torch.Tensor, block_table: 
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     else:
         _check_dev("workspace", workspace, torch.uint8)
-    st = _lib.paged_attention(_ptr(out), _ptr(q), _ptr(kv_cache_layer), _ptr(block_table),
-                              _ptr(seq_lens), _ptr(query_start_loc), _ptr(num_computed_tokens),
-                              float(scale), R, T, hq, hkv, d, nb, max(mb, 1), max_query_len,
-                              max_seq_len, _dtype_code(q.dtype), _ptr(workspace),
-                              workspace.numel(), _stream_ptr(stream))
+    args = (_ptr(out), _ptr(q), _ptr(kv_cache_layer), _ptr(block_table), _ptr(seq_lens),
+            _ptr(query_start_loc), _ptr(num_computed_tokens), float(scale), R, T, hq, hkv, d, nb,
+            max(mb, 1), max_query_len, max_seq_len, _dtype_code(q.dtype), _ptr(workspace),
+            workspace.numel(), _stream_ptr(stream))
+    if phase_events is None:
+        st = _lib.paged_attention(*args)
+    else:
+        if len(phase_events) != 2 * NUM_PHASES:
+            raise ValueError(f"phase_events needs {2 * NUM_PHASES} entries")
+        handles = (ctypes.c_void_p * (2 * NUM_PHASES))(
+            *[None if e is None else int(e.cuda_event) for e in phase_events])
+        st = _lib.paged_attention_profiled(*args, handles)
     if st != 0:
         raise PagedKVError(st, "paged_attention")
     return out
