@@ -50,10 +50,12 @@ int num_cus() {
   return n;
 }
 
-bool prefill_on_mfma(int32_t dtype) { return false && dtype == PKV_BF16; }
+// bf16 prefill chunks with head_dim 128 run on the MFMA tile kernel; other
+// prefill rows go through the row kernel, one query row at a time.
+bool prefill_on_mfma(int32_t dtype, int32_t head_dim) { return dtype == PKV_BF16 && head_dim == 128; }
 
-int64_t tile_rows_for(int32_t dtype, int32_t group) {
-  return prefill_on_mfma(dtype) ? pkv::prefill_tile_rows(group) : 1;
+int64_t tile_rows_for(int32_t dtype, int32_t head_dim, int32_t group) {
+  return prefill_on_mfma(dtype, head_dim) ? pkv::prefill_tile_rows(group) : 1;
 }
 
 }  // namespace
@@ -149,7 +151,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     return fail(PKV_ERR_DIMS, "cache too large");
 
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t tile_rows = tile_rows_for(dtype, group);
+  const int64_t tile_rows = tile_rows_for(dtype, head_dim, group);
   const pkv::WsLayout ws =
       pkv::ws_layout(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len, max_seq_len, tile_rows);
   if (workspace_bytes < ws.total)
@@ -174,7 +176,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   pp.max_seq_len = max_seq_len;
   pp.max_blocks_per_req = max_blocks_per_req;
   pp.split_decode = 1;
-  pp.mfma_prefill = prefill_on_mfma(dtype) ? 1 : 0;
+  pp.mfma_prefill = prefill_on_mfma(dtype, head_dim) ? 1 : 0;
   pp.prefill_tile_rows = (int32_t)tile_rows;
   pp.hdr = hdr;
   pp.row_items = (int4*)(wsb + ws.row_items);
@@ -209,7 +211,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.num_blocks = num_blocks;
     fp.max_blocks_per_req = max_blocks_per_req;
     const int64_t bound = ws.cap_prefill_items * num_kv_heads;
-    const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 16);
+    const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 2);
     if (pkv::launch_prefill(fp, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "prefill launch failed");
   }
 

@@ -239,3 +239,45 @@ def test_empty_step():
     torch.cuda.synchronize()
     assert device_error(s) == 0
     assert out.shape[0] == 0
+
+
+# ---------------------------------------------------------------------------
+# prefill chunks on the MFMA path
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (12, 4), (32, 8), (64, 8), (32, 2)])
+def test_prefill_group_sizes(Hq, Hkv):
+    reqs = [(0, 130), (37, 64), (700, 200), (5, 1), (0, 2), (1100, 77), (16, 16)]
+    wl = workloads.build(workloads.small_spec(f"prefill-{Hq}-{Hkv}", 31 + Hq, "bf16", Hq, Hkv, 128, reqs))
+    _full_step(wl, f"prefill G={Hq // Hkv}")
+
+
+def test_prefill_chunk_split_and_decode_consistency():
+    # one 300-token chunk on a 100-token prefix, the same tokens as two chunks,
+    # and the last token as a decode: all agree with the oracle and each other
+    rng = np.random.default_rng(5)
+    wl = workloads.build(workloads.small_spec("split", 32, "bf16", 32, 8, 128,
+                                               [(100, 300), (100, 150), (250, 150), (399, 1)]))
+    # make the four requests read the same cache: copy request 0's blocks
+    wl.block_table[1:] = wl.block_table[0]
+    wl.q[300:600] = wl.q[0:300]
+    wl.q[600] = wl.q[299]
+    wl.k_new[:] = wl.k_new[0]   # any values: all requests write the same slots with equal data
+    wl.v_new[:] = wl.v_new[0]
+    sm = wl.slot_mapping.copy()
+    sm[300:450] = sm[0:150]
+    sm[450:600] = sm[150:300]
+    sm[600] = sm[299]
+    wl.slot_mapping = sm
+    ref_pool = oracle.kv_write(wl.pool, wl.k_new[:300], wl.v_new[:300], sm[:300])
+    s = upload(wl)
+    import paged_kv_cache_61_amd as pkv
+    pkv.paged_kv_write(s.k_new[:300].contiguous(), s.v_new[:300].contiguous(), s.slot_mapping[:300].contiguous(), s.pool)
+    run_attention(s)
+    torch.cuda.synchronize()
+    assert device_error(s) == 0
+    got = out_f64(s.out)
+    ref = oracle.attention(wl.q, ref_pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
+                           wl.num_computed_tokens, wl.scale, "bf16")
+    assert_close(got, ref, "bf16", "chunk split")
+    assert np.abs(got[0:300] - got[300:600]).max() <= 2e-2
+    assert np.abs(got[299] - got[600]).max() <= 2e-2
