@@ -38,6 +38,10 @@
 // result does not depend on the rest of the batch.
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
 #include "pkv_common.h"
 #include "pkv_internal.h"
 
@@ -116,218 +120,402 @@ PKV_DEV void store_out<false>(void* out, size_t idx, float x) {
   ((float*)out)[idx] = x;
 }
 
+// Lanes that share one token's q.k: 4 (each owns a quarter of head_dim), or
+// 8 for groups of 8 heads, which halves the q registers a lane holds.
+template <int GM>
+struct Lanes {
+  static constexpr int kPerToken = GM == 8 ? 8 : 4;
+  static constexpr int kTokensPerPass = kWave / kPerToken;   // 16 or 8
+  static constexpr int kPasses = kBlock / kTokensPerPass;      // 1 or 2
+  static constexpr int kHeadsPerLane = GM > kPerToken ? GM / kPerToken : 1;
+  // head held by lane quarter/eighth c in slot k after the reduce-scatter
+  PKV_DEV static int head(int c, int k) {
+    return GM >= kPerToken ? c + kPerToken * k : (GM == 2 ? (c & 1) : 0);
+  }
+  // one lane per distinct head writes shared per-head values
+  PKV_DEV static bool writer(int c) { return c < (GM < kPerToken ? GM : kPerToken); }
+};
+
+// Sum the partial dots x[0..GM) over the lanes of a token so that lane c ends
+// with the full dots of its Lanes<GM>::head(c, k) heads in y[].  Each DPP step
+// halves the heads a lane keeps: the lane keeps one half and adds what its
+// partner sends of that half.
+template <int GM>
+PKV_DEV void reduce_scatter(const float (&x)[GM], float (&y)[Lanes<GM>::kHeadsPerLane], int c) {
+  if constexpr (GM == 1) {
+    const float v = x[0] + dpp_mov<kDppQuadSwap1>(x[0]);
+    y[0] = v + dpp_mov<kDppQuadSwap2>(v);
+  } else if constexpr (GM == 2) {
+    const bool b = c & 1;
+    const float v = (b ? x[1] : x[0]) + dpp_mov<kDppQuadSwap1>(b ? x[0] : x[1]);
+    y[0] = v + dpp_mov<kDppQuadSwap2>(v);
+  } else if constexpr (GM == 4) {
+    const bool b0 = c & 1, b1 = (c >> 1) & 1;
+    float x1[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      x1[j] = (b0 ? x[2 * j + 1] : x[2 * j]) + dpp_mov<kDppQuadSwap1>(b0 ? x[2 * j] : x[2 * j + 1]);
+    y[0] = (b1 ? x1[1] : x1[0]) + dpp_mov<kDppQuadSwap2>(b1 ? x1[0] : x1[1]);
+  } else {  // GM == 8 over 8 lanes: bit 2 (half-row mirror), then bits 0 and 1
+    const bool b2 = (c >> 2) & 1, b0 = c & 1, b1 = (c >> 1) & 1;
+    float x1[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      x1[h] = (b2 ? x[h + 4] : x[h]) + dpp_mov<kDppRowHalfMirror>(b2 ? x[h] : x[h + 4]);
+    float x2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      x2[j] = (b0 ? x1[2 * j + 1] : x1[2 * j]) + dpp_mov<kDppQuadSwap1>(b0 ? x1[2 * j] : x1[2 * j + 1]);
+    y[0] = (b1 ? x2[1] : x2[0]) + dpp_mov<kDppQuadSwap2>(b1 ? x2[0] : x2[1]);
+  }
+}
+
+// Max / sum over the tokens of one pass for lanes sharing c (lane = token *
+// LPT + c): rotate within 16-lane rows, then exchange across rows.
+template <int LPT>
+PKV_DEV float pass_max(float v) {
+  if constexpr (LPT == 4) v = fmaxf(v, dpp_mov<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_mov<kDppRowRor8>(v));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+template <int LPT>
+PKV_DEV float pass_sum(float v) {
+  if constexpr (LPT == 4) v += dpp_mov<kDppRowRor4>(v);
+  v += dpp_mov<kDppRowRor8>(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// A head's reference max moves only when a score exceeds it by more than
+// this (log2 units), so p = exp2(s - ref) <= 2^8.  Numerator and denominator
+// share the reference, so the softmax stays exact.
+constexpr float kRefSlack = 8.f;
+
+// What a wave needs to know about one work item.
+struct RowItem {
+  int t, r, part, slot0;   // query row, request, partition (or kWholeRow / kNanRow), first slot
+  int g, h0, nh;           // kv head, first query head, heads handled
+  int vis, jb, je;         // visible keys, block range [jb, je)
+};
+
+template <int GM>
+PKV_DEV RowItem fetch_item(const RowParams& a, int64_t it, int per_pair) {
+  RowItem d;
+  const int4 item = a.items[it / per_pair];
+  const int rem = (int)(it % per_pair);
+  d.g = rem / a.head_groups;
+  const int hg = rem - d.g * a.head_groups;
+  d.h0 = d.g * a.group + hg * GM;
+  d.nh = min(GM, a.group - hg * GM);
+  d.t = item.x;
+  d.r = item.y;
+  d.part = item.z;
+  d.slot0 = item.w;
+  d.vis = d.jb = d.je = 0;
+  if (d.part != kNanRow) {
+    d.vis = a.nct[d.r] + (d.t - a.qsl[d.r]) + 1;  // keys 0 .. position
+    const int nblk = (d.vis + kBlock - 1) / kBlock;
+    d.je = nblk;
+    if (d.part >= 0) {
+      d.jb = d.part * kSplitBlocks;
+      d.je = min(nblk, d.jb + kSplitBlocks);
+    }
+  }
+  return d;
+}
+
+// Lane j gets the physical id of block jb + k0 + j of the item (j < 64).
+PKV_DEV int fetch_ids(const RowParams& a, const RowItem& d, int k0, int lane) {
+  const int j = d.jb + k0 + lane;
+  return j < d.je ? a.block_table[(size_t)d.r * a.max_blocks_per_req + j] : 0;
+}
+
+// Each wave is an independent persistent worker: it takes work items
+// gw, gw + NW, ... (gw = global wave index, NW = waves in the grid) and,
+// while it streams one item's blocks, already holds the next item's
+// descriptor and block ids, so switching items costs one memory round trip.
 template <bool BF16, int D, int GM>
 __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
   using C = RowCfg<BF16, D>;
   using VT = typename VType<BF16>::T;
-  __shared__ __attribute__((aligned(16))) float p_lds[4][GM][kBlock];
-  __shared__ float comb_o[4][GM][D];
-  __shared__ float comb_m[4][GM];
-  __shared__ float comb_l[4][GM];
-  __shared__ int comb_bad[4];
+  using LN = Lanes<GM>;
+  constexpr int LPT = LN::kPerToken;
+  constexpr int TPP = LN::kTokensPerPass;
+  constexpr int NPASS = LN::kPasses;
+  constexpr int HPL = LN::kHeadsPerLane;
+  constexpr int CPL = C::NCH / LPT;      // 16-byte chunks of a row per lane
+  constexpr int PSZ = BF16 ? 2 : 4;      // bytes of one p value in LDS
+  __shared__ __attribute__((aligned(16))) char p_lds[4][GM * kBlock * PSZ];
+  __shared__ float alpha_lds[4][GM];
+  __shared__ float2 ml_lds[4][GM];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  const int tk = lane >> 2;          // token of the block (q.k layout)
-  const int cq = lane & 3;           // quarter of head_dim (q.k layout)
+  // wave index, made visibly wave-uniform so everything derived from it is scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int tk = lane / LPT;         // token of the pass (q.k layout)
+  const int cq = lane % LPT;         // slice of head_dim (q.k layout)
   const int dl = lane % (D / 2);     // element pair of head_dim (p.v layout)
   const int sub = lane / (D / 2);    // token parity when D = 64 (p.v layout)
   const int d0 = 2 * dl;
 
-  const int n_items = a.hdr[kHdrRowItems];
   const int per_pair = a.num_kv_heads * a.head_groups;
-  const int64_t total = (int64_t)n_items * per_pair;
+  const int64_t total = (int64_t)a.hdr[kHdrRowItems] * per_pair;
+  const int64_t nw = (int64_t)gridDim.x * 4;
   const uint32_t row_stride = (uint32_t)a.num_kv_heads * C::ROWB;  // bytes between token rows
   const uint32_t blk_bytes = kBlock * row_stride;
   const char* kbase = (const char*)a.cache;
   const char* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
+  char* my_p = p_lds[w];
 
-  for (int64_t it = blockIdx.x; it < total; it += gridDim.x) {
-    const int4 item = a.items[it / per_pair];
-    const int rem = (int)(it % per_pair);
-    const int g = rem / a.head_groups;
-    const int hg = rem - g * a.head_groups;
-    const int h0 = g * a.group + hg * GM;
-    const int nh = min(GM, a.group - hg * GM);
-    const int t = item.x, r = item.y, part = item.z, slot0 = item.w;
-    const size_t out_row = ((size_t)t * a.num_q_heads + h0) * D;
+  int64_t it = (int64_t)blockIdx.x * 4 + w;
+  if (it >= total) return;
+  RowItem cur = fetch_item<GM>(a, it, per_pair);
+  int btv = fetch_ids(a, cur, 0, lane);
 
-    if (part == kNanRow) {
-      for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x)
+  while (true) {
+    const int64_t nx = it + nw;
+    const bool has_next = nx < total;
+    RowItem nxt = cur;
+    int btv_next = 0;
+    if (has_next) {  // prefetch: consumed only after this item
+      nxt = fetch_item<GM>(a, nx, per_pair);
+      btv_next = fetch_ids(a, nxt, 0, lane);
+    }
+    const size_t out_row = ((size_t)cur.t * a.num_q_heads + cur.h0) * D;
+
+    if (cur.part == kNanRow) {
+      for (int idx = lane; idx < cur.nh * D; idx += kWave)
         store_out<BF16>(a.out, out_row + idx, __builtin_nanf(""));
-      continue;
-    }
-    const int vis = a.nct[r] + (t - a.qsl[r]) + 1;  // keys 0 .. position
-    const int nblk = (vis + kBlock - 1) / kBlock;
-    int jb = 0, je = nblk;
-    if (part >= 0) {
-      jb = part * kSplitBlocks;
-      je = min(nblk, jb + kSplitBlocks);
-    }
+    } else {
+      const int g = cur.g, nh = cur.nh, vis = cur.vis;
+      // This lane's slice of q for the group's heads: chunks cq + LPT * k.
+      u32x4 qr[GM][CPL];
+      const char* qrow = (const char*)a.q + out_row * C::ES;
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+          qr[hh][k] = hh < nh ? *(const u32x4*)(qrow + hh * C::ROWB + (cq + LPT * k) * 16)
+                              : u32x4{0, 0, 0, 0};
 
-    // This lane's quarter of q for the group's heads.
-    u32x4 qr[GM][C::CPL];
-    const char* qrow = (const char*)a.q + out_row * C::ES;
+      float mref[HPL], lsum[HPL], o[GM][2];
 #pragma unroll
-    for (int hh = 0; hh < GM; ++hh)
-#pragma unroll
-      for (int k = 0; k < C::CPL; ++k)
-        qr[hh][k] = hh < nh ? *(const u32x4*)(qrow + hh * C::ROWB + (cq + 4 * k) * 16)
-                            : u32x4{0, 0, 0, 0};
-
-    float m[GM], l[GM], o[GM][2];
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      m[hh] = -INFINITY;
-      l[hh] = 0.f;
-      o[hh][0] = o[hh][1] = 0.f;
-    }
-    bool bad = false;
-
-    const int nmine = (je - jb > w) ? (je - jb - w + 3) / 4 : 0;
-    const int* bt_row = a.block_table + (size_t)r * a.max_blocks_per_req;
-    const uint32_t koff = tk * row_stride + g * C::ROWB + cq * 16;
-    const uint32_t voff = sub * row_stride + g * C::ROWB + d0 * C::ES;
-
-    struct Stage {
-      u32x4 k[C::CPL];
-      VT v[C::VLD];
-    };
-    auto load = [&](Stage& s, int phys) {
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)phys * blk_bytes, blk_bytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)phys * blk_bytes, blk_bytes);
-#pragma unroll
-      for (int k = 0; k < C::CPL; ++k)
-        s.k[k] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + k * 64, 0, 0);
-#pragma unroll
-      for (int kk = 0; kk < C::VLD; ++kk) s.v[kk] = load_v(rv, voff, kk * C::TPI * row_stride, VT{});
-    };
-    auto compute = [&](const Stage& s, int jblk) {
-      const int tok0 = jblk * kBlock;
-      const bool tail = tok0 + kBlock > vis;
-      float sc[GM];
-#pragma unroll
-      for (int hh = 0; hh < GM; ++hh) {
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < C::CPL; ++k) acc = chunk_dot<BF16>(qr[hh][k], s.k[k], acc);
-        acc += dpp_mov<kDppQuadSwap1>(acc);
-        acc += dpp_mov<kDppQuadSwap2>(acc);
-        sc[hh] = acc * a.scale_log2;
-      }
-      if (tail && tok0 + tk >= vis) {
-#pragma unroll
-        for (int hh = 0; hh < GM; ++hh) sc[hh] = -INFINITY;
+      for (int k = 0; k < HPL; ++k) {
+        mref[k] = -INFINITY;
+        lsum[k] = 0.f;
       }
 #pragma unroll
-      for (int hh = 0; hh < GM; ++hh) {
-        float bm = sc[hh];
-        bm = fmaxf(bm, dpp_mov<kDppRowRor4>(bm));
-        bm = fmaxf(bm, dpp_mov<kDppRowRor8>(bm));
-        bm = fmaxf(fmaxf(readlane_f(bm, 0), readlane_f(bm, 16)),
-                   fmaxf(readlane_f(bm, 32), readlane_f(bm, 48)));
-        if (bm > m[hh]) {
-          const float alpha = fast_exp2(m[hh] - bm);
-          l[hh] *= alpha;
-          o[hh][0] *= alpha;
-          o[hh][1] *= alpha;
-          m[hh] = bm;
+      for (int hh = 0; hh < GM; ++hh) o[hh][0] = o[hh][1] = 0.f;
+      bool bad = false;
+
+      const uint32_t koff = tk * row_stride + g * C::ROWB + cq * 16;
+      const uint32_t voff = sub * row_stride + g * C::ROWB + d0 * C::ES;
+
+      struct Stage {
+        u32x4 k[NPASS][CPL];
+        VT v[C::VLD];
+      };
+      auto load = [&](Stage& s, int phys) {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)phys * blk_bytes, blk_bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)phys * blk_bytes, blk_bytes);
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+          for (int k = 0; k < CPL; ++k)
+            s.k[ps][k] = __builtin_amdgcn_raw_buffer_load_b128(
+                rk, koff + ps * TPP * row_stride + k * LPT * 16, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < C::VLD; ++kk) s.v[kk] = load_v(rv, voff, kk * C::TPI * row_stride, VT{});
+      };
+
+      auto compute = [&](auto mask_tag, const Stage& s, int jblk) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int tok0 = jblk * kBlock;
+        float sc[NPASS][HPL];
+        bool raise = false;
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          // q.k partial dots over this lane's slice, then reduce-scatter.
+          float x[GM];
+#pragma unroll
+          for (int hh = 0; hh < GM; ++hh) {
+            float acc = 0.f;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) acc = chunk_dot<BF16>(qr[hh][k], s.k[ps][k], acc);
+            x[hh] = acc;
+          }
+          reduce_scatter<GM>(x, sc[ps], cq);
+          const bool live = !MASK || tok0 + ps * TPP + tk < vis;
+#pragma unroll
+          for (int k = 0; k < HPL; ++k) {
+            sc[ps][k] = live ? sc[ps][k] * a.scale_log2 : -INFINITY;
+            raise |= sc[ps][k] > mref[k] + kRefSlack;
+          }
         }
-        const float pr = fast_exp2(sc[hh] - m[hh]);
-        l[hh] += pr;
-        if (cq == 0) p_lds[w][hh][(tk % C::TPI) * C::VLD + tk / C::TPI] = pr;
+        const bool rescale = __any(raise);
+        if (rescale) {  // rare: move the reference max
+#pragma unroll
+          for (int k = 0; k < HPL; ++k) {
+            float bm = sc[0][k];
+#pragma unroll
+            for (int ps = 1; ps < NPASS; ++ps) bm = fmaxf(bm, sc[ps][k]);
+            const float mnew = fmaxf(mref[k], pass_max<LPT>(bm));
+            const float alpha = __builtin_amdgcn_exp2f(mref[k] - mnew);
+            lsum[k] *= alpha;
+            mref[k] = mnew;
+            if (tk == 0 && LN::writer(cq)) alpha_lds[w][LN::head(cq, k)] = alpha;
+          }
+        }
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+          for (int k = 0; k < HPL; ++k) {
+            const float p = __builtin_amdgcn_exp2f(sc[ps][k] - mref[k]);
+            const int hh = LN::head(cq, k);
+            const int tb = ps * TPP + tk;  // token of the block
+            const int pidx = (hh * C::TPI + tb % C::TPI) * C::VLD + tb / C::TPI;
+            if constexpr (BF16) {
+              const uint16_t pb = f32_to_bf16(p);
+              lsum[k] += __uint_as_float((uint32_t)pb << 16);
+              if (LN::writer(cq)) ((uint16_t*)my_p)[pidx] = pb;
+            } else {
+              lsum[k] += p;
+              if (LN::writer(cq)) ((float*)my_p)[pidx] = p;
+            }
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (rescale) {
+#pragma unroll
+          for (int hh = 0; hh < GM; ++hh) {
+            const float al = alpha_lds[w][hh];
+            o[hh][0] *= al;
+            o[hh][1] *= al;
+          }
+        }
+        // p.v: lanes own head_dim pairs; tokens kk*TPI + sub.
+        if constexpr (BF16) {
+#pragma unroll
+          for (int j = 0; j < C::VLD / 2; j += 2) {
+            u32x2 pp[GM];
+#pragma unroll
+            for (int hh = 0; hh < GM; ++hh)
+              pp[hh] = *(const u32x2*)(my_p + ((hh * C::TPI + sub) * C::VLD + 2 * j) * 2);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              uint32_t x0 = s.v[2 * (j + e)], x1 = s.v[2 * (j + e) + 1];
+              if constexpr (MASK) {
+                if (tok0 + (2 * (j + e)) * C::TPI + sub >= vis) x0 = 0;
+                if (tok0 + (2 * (j + e) + 1) * C::TPI + sub >= vis) x1 = 0;
+              }
+              const uint32_t vd0 = __builtin_amdgcn_perm(x1, x0, 0x05040100);
+              const uint32_t vd1 = __builtin_amdgcn_perm(x1, x0, 0x07060302);
+#pragma unroll
+              for (int hh = 0; hh < GM; ++hh) {
+                const uint32_t p2 = pp[hh][e];
+                o[hh][0] = dot2_bf16(p2, vd0, o[hh][0]);
+                o[hh][1] = dot2_bf16(p2, vd1, o[hh][1]);
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < C::VLD; kk += 4) {
+            float4 pv[GM];
+#pragma unroll
+            for (int hh = 0; hh < GM; ++hh)
+              pv[hh] = *(const float4*)(my_p + ((hh * C::TPI + sub) * C::VLD + kk) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v0, v1;
+              unpack_v(s.v[kk + e], v0, v1);
+              if constexpr (MASK) {
+                if (tok0 + (kk + e) * C::TPI + sub >= vis) v0 = v1 = 0.f;
+              }
+#pragma unroll
+              for (int hh = 0; hh < GM; ++hh) {
+                const float pr = e == 0 ? pv[hh].x : e == 1 ? pv[hh].y : e == 2 ? pv[hh].z : pv[hh].w;
+                o[hh][0] = fmaf(pr, v0, o[hh][0]);
+                o[hh][1] = fmaf(pr, v1, o[hh][1]);
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
+      auto step = [&](const Stage& s, int jblk) {
+        if (jblk * kBlock + kBlock > vis)
+          compute(std::true_type{}, s, jblk);
+        else
+          compute(std::false_type{}, s, jblk);
+      };
+
+      // Blocks jb .. je-1, 64 ids at a time (split items have at most 32).
+      const int n = cur.je - cur.jb;
+      for (int k0 = 0; k0 < n; k0 += kWave) {
+        if (k0 > 0) btv = fetch_ids(a, cur, k0, lane);
+        if (btv < 0 || btv >= a.num_blocks) {
+          btv = 0;
+          bad = true;
+        }
+        const int nb = min(kWave, n - k0);
+        const int jfirst = cur.jb + k0;
+        Stage sa, sb;
+        load(sa, __builtin_amdgcn_readlane(btv, 0));
+        if (nb > 1) load(sb, __builtin_amdgcn_readlane(btv, 1));
+        for (int k = 0; k < nb; k += 2) {
+          step(sa, jfirst + k);
+          if (k + 2 < nb) load(sa, __builtin_amdgcn_readlane(btv, k + 2));
+          if (k + 1 < nb) {
+            step(sb, jfirst + k + 1);
+            if (k + 3 < nb) load(sb, __builtin_amdgcn_readlane(btv, k + 3));
+          }
+        }
+      }
+
+      // Finish: per-head (m, l) through LDS, then out or the partial.
+      const bool wave_bad = __any(bad);
+#pragma unroll
+      for (int k = 0; k < HPL; ++k) {
+        const float lt = pass_sum<LPT>(lsum[k]);
+        if (tk == 0 && LN::writer(cq)) ml_lds[w][LN::head(cq, k)] = make_float2(mref[k], lt);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (wave_bad && lane == 0) atomicOr(a.err, PKV_DEVERR_BLOCK_ID);
 #pragma unroll
-      for (int kk = 0; kk < C::VLD; kk += 4) {
-        float4 pv[GM];
-#pragma unroll
-        for (int hh = 0; hh < GM; ++hh) pv[hh] = *(const float4*)&p_lds[w][hh][sub * C::VLD + kk];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v0, v1;
-          unpack_v(s.v[kk + e], v0, v1);
-          if (tail && tok0 + (kk + e) * C::TPI + sub >= vis) v0 = v1 = 0.f;
-#pragma unroll
-          for (int hh = 0; hh < GM; ++hh) {
-            const float pr = e == 0 ? pv[hh].x : e == 1 ? pv[hh].y : e == 2 ? pv[hh].z : pv[hh].w;
-            o[hh][0] = fmaf(pr, v0, o[hh][0]);
-            o[hh][1] = fmaf(pr, v1, o[hh][1]);
+      for (int hh = 0; hh < GM; ++hh) {
+        if (C::TPI == 2) {
+          o[hh][0] += __shfl_xor(o[hh][0], 32);
+          o[hh][1] += __shfl_xor(o[hh][1], 32);
+        }
+        if (hh < nh && sub == 0) {
+          const float2 ml = ml_lds[w][hh];
+          if (cur.slot0 < 0) {
+            const float inv = wave_bad ? __builtin_nanf("") : 1.f / ml.y;
+            store_out<BF16>(a.out, out_row + hh * D + d0, o[hh][0] * inv);
+            store_out<BF16>(a.out, out_row + hh * D + d0 + 1, o[hh][1] * inv);
+          } else {
+            const size_t sidx = (size_t)(cur.slot0 + cur.part) * a.num_q_heads + cur.h0 + hh;
+            const float nan_or_0 = wave_bad ? __builtin_nanf("") : 0.f;
+            *(float2*)(a.part_o + sidx * D + d0) = make_float2(o[hh][0] + nan_or_0, o[hh][1] + nan_or_0);
+            if (dl == 0) a.part_ml[sidx] = ml;
           }
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
-    for (int kdone = 0; kdone < nmine; kdone += kWave) {
-      const int nb = min(kWave, nmine - kdone);
-      int btv = lane < nb ? bt_row[jb + w + 4 * (kdone + lane)] : 0;
-      if (btv < 0 || btv >= a.num_blocks) {
-        btv = 0;
-        bad = true;
-      }
-      const int jfirst = jb + w + 4 * kdone;
-      Stage sa, sb;
-      load(sa, __builtin_amdgcn_readlane(btv, 0));
-      for (int k = 0; k < nb; k += 2) {
-        if (k + 1 < nb) load(sb, __builtin_amdgcn_readlane(btv, k + 1));
-        compute(sa, jfirst + 4 * k);
-        if (k + 1 < nb) {
-          if (k + 2 < nb) load(sa, __builtin_amdgcn_readlane(btv, k + 2));
-          compute(sb, jfirst + 4 * (k + 1));
-        }
-      }
     }
-
-    // Wave state -> LDS.
-    const bool wave_bad = __builtin_amdgcn_read_exec() != 0 && __any(bad);
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      l[hh] = wave_sum(l[hh]) * 0.25f;  // every token was counted by its 4 lanes
-      if (C::TPI == 2) {
-        o[hh][0] += __shfl_xor(o[hh][0], 32);
-        o[hh][1] += __shfl_xor(o[hh][1], 32);
-      }
-      if (sub == 0) {
-        comb_o[w][hh][d0] = o[hh][0];
-        comb_o[w][hh][d0 + 1] = o[hh][1];
-      }
-      if (lane == 0) {
-        comb_m[w][hh] = m[hh];
-        comb_l[w][hh] = l[hh];
-      }
-    }
-    if (lane == 0) comb_bad[w] = wave_bad;
-    __syncthreads();
-    const bool any_bad = comb_bad[0] | comb_bad[1] | comb_bad[2] | comb_bad[3];
-    if (any_bad && threadIdx.x == 0) atomicOr(a.err, PKV_DEVERR_BLOCK_ID);
-    for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
-      const int hh = idx / D;
-      const int d = idx - hh * D;
-      float M = comb_m[0][hh];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, comb_m[ww][hh]);
-      float den = 0.f, num = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float f = comb_m[ww][hh] == -INFINITY ? 0.f : fast_exp2(comb_m[ww][hh] - M);
-        den = fmaf(f, comb_l[ww][hh], den);
-        num = fmaf(f, comb_o[ww][hh][d], num);
-      }
-      if (any_bad) num = __builtin_nanf("");
-      if (slot0 < 0) {
-        store_out<BF16>(a.out, out_row + idx, num / den);
-      } else {
-        const size_t s = (size_t)(slot0 + part) * a.num_q_heads + h0 + hh;
-        a.part_o[s * D + d] = num;
-        if (d == 0) a.part_ml[s] = make_float2(M, den);
-      }
-    }
-    __syncthreads();
+    if (!has_next) break;
+    it = nx;
+    cur = nxt;
+    btv = btv_next;
   }
 }
 
@@ -363,30 +551,47 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams a) {
   }
 }
 
-template <bool BF16, int D>
-int launch_rows_d(const RowParams& p, int64_t grid, hipStream_t s) {
-  const int gm = p.head_groups > 1 ? kMaxGroupRegs : p.group;
-  if (gm <= 1)
-    hipLaunchKernelGGL((row_attn_kernel<BF16, D, 1>), dim3(grid), dim3(256), 0, s, p);
-  else if (gm <= 2)
-    hipLaunchKernelGGL((row_attn_kernel<BF16, D, 2>), dim3(grid), dim3(256), 0, s, p);
-  else if (gm <= 4)
-    hipLaunchKernelGGL((row_attn_kernel<BF16, D, 4>), dim3(grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((row_attn_kernel<BF16, D, 8>), dim3(grid), dim3(256), 0, s, p);
+// Persistent grid: as many 4-wave workgroups as fit on the device at once,
+// but no more than the work items need.
+template <typename K>
+int64_t persistent_grid(K kernel, int64_t bound_wgs, int cus) {
+  static std::atomic<int> occ_cache{0};
+  int occ = occ_cache.load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ <= 0)
+      occ = 2;
+    occ_cache.store(occ, std::memory_order_relaxed);
+  }
+  return std::max<int64_t>(1, std::min<int64_t>(bound_wgs, (int64_t)cus * occ));
+}
+
+template <bool BF16, int D, int GM>
+int launch_rows_g(const RowParams& p, int64_t bound_waves, int cus, hipStream_t s) {
+  auto k = row_attn_kernel<BF16, D, GM>;
+  const int64_t grid = persistent_grid(k, (bound_waves + 3) / 4, cus);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <bool BF16, int D>
+int launch_rows_d(const RowParams& p, int64_t bound_waves, int cus, hipStream_t s) {
+  const int gm = p.head_groups > 1 ? kMaxGroupRegs : p.group;
+  if (gm <= 1) return launch_rows_g<BF16, D, 1>(p, bound_waves, cus, s);
+  if (gm <= 2) return launch_rows_g<BF16, D, 2>(p, bound_waves, cus, s);
+  if (gm <= 4) return launch_rows_g<BF16, D, 4>(p, bound_waves, cus, s);
+  return launch_rows_g<BF16, D, 8>(p, bound_waves, cus, s);
 }
 
 }  // namespace
 
-int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t grid,
+int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bound_waves, int cus,
                 hipStream_t stream) {
-  if (grid <= 0) return 0;
+  if (bound_waves <= 0) return 0;
   const bool bf16 = dtype == PKV_BF16;
-  if (head_dim == 64) return bf16 ? launch_rows_d<true, 64>(p, grid, stream)
-                                  : launch_rows_d<false, 64>(p, grid, stream);
-  return bf16 ? launch_rows_d<true, 128>(p, grid, stream)
-              : launch_rows_d<false, 128>(p, grid, stream);
+  if (head_dim == 64) return bf16 ? launch_rows_d<true, 64>(p, bound_waves, cus, stream)
+                                  : launch_rows_d<false, 64>(p, bound_waves, cus, stream);
+  return bf16 ? launch_rows_d<true, 128>(p, bound_waves, cus, stream)
+              : launch_rows_d<false, 128>(p, bound_waves, cus, stream);
 }
 
 int launch_reduce(const ReduceParams& p, int32_t dtype, int32_t head_dim, int64_t grid,

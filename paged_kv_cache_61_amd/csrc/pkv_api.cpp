@@ -236,10 +236,10 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   rp.num_blocks = num_blocks;
   rp.max_blocks_per_req = max_blocks_per_req;
   {
-    const int64_t bound = ws.cap_row_items * num_kv_heads * rp.head_groups;
-    const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 8);
+    const int64_t bound_waves = ws.cap_row_items * num_kv_heads * rp.head_groups;
     mark(PKV_PHASE_ROWS, 0);
-    if (pkv::launch_rows(rp, dtype, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "row launch failed");
+    if (pkv::launch_rows(rp, dtype, head_dim, bound_waves, cus, s))
+      return fail(PKV_ERR_LAUNCH, "row launch failed");
     mark(PKV_PHASE_ROWS, 1);
   }
   mark(PKV_PHASE_REDUCE, 0);

@@ -78,11 +78,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 PKV_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 PKV_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-PKV_DEV uint16_t f32_to_bf16(float f) {  // round to nearest even; NaN stays NaN
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even, NaN stays NaN (v_cvt_pk_bf16_f32).
+PKV_DEV uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // a.lo*b.lo + a.hi*b.hi + c, bf16 products accumulated in fp32.
@@ -96,6 +94,7 @@ constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;   // rotate right by 4 inside each row of 16 lanes
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i inside each group of 8
 
 template <int CTRL>
 PKV_DEV float dpp_mov(float x) {

@@ -70,7 +70,8 @@ int launch_kv_write(const void* k, const void* v, const int64_t* slot_mapping, v
                     int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
                     hipStream_t stream);
 int launch_plan(const PlanParams& p, hipStream_t stream);
-int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t grid,
+// bound_waves: upper bound on row work items (one wave each); cus: compute units.
+int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bound_waves, int cus,
                 hipStream_t stream);
 int launch_reduce(const ReduceParams& p, int32_t dtype, int32_t head_dim, int64_t grid,
                   hipStream_t stream);

@@ -62,10 +62,21 @@ PKV_DEV f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Pack two fp32 to a bf16 pair (round to nearest even), low element first.
+// Pack two fp32 to a bf16 pair (round to nearest even, v_cvt_pk_bf16_f32),
+// low element first.
 PKV_DEV uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// A row's reference max moves only when a tile's max exceeds it by more than
+// this (log2 units); p = exp2(s - ref) stays <= 2^8 and O is rescaled rarely.
+constexpr float kRefSlack = 8.f;
+
+// LDS row of head_dim element d in the V^T tile.  The XOR spreads both the
+// staging stores (rows 8 apart) and the MFMA operand reads (16 consecutive
+// rows) over distinct banks with the 144-byte pitch.
+PKV_DEV int vt_row(int d) { return d ^ ((d >> 4) & 7); }
 
 struct TileRegs {
   u32x4 k[4];  // K: chunk (t & 15) of key (t >> 4) + 16 j of the tile
@@ -78,7 +89,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
+  // wave index, made visibly wave-uniform so everything derived from it is scalar
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane >> 5;        // which 8-wide k group of the MFMA operand
   const int lrow = lane & 31;        // MFMA row / column owned by the lane
   const int G = a.group;
@@ -91,6 +103,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
   const char* kbase = (const char*)a.cache;
   const char* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
   const float sl2 = a.scale_log2;
+  const float csc = fabsf(sl2);
 
   // staging roles
   const int kchunk = tid & 15, krow = tid >> 4;   // K: chunk, key within a block
@@ -115,53 +128,45 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
     const int pos_abs = c + row0 + pos;
     const size_t qrow = ((size_t)(qs + row0 + pos) * a.num_q_heads + g * G + head) * kD;
 
+    // With a negative scale, q's sign is flipped (exact in bf16) and |scale|
+    // used, so the row max of the raw dots is the max of the scaled scores.
+    const uint32_t qsign = sl2 < 0.f ? 0x80008000u : 0u;
     u32x4 qf[kKSteps];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
-      qf[ks] = row_ok ? *(const u32x4*)((const uint16_t*)a.q + qrow + ks * 16 + 8 * half)
+      qf[ks] = row_ok ? (*(const u32x4*)((const uint16_t*)a.q + qrow + ks * 16 + 8 * half) ^ qsign)
                       : u32x4{0, 0, 0, 0};
 
     if (tid == 0) tile_bad = 0;
     bool bad = false;
 
+    // Per-lane byte offsets inside a cache block (token row, kv head g, chunk).
+    const uint32_t koff = krow * (uint32_t)row_bytes + g * kD * 2 + kchunk * 16;
+    const uint32_t voff = 4 * (vkg & 3) * (uint32_t)row_bytes + g * kD * 2 + vdg * 16;
+    // Buffer descriptor over the first `nvalid` token rows of logical block
+    // b of the request: reads of rows past the chunk's last key return 0.
+    auto block_rsrc = [&](const char* half_base, int b, int nvalid) {
+      if (nvalid <= 0) return make_rsrc(half_base, 0);
+      int phys = bt[b];
+      if (phys < 0 || phys >= a.num_blocks) {
+        bad = true;
+        phys = 0;
+      }
+      return make_rsrc(half_base + (size_t)phys * blk_bytes, (uint32_t)min(nvalid, kBlock) * (uint32_t)row_bytes);
+    };
     auto load_tile = [&](TileRegs& tr, int tile) {
       const int kv0 = tile * kPfKeys;
       const int b0 = kv0 / kBlock;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int key = kv0 + 16 * j + krow;
-        u32x4 x = {0, 0, 0, 0};
-        if (key < kv_end) {
-          int phys = bt[b0 + j];
-          if (phys < 0 || phys >= a.num_blocks) {
-            bad = true;
-            phys = 0;
-          }
-          x = *(const u32x4*)(kbase + (size_t)phys * blk_bytes + (size_t)krow * row_bytes +
-                              (size_t)g * kD * 2 + kchunk * 16);
-        }
-        tr.k[j] = x;
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, b0 + j, kv_end - (kv0 + 16 * j));
+        tr.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, 0);
       }
-      {
-        const int key0 = kv0 + 4 * vkg;
-        int phys = 0;
-        if (key0 < kv_end) {
-          phys = bt[b0 + (vkg >> 2)];
-          if (phys < 0 || phys >= a.num_blocks) {
-            bad = true;
-            phys = 0;
-          }
-        }
+      // V: wave w stages block w of the tile (4 keys x 8 head_dim per lane).
+      const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, b0 + w, kv_end - (kv0 + 16 * w));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 x = {0, 0, 0, 0};
-          if (key0 + j < kv_end)
-            x = *(const u32x4*)(vbase + (size_t)phys * blk_bytes +
-                                (size_t)((key0 + j) & (kBlock - 1)) * row_bytes +
-                                (size_t)g * kD * 2 + vdg * 16);
-          tr.v[j] = x;
-        }
-      }
+      for (int j = 0; j < 4; ++j)
+        tr.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + j * (uint32_t)row_bytes, 0, 0);
     };
 
     auto store_tile = [&](const TileRegs& tr, int buf) {
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
           lo = __builtin_amdgcn_perm(x1, x0, 0x05040100);  // low halves of x0, x1
           hi = __builtin_amdgcn_perm(x3, x2, 0x05040100);
         }
-        *(u32x2*)(vl + (8 * vdg + e) * kVPitch + col * 2) = u32x2{lo, hi};
+        *(u32x2*)(vl + vt_row(8 * vdg + e) * kVPitch + col * 2) = u32x2{lo, hi};
       }
     };
 
@@ -212,51 +217,54 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
       // S^T = K Q^T for the two 32-key halves of the tile.
       f32x16 sacc[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
+      for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
           const u32x4 kf = *(const u32x4*)(kl + (kt * 32 + lrow) * kKPitch + (ks * 16 + 8 * half) * 2);
           sacc[kt] = mfma32(kf, qf[ks], sacc[kt]);
         }
-      }
 
-      // Scale, causal mask on tiles that reach past the first row's position.
-      const bool diag = kv0 + kPfKeys - 1 > c + row0;
+      // Causal mask only on tiles that reach past the first row's position,
+      // then the online softmax on raw dots: p = exp2(dot*|scale|*log2 e - ref).
+      if (kv0 + kPfKeys - 1 > c + row0) {
+        const int rel = pos_abs - kv0 - 4 * half;  // key index limit for this lane
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kt * 32 + 8 * (i >> 2) + (i & 3) > rel) sacc[kt][i] = -INFINITY;
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float s = sacc[kt][i] * sl2;
-          if (diag) {
-            const int key = kv0 + kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key > pos_abs) s = -INFINITY;
-          }
-          sacc[kt][i] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kt][i] - m_new);
-          sacc[kt][i] = p;
-          psum += p;
-        }
-      l_run = l_run * alpha + psum;
-      if (__any(alpha != 1.f)) {
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kt][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * csc;
+      if (__any(tmax > m_run + kRefSlack)) {  // move the reference max (rare)
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kDTiles; ++dt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       }
+      const float neg_m = -m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], csc, neg_m));
+          sacc[kt][i] = p;
+          psum += p;
+        }
+      l_run += psum;
 
       // P^T operands: 16 keys per k-step, 8 per lane, taken from S^T values
       // 8*(ks & 1) .. +7 of half ks >> 1.
@@ -271,10 +279,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
       }
       // O^T += V^T P^T
 #pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 vf = *(const u32x4*)(vl + (dt * 32 + lrow) * kVPitch + (ks * 16 + 8 * half) * 2);
+        for (int dt = 0; dt < kDTiles; ++dt) {
+          const u32x4 vf = *(const u32x4*)(vl + vt_row(dt * 32 + lrow) * kVPitch + (ks * 16 + 8 * half) * 2);
           oacc[dt] = mfma32(vf, pf[ks], oacc[dt]);
         }
 
