@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="CPU seconds the oracle baseline may spend on its sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain device-to-device copy of known size instead (HBM calibration)")
+    ap.add_argument("--copy-gib", type=float, default=4.0)
     return ap.parse_args()
 
 
@@ -120,8 +123,49 @@ def cpu_baseline(wl, acct, budget_s):
             "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
 
 
+def copy_probe(args):
+    """A plain copy kernel of known size: the practical HBM rate, and the
+    reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = int(args.copy_gib * (1 << 30)) // 4
+    src = torch.randn(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    nbytes = 2 * n * 4
+    print(json.dumps({"probe": "device copy (torch copy_)", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                      "frac_of_8TBs": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per row-kernel launch from the committed PMC summary, if it was
+    taken on this workload and on the current decode kernel source; else None."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "decode_llama7b_bs64_traffic.json")
+    src_path = os.path.join(ROOT, "paged_kv_cache_61_amd", "csrc", "decode.hip")
+    if workload != 2 or not os.path.exists(rec_path):
+        return None
+    rec = json.load(open(rec_path))
+    if hashlib.sha256(open(src_path, "rb").read()).hexdigest() != rec.get("decode_hip_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -224,7 +268,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "algorithmic_bytes_per_launch": acct["decode_bytes"],
             "avg_launch_ms": round(phase_ms["rows"], 5),
         },
