@@ -200,9 +200,10 @@ struct RowItem {
 };
 
 template <int GM>
-PKV_DEV RowItem fetch_item(const RowParams& a, int64_t it, int per_pair) {
+PKV_DEV RowItem fetch_item(const RowParams& a, int64_t it, int per_pair, int n_head) {
   RowItem d;
-  const int4 item = a.items[it / per_pair];
+  const int64_t e = it / per_pair;
+  const int4 item = e < n_head ? a.items[e] : a.items_tail[e - n_head];
   const int rem = (int)(it % per_pair);
   d.g = rem / a.head_groups;
   const int hg = rem - d.g * a.head_groups;
@@ -232,9 +233,13 @@ PKV_DEV int fetch_ids(const RowParams& a, const RowItem& d, int k0, int lane) {
 }
 
 // Each wave is an independent persistent worker: it takes work items
-// gw, gw + NW, ... (gw = global wave index, NW = waves in the grid) and,
-// while it streams one item's blocks, already holds the next item's
-// descriptor and block ids, so switching items costs one memory round trip.
+// gw, gw + NW, ... (gw = global wave index, NW = waves in the grid; items are
+// listed longest first) and, while it streams one item's blocks, already
+// holds the next item's descriptor and block ids, so switching items costs one
+// memory round trip.  Consecutive items (the heads of one partition) go to
+// the 4 waves of one workgroup, so a CU reads adjacent head rows together.
+// (A shared atomic work counter was measured slower: claims serialise on one
+// address.)
 template <bool BF16, int D, int GM>
 __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
   using C = RowCfg<BF16, D>;
@@ -261,25 +266,27 @@ __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
 
   const int per_pair = a.num_kv_heads * a.head_groups;
   const int64_t total = (int64_t)a.hdr[kHdrRowItems] * per_pair;
-  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int n_head = a.hdr[kHdrRowHead];
   const uint32_t row_stride = (uint32_t)a.num_kv_heads * C::ROWB;  // bytes between token rows
   const uint32_t blk_bytes = kBlock * row_stride;
   const char* kbase = (const char*)a.cache;
   const char* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
   char* my_p = p_lds[w];
 
-  int64_t it = (int64_t)blockIdx.x * 4 + w;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t it = (int64_t)blockIdx.x * 4 + w;
   if (it >= total) return;
-  RowItem cur = fetch_item<GM>(a, it, per_pair);
+  int64_t nx = it + nw;
+  RowItem cur = fetch_item<GM>(a, it, per_pair, n_head);
   int btv = fetch_ids(a, cur, 0, lane);
 
   while (true) {
-    const int64_t nx = it + nw;
     const bool has_next = nx < total;
+    const int64_t nx2 = nx + nw;
     RowItem nxt = cur;
     int btv_next = 0;
     if (has_next) {  // prefetch: consumed only after this item
-      nxt = fetch_item<GM>(a, nx, per_pair);
+      nxt = fetch_item<GM>(a, nx, per_pair, n_head);
       btv_next = fetch_ids(a, nxt, 0, lane);
     }
     const size_t out_row = ((size_t)cur.t * a.num_q_heads + cur.h0) * D;
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (!has_next) break;
-    it = nx;
+    nx = nx2;
     cur = nxt;
     btv = btv_next;
   }

@@ -180,6 +180,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   pp.prefill_tile_rows = (int32_t)tile_rows;
   pp.hdr = hdr;
   pp.row_items = (int4*)(wsb + ws.row_items);
+  pp.row_items_tail = (int4*)(wsb + ws.row_items_tail);
   pp.prefill_items = (int4*)(wsb + ws.prefill_items);
   pp.reduce_items = (int4*)(wsb + ws.reduce_items);
   pp.cap_row_items = ws.cap_row_items;
@@ -224,6 +225,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   rp.qsl = query_start_loc;
   rp.nct = num_computed_tokens;
   rp.items = pp.row_items;
+  rp.items_tail = pp.row_items_tail;
   rp.hdr = hdr;
   rp.part_o = (float*)(wsb + ws.part_o);
   rp.part_ml = (float2*)(wsb + ws.part_ml);

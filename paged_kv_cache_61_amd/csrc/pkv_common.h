@@ -12,7 +12,7 @@ constexpr int kBlock = 16;        // tokens per cache block (fixed)
 constexpr int kWave = 64;         // CDNA wavefront width
 constexpr int kSplitTokens = 512; // split-KV partition length of a decode row
 constexpr int kSplitBlocks = kSplitTokens / kBlock;
-constexpr int kMaxGroupRegs = 8;  // query heads per kv head handled in one pass
+constexpr int kMaxGroupRegs = 4;  // query heads per kv head handled by one wave
 
 // Header words at the start of the workspace (int32).
 enum HdrWord {
@@ -21,6 +21,7 @@ enum HdrWord {
   kHdrPrefillItems = 2,
   kHdrReduceItems = 3,
   kHdrSlots = 4,
+  kHdrRowHead = 5,      // row items in the first region (the rest are in the tail region)
 };
 constexpr size_t kHdrBytes = 256;
 
@@ -34,7 +35,7 @@ constexpr int kNanRow = -2;
 // (relative to the request), z = rows in the tile, w = unused.
 
 struct WsLayout {
-  size_t row_items, prefill_items, reduce_items, part_ml, part_o, total;
+  size_t row_items, row_items_tail, prefill_items, reduce_items, part_ml, part_o, total;
   int64_t cap_row_items, cap_prefill_items, cap_reduce, cap_slots;
 };
 
@@ -55,6 +56,7 @@ inline WsLayout ws_layout(int64_t num_reqs, int64_t num_tokens, int64_t num_q_he
   (void)max_query_len;
   size_t off = kHdrBytes;
   w.row_items = off;      off = align_up(off + sizeof(int32_t) * 4 * w.cap_row_items, 256);
+  w.row_items_tail = off; off = align_up(off + sizeof(int32_t) * 4 * w.cap_row_items, 256);
   w.prefill_items = off;  off = align_up(off + sizeof(int32_t) * 4 * w.cap_prefill_items, 256);
   w.reduce_items = off;   off = align_up(off + sizeof(int32_t) * 4 * w.cap_reduce, 256);
   w.part_ml = off;        off = align_up(off + sizeof(float) * 2 * w.cap_slots * num_q_heads, 256);

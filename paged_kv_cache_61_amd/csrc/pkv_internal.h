@@ -21,6 +21,7 @@ struct PlanParams {
   int32_t prefill_tile_rows; // query rows per prefill tile
   int32_t* hdr;
   int4* row_items;
+  int4* row_items_tail;
   int4* prefill_items;
   int4* reduce_items;
   int64_t cap_row_items, cap_prefill_items, cap_reduce, cap_slots;
@@ -33,8 +34,9 @@ struct RowParams {
   const int32_t* block_table;
   const int32_t* qsl;
   const int32_t* nct;
-  const int4* items;
-  const int32_t* hdr;
+  const int4* items;       // first region (long items)
+  const int4* items_tail;  // second region
+  int32_t* hdr;
   float* part_o;
   float2* part_ml;
   int32_t* err;
@@ -59,7 +61,7 @@ struct PrefillParams {
   const int32_t* qsl;
   const int32_t* nct;
   const int4* items;
-  const int32_t* hdr;
+  int32_t* hdr;
   int32_t* err;
   float scale_log2;
   int32_t num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_req;

@@ -109,6 +109,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
   const int kchunk = tid & 15, krow = tid >> 4;   // K: chunk, key within a block
   const int vdg = tid & 15, vkg = tid >> 4;       // V: 8-wide head_dim group, 4-key group
 
+  // Persistent grid over items listed longest first.  With 8 kv heads and a
+  // grid that is a multiple of 8, workgroup b (on XCD b mod 8) only ever takes
+  // items of head b mod 8, so an XCD's L2 serves one head's K/V to all of its
+  // query tiles.
   for (int64_t it = blockIdx.x; it < total; it += gridDim.x) {
     const int4 item = a.items[it / Hkv];
     const int g = (int)(it % Hkv);
