@@ -232,12 +232,13 @@ PKV_DEV int fetch_ids(const RowParams& a, const RowItem& d, int k0, int lane) {
   return j < d.je ? a.block_table[(size_t)d.r * a.max_blocks_per_req + j] : 0;
 }
 
-// Each wave is an independent persistent worker: it takes work items
-// gw, gw + NW, ... (gw = global wave index, NW = waves in the grid; items are
-// listed longest first) and, while it streams one item's blocks, already
-// holds the next item's descriptor and block ids, so switching items costs one
-// memory round trip.  Consecutive items (the heads of one partition) go to
-// the 4 waves of one workgroup, so a CU reads adjacent head rows together.
+// Each wave is an independent persistent worker: in round k it takes item
+// k*NW + gw or, in odd rounds, k*NW + NW-1-gw (gw = global wave index, NW =
+// waves in the grid; items are listed longest first), and while it streams
+// one item's blocks it already holds the next item's descriptor and block
+// ids, so switching items costs one memory round trip.  Consecutive items
+// (the heads of one partition) go to adjacent waves of one workgroup, so a CU
+// reads adjacent head rows together.
 // (A shared atomic work counter was measured slower: claims serialise on one
 // address.)
 template <bool BF16, int D, int GM>
@@ -273,16 +274,22 @@ __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
   const char* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
   char* my_p = p_lds[w];
 
+  // Serpentine order over the longest-first list: round k takes item
+  // k*NW + gw (k even) or k*NW + NW-1-gw (k odd), which balances the total
+  // work per wave like longest-processing-time-first.
   const int64_t nw = (int64_t)gridDim.x * 4;
-  const int64_t it = (int64_t)blockIdx.x * 4 + w;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + w;
+  auto item_of = [&](int64_t k) { return k * nw + ((k & 1) ? nw - 1 - gw : gw); };
+  int64_t round = 0;
+  const int64_t it = item_of(0);
   if (it >= total) return;
-  int64_t nx = it + nw;
+  int64_t nx = item_of(1);
   RowItem cur = fetch_item<GM>(a, it, per_pair, n_head);
   int btv = fetch_ids(a, cur, 0, lane);
 
   while (true) {
     const bool has_next = nx < total;
-    const int64_t nx2 = nx + nw;
+    const int64_t nx2 = item_of(round + 2);
     RowItem nxt = cur;
     int btv_next = 0;
     if (has_next) {  // prefetch: consumed only after this item
@@ -520,6 +527,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (!has_next) break;
+    ++round;
     nx = nx2;
     cur = nxt;
     btv = btv_next;

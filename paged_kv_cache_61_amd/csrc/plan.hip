@@ -75,92 +75,104 @@ __device__ Counts block_exclusive_scan(Counts c, Counts* total) {
   return ex;
 }
 
+// Buckets of the counting sorts that list work longest first.
+constexpr int kPfBuckets = 4096;          // prefill tiles by KV tiles to read (clamped)
+static_assert(kPfBuckets % 1024 == 0, "buckets split evenly over the plan threads");
+constexpr int kTailBuckets = kSplitBlocks; // partial partitions by block count
+
+struct ReqInfo {
+  int kind;  // 0 none, 1 decode row, 2 prefill tiles, 3 rows per query, 4 NaN rows
+  int qs, ql, L, c, nparts, err;
+};
+
+__device__ ReqInfo classify(const PlanParams& a, int r) {
+  ReqInfo q{0, 0, 0, 0, 0, 1, 0};
+  if (r >= a.num_reqs) return q;
+  q.qs = a.qsl[r];
+  const int qe = a.qsl[r + 1];
+  q.ql = qe - q.qs;
+  q.L = a.seq_lens[r];
+  q.c = a.nct[r];
+  const bool qsl_ok = q.qs >= 0 && q.ql >= 0 && (int64_t)qe <= a.num_tokens && (r > 0 || q.qs == 0);
+  if (!qsl_ok) {
+    q.err |= PKV_DEVERR_QSL;
+  } else if (q.c < 0 || q.L != q.c + q.ql) {
+    q.err |= PKV_DEVERR_SEQ_LEN;
+    q.kind = 4;
+  } else if (q.ql > a.max_query_len || q.L > a.max_seq_len || q.L > a.max_blocks_per_req * kBlock) {
+    q.err |= PKV_DEVERR_LIMITS;
+    q.kind = 4;
+  } else if (q.ql == 1) {
+    q.kind = 1;
+    q.nparts = a.split_decode ? (q.L + kSplitTokens - 1) / kSplitTokens : 1;
+  } else if (q.ql > 1) {
+    q.kind = a.mfma_prefill ? 2 : 3;
+  }
+  if (q.kind == 4 && q.ql == 0) q.kind = 0;
+  return q;
+}
+
+// KV tiles (of 64 keys) a prefill tile starting at query row0 with `rows`
+// rows reads: its bucket in the longest-first order.
+__device__ int pf_bucket(const ReqInfo& q, int row0, int rows) {
+  const int kv_end = q.c + row0 + rows;
+  return min((kv_end + 63) / 64, kPfBuckets - 1);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   __shared__ int err_acc;
+  __shared__ int pf_off[kPfBuckets];
+  __shared__ int tail_off[kTailBuckets];
+  for (int i = threadIdx.x; i < kPfBuckets; i += kPlanThreads) pf_off[i] = 0;
+  if (threadIdx.x < kTailBuckets) tail_off[threadIdx.x] = 0;
   if (threadIdx.x == 0) err_acc = 0;
   __syncthreads();
+
+  // Pass 1: check requests, place decode rows (full partitions) and reduce
+  // items, count everything, and histogram the items that are sorted.
   Counts base{0, 0, 0, 0, 0};
-  const int64_t T = a.num_tokens;
   for (int r0 = 0; r0 < a.num_reqs; r0 += kPlanThreads) {
     const int r = r0 + threadIdx.x;
-    int kind = 0;  // 0 none, 1 decode row, 2 prefill tiles, 3 rows per query, 4 NaN rows
-    int qs = 0, ql = 0, nparts = 1, L = 0;
-    int err = 0;
-    if (r < a.num_reqs) {
-      qs = a.qsl[r];
-      const int qe = a.qsl[r + 1];
-      ql = qe - qs;
-      L = a.seq_lens[r];
-      const int c = a.nct[r];
-      const bool qsl_ok = qs >= 0 && ql >= 0 && (int64_t)qe <= T && (r > 0 || qs == 0);
-      if (!qsl_ok) {
-        err |= PKV_DEVERR_QSL;
-      } else if (c < 0 || L != c + ql) {
-        err |= PKV_DEVERR_SEQ_LEN;
-        kind = 4;
-      } else if (ql > a.max_query_len || L > a.max_seq_len ||
-                 L > a.max_blocks_per_req * kBlock) {
-        err |= PKV_DEVERR_LIMITS;
-        kind = 4;
-      } else if (ql == 1) {
-        kind = 1;
-        nparts = a.split_decode ? (L + kSplitTokens - 1) / kSplitTokens : 1;
-      } else if (ql > 1) {
-        kind = a.mfma_prefill ? 2 : 3;
-      }
-      if (kind == 4 && ql == 0) kind = 0;
-    }
-    // Row items go to two regions so that workers claim the long ones first:
-    // "rows" holds full 512-token partitions and whole rows, "tail" the
-    // partial last partition of each decode row.
+    const ReqInfo q = classify(a, r);
+    int err = q.err;
+    const bool partial_last = q.kind == 1 && q.L % kSplitTokens != 0;
     Counts mine{0, 0, 0, 0, 0};
-    const bool partial_last = kind == 1 && L % kSplitTokens != 0;
-    if (kind == 1) {
-      mine.rows = nparts - (partial_last ? 1 : 0);
+    if (q.kind == 1) {
+      mine.rows = q.nparts - (partial_last ? 1 : 0);
       mine.tail = partial_last ? 1 : 0;
-      if (nparts > 1) {
+      if (q.nparts > 1) {
         mine.reduce = 1;
-        mine.slots = nparts;
+        mine.slots = q.nparts;
       }
-    } else if (kind == 2) {
-      mine.prefill = (ql + a.prefill_tile_rows - 1) / a.prefill_tile_rows;
-    } else if (kind == 3 || kind == 4) {
-      mine.rows = ql;
+    } else if (q.kind == 2) {
+      mine.prefill = (q.ql + a.prefill_tile_rows - 1) / a.prefill_tile_rows;
+    } else if (q.kind == 3 || q.kind == 4) {
+      mine.rows = q.ql;
     }
     Counts tot;
     Counts ex = block_exclusive_scan(mine, &tot);
     ex.rows += base.rows;
-    ex.prefill += base.prefill;
     ex.reduce += base.reduce;
     ex.slots += base.slots;
-    ex.tail += base.tail;
     const bool fits = ex.rows + mine.rows <= a.cap_row_items &&
-                      ex.tail + mine.tail <= a.cap_row_items &&
-                      ex.prefill + mine.prefill <= a.cap_prefill_items &&
-                      ex.reduce + mine.reduce <= a.cap_reduce &&
-                      ex.slots + mine.slots <= a.cap_slots;
+                      base.tail + tot.tail <= a.cap_row_items &&
+                      base.prefill + tot.prefill <= a.cap_prefill_items &&
+                      ex.reduce + mine.reduce <= a.cap_reduce && ex.slots + mine.slots <= a.cap_slots;
     if (!fits) {
       err |= PKV_DEVERR_CAPACITY;
-    } else if (kind == 1) {
-      for (int p = 0; p < nparts; ++p) {
-        const int4 it = make_int4(qs, r, nparts == 1 ? kWholeRow : p, nparts == 1 ? -1 : ex.slots);
-        if (partial_last && p == nparts - 1)
-          a.row_items_tail[ex.tail] = it;
-        else
-          a.row_items[ex.rows + p] = it;
-      }
-      if (nparts > 1) a.reduce_items[ex.reduce] = make_int4(qs, r, nparts, ex.slots);
-    } else if (kind == 2) {
-      // Latest tiles first: they see the most keys (longest work first).
-      for (int j = 0; j < mine.prefill; ++j) {
-        const int tile = mine.prefill - 1 - j;
-        const int row0 = tile * a.prefill_tile_rows;
-        const int rows = min(a.prefill_tile_rows, ql - row0);
-        a.prefill_items[ex.prefill + j] = make_int4(r, row0, rows, 0);
-      }
-    } else if (kind == 3 || kind == 4) {
-      const int z = kind == 3 ? kWholeRow : kNanRow;
-      for (int i = 0; i < ql; ++i) a.row_items[ex.rows + i] = make_int4(qs + i, r, z, -1);
+    } else if (q.kind == 1) {
+      const int nfull = q.nparts - (partial_last ? 1 : 0);
+      for (int p = 0; p < nfull; ++p)
+        a.row_items[ex.rows + p] =
+            make_int4(q.qs, r, q.nparts == 1 ? kWholeRow : p, q.nparts == 1 ? -1 : ex.slots);
+      if (partial_last) atomicAdd(&tail_off[(q.L % kSplitTokens + kBlock - 1) / kBlock - 1], 1);
+      if (q.nparts > 1) a.reduce_items[ex.reduce] = make_int4(q.qs, r, q.nparts, ex.slots);
+    } else if (q.kind == 2) {
+      for (int row0 = 0; row0 < q.ql; row0 += a.prefill_tile_rows)
+        atomicAdd(&pf_off[pf_bucket(q, row0, min(a.prefill_tile_rows, q.ql - row0))], 1);
+    } else if (q.kind == 3 || q.kind == 4) {
+      const int z = q.kind == 3 ? kWholeRow : kNanRow;
+      for (int i = 0; i < q.ql; ++i) a.row_items[ex.rows + i] = make_int4(q.qs + i, r, z, -1);
     }
     if (err) atomicOr(&err_acc, err);
     base.rows += tot.rows;
@@ -170,10 +182,66 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     base.tail += tot.tail;
   }
   __syncthreads();
+  const bool over = base.rows > a.cap_row_items || base.tail > a.cap_row_items ||
+                    base.prefill > a.cap_prefill_items || base.reduce > a.cap_reduce ||
+                    base.slots > a.cap_slots;
+  // Bucket offsets, longest bucket first: thread t owns the 4 buckets at
+  // descending positions 4t .. 4t+3 of the prefill list; thread 0 also does
+  // the 32 tail buckets.
+  {
+    constexpr int kPer = kPfBuckets / kPlanThreads;
+    int n[kPer], local = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      n[i] = pf_off[kPfBuckets - 1 - (kPer * threadIdx.x + i)];
+      local += n[i];
+    }
+    Counts tot;
+    int run = block_exclusive_scan(Counts{local, 0, 0, 0, 0}, &tot).rows;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      pf_off[kPfBuckets - 1 - (kPer * threadIdx.x + i)] = run;
+      run += n[i];
+    }
+    if (threadIdx.x == 0) {
+      int trun = 0;
+      for (int b = kTailBuckets - 1; b >= 0; --b) {
+        const int m = tail_off[b];
+        tail_off[b] = trun;
+        trun += m;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Pass 2: scatter the sorted items (order inside a bucket is irrelevant:
+  // an item's result does not depend on which worker computes it).
+  if (!over) {
+    int slot_base = 0;  // the split rows' partial slots, recomputed as in pass 1
+    for (int r0 = 0; r0 < a.num_reqs; r0 += kPlanThreads) {
+      const int r = r0 + threadIdx.x;
+      const ReqInfo q = classify(a, r);
+      Counts mine{0, 0, 0, 0, 0};
+      if (q.kind == 1 && q.nparts > 1) mine.slots = q.nparts;
+      Counts tot;
+      const int slot0 = block_exclusive_scan(mine, &tot).slots + slot_base;
+      slot_base += tot.slots;
+      if (q.kind == 1 && q.L % kSplitTokens != 0) {
+        const int nb = (q.L % kSplitTokens + kBlock - 1) / kBlock;
+        const int pos = atomicAdd(&tail_off[nb - 1], 1);
+        a.row_items_tail[pos] = q.nparts == 1 ? make_int4(q.qs, r, kWholeRow, -1)
+                                              : make_int4(q.qs, r, q.nparts - 1, slot0);
+      } else if (q.kind == 2) {
+        for (int row0 = 0; row0 < q.ql; row0 += a.prefill_tile_rows) {
+          const int rows = min(a.prefill_tile_rows, q.ql - row0);
+          const int pos = atomicAdd(&pf_off[pf_bucket(q, row0, rows)], 1);
+          a.prefill_items[pos] = make_int4(r, row0, rows, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    const bool over = base.rows > a.cap_row_items || base.tail > a.cap_row_items ||
-                      base.prefill > a.cap_prefill_items ||
-                      base.reduce > a.cap_reduce || base.slots > a.cap_slots;
     // On overflow nothing past the capacity was written; run no work at all.
     a.hdr[kHdrError] = err_acc | (over ? PKV_DEVERR_CAPACITY : 0);
     a.hdr[kHdrRowItems] = over ? 0 : base.rows + base.tail;

@@ -96,8 +96,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
   const int G = a.group;
   const int BQ = kPfRows / G;        // query positions per tile
   const int Hkv = a.num_kv_heads;
-  const int n_items = a.hdr[kHdrPrefillItems];
-  const int64_t total = (int64_t)n_items * Hkv;
   const size_t row_bytes = (size_t)Hkv * kD * 2;           // bytes between token rows
   const size_t blk_bytes = kBlock * row_bytes;
   const char* kbase = (const char*)a.cache;
@@ -109,13 +107,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
   const int kchunk = tid & 15, krow = tid >> 4;   // K: chunk, key within a block
   const int vdg = tid & 15, vkg = tid >> 4;       // V: 8-wide head_dim group, 4-key group
 
-  // Persistent grid over items listed longest first.  With 8 kv heads and a
-  // grid that is a multiple of 8, workgroup b (on XCD b mod 8) only ever takes
-  // items of head b mod 8, so an XCD's L2 serves one head's K/V to all of its
-  // query tiles.
-  for (int64_t it = blockIdx.x; it < total; it += gridDim.x) {
-    const int4 item = a.items[it / Hkv];
-    const int g = (int)(it % Hkv);
+  // Persistent grid over query tiles listed longest first, in serpentine
+  // order (round k takes tile group k*NG + u or k*NG + NG-1-u) so the total
+  // work per workgroup evens out.  Workgroup b keeps kv head b mod Hkv; with 8
+  // kv heads and a grid that is a multiple of 8, workgroup b runs on XCD
+  // b mod 8, so an XCD's L2 serves one head's K/V to all of its query tiles.
+  const int n_entries = a.hdr[kHdrPrefillItems];
+  const int wg_head = blockIdx.x % Hkv;
+  const int64_t ng = gridDim.x / Hkv;            // workgroups per head
+  const int64_t u = blockIdx.x / Hkv;
+  const bool active = u < ng;                    // grid remainder stays idle
+  for (int64_t k = 0; active; ++k) {
+    const int64_t e = k * ng + ((k & 1) ? ng - 1 - u : u);
+    if (e >= n_entries) break;
+    const int4 item = a.items[e];
+    const int g = wg_head;
     const int r = item.x, row0 = item.y, nrows = item.z;
     const int c = a.nct[r];
     const int qs = a.qsl[r];
