@@ -211,10 +211,10 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.group = group;
     fp.num_blocks = num_blocks;
     fp.max_blocks_per_req = max_blocks_per_req;
-    // Two 4-wave workgroups fit per CU; the grid is a multiple of the kv head
+    // One 8-wave workgroup per CU; the grid is a multiple of the kv head
     // count so every workgroup owns one head.
     const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(ws.cap_prefill_items,
-                                                                   (int64_t)cus * 2 / num_kv_heads));
+                                                                   (int64_t)cus / num_kv_heads));
     const int64_t grid = per_head * num_kv_heads;
     if (pkv::launch_prefill(fp, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "prefill launch failed");
   }

@@ -14,9 +14,9 @@
 //
 // Work item = (request, tile of BQ query positions, kv head g).  The G query
 // heads of group g share every K/V tile (GQA by index mapping): the tile's
-// 128 MFMA rows are (position, head) pairs, position-major, BQ = 128 / G.
+// 256 MFMA rows are (position, head) pairs, position-major, BQ = 256 / G.
 //
-// Per 64-key tile, each of the 4 waves owns 32 rows and computes
+// Per 64-key tile, each of the 8 waves owns 32 rows and computes
 //   S^T = K Q^T      (v_mfma_f32_32x32x16_bf16: A = K from LDS, B = Q from
 //                     registers), so lane l holds the scores of row l % 32;
 //   online softmax   per lane: the row max needs one exchange with lane l^32
@@ -28,8 +28,8 @@
 // tile; V is written to LDS transposed ([head_dim][key]) in that same order,
 // so one 16-byte LDS read gives a lane its PV operand.
 // K and V tiles are gathered block by block (4 cache blocks of 16 tokens)
-// with coalesced 16-byte loads into registers one tile ahead, then stored to
-// a double-buffered LDS tile; row pitches are padded (K 272 B, V^T 144 B) so
+// with coalesced 16-byte loads into registers one tile ahead (waves 0-3 load
+// K, waves 4-7 load V), then stored to a double-buffered LDS tile; row pitches are padded (K 272 B, V^T 144 B) so
 // the 16-lane phases of the MFMA operand reads hit distinct banks.
 // Causal masks are applied only on tiles that cross a row's position; keys
 // past the chunk's last position are never loaded (zero-filled), so tail
@@ -46,9 +46,9 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPfRows = 128;   // MFMA rows per workgroup
+constexpr int kPfRows = 256;   // MFMA rows per workgroup (8 waves x 32)
 constexpr int kPfKeys = 64;    // keys per tile (4 cache blocks)
-constexpr int kPfThreads = 256;
+constexpr int kPfThreads = 512;
 constexpr int kD = 128;        // head_dim handled by this kernel
 constexpr int kKPitch = kD * 2 + 16;        // bytes per key row of the K tile
 constexpr int kVPitch = kPfKeys * 2 + 16;   // bytes per head_dim row of the V^T tile
@@ -78,12 +78,14 @@ constexpr float kRefSlack = 8.f;
 // rows) over distinct banks with the 144-byte pitch.
 PKV_DEV int vt_row(int d) { return d ^ ((d >> 4) & 7); }
 
+// Staging registers of one thread: waves 0-3 hold K (chunk t & 15 of key
+// (t >> 4) + 16 j of the tile), waves 4-7 hold V (head_dim elements
+// 8*(u & 15) .. +7 of key 4*(u >> 4) + j, u = t - 256).
 struct TileRegs {
-  u32x4 k[4];  // K: chunk (t & 15) of key (t >> 4) + 16 j of the tile
-  u32x4 v[4];  // V: head_dim elements 8*(t & 15) .. +7 of key 4*(t >> 4) + j
+  u32x4 x[4];
 };
 
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * (kKTile + kVTile)];
   __shared__ int tile_bad;
 
@@ -103,9 +105,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
   const float sl2 = a.scale_log2;
   const float csc = fabsf(sl2);
 
-  // staging roles
-  const int kchunk = tid & 15, krow = tid >> 4;   // K: chunk, key within a block
-  const int vdg = tid & 15, vkg = tid >> 4;       // V: 8-wide head_dim group, 4-key group
+  // staging roles: waves 0-3 stage K, waves 4-7 stage V
+  const bool stage_v = w >= 4;
+  const int st = tid & 255;
+  const int kchunk = st & 15, krow = st >> 4;     // K: chunk, key within a block
+  const int vdg = st & 15, vkg = st >> 4;         // V: 8-wide head_dim group, 4-key group
+  const int vwave = w - 4;                        // V: block of the tile this wave stages
 
   // Persistent grid over query tiles listed longest first, in serpentine
   // order (round k takes tile group k*NG + u or k*NG + NG-1-u) so the total
@@ -167,40 +172,46 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillParams a)
     auto load_tile = [&](TileRegs& tr, int tile) {
       const int kv0 = tile * kPfKeys;
       const int b0 = kv0 / kBlock;
+      if (!stage_v) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, b0 + j, kv_end - (kv0 + 16 * j));
-        tr.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, b0 + j, kv_end - (kv0 + 16 * j));
+          tr.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, 0);
+        }
+      } else {
+        // V: wave 4+i stages block i of the tile (4 keys x 8 head_dim per lane).
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, b0 + vwave, kv_end - (kv0 + 16 * vwave));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tr.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + j * (uint32_t)row_bytes, 0, 0);
       }
-      // V: wave w stages block w of the tile (4 keys x 8 head_dim per lane).
-      const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, b0 + w, kv_end - (kv0 + 16 * w));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        tr.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + j * (uint32_t)row_bytes, 0, 0);
     };
 
     auto store_tile = [&](const TileRegs& tr, int buf) {
       char* kl = lds + buf * (kKTile + kVTile);
       char* vl = kl + kKTile;
+      if (!stage_v) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4*)(kl + (16 * j + krow) * kKPitch + kchunk * 16) = tr.k[j];
-      // V^T: 4 keys of one head_dim element per 8-byte store, keys in the
-      // S^T accumulator order (see the file comment).
-      const int q4 = vkg & 3;
-      const int col = 16 * (vkg >> 2) + 8 * (q4 & 1) + 4 * (q4 >> 1);
+        for (int j = 0; j < 4; ++j) *(u32x4*)(kl + (16 * j + krow) * kKPitch + kchunk * 16) = tr.x[j];
+      } else {
+        // V^T: 4 keys of one head_dim element per 8-byte store, keys in the
+        // S^T accumulator order (see the file comment).
+        const int q4 = vkg & 3;
+        const int col = 16 * (vkg >> 2) + 8 * (q4 & 1) + 4 * (q4 >> 1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int word = e >> 1;
-        const uint32_t x0 = tr.v[0][word], x1 = tr.v[1][word], x2 = tr.v[2][word], x3 = tr.v[3][word];
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = __builtin_amdgcn_perm(x1, x0, 0x07060302);  // high halves of x0, x1
-          hi = __builtin_amdgcn_perm(x3, x2, 0x07060302);
-        } else {
-          lo = __builtin_amdgcn_perm(x1, x0, 0x05040100);  // low halves of x0, x1
-          hi = __builtin_amdgcn_perm(x3, x2, 0x05040100);
+        for (int e = 0; e < 8; ++e) {
+          const int word = e >> 1;
+          const uint32_t x0 = tr.x[0][word], x1 = tr.x[1][word], x2 = tr.x[2][word], x3 = tr.x[3][word];
+          uint32_t lo, hi;
+          if (e & 1) {
+            lo = __builtin_amdgcn_perm(x1, x0, 0x07060302);  // high halves of x0, x1
+            hi = __builtin_amdgcn_perm(x3, x2, 0x07060302);
+          } else {
+            lo = __builtin_amdgcn_perm(x1, x0, 0x05040100);  // low halves of x0, x1
+            hi = __builtin_amdgcn_perm(x3, x2, 0x05040100);
+          }
+          *(u32x2*)(vl + vt_row(8 * vdg + e) * kVPitch + col * 2) = u32x2{lo, hi};
         }
-        *(u32x2*)(vl + vt_row(8 * vdg + e) * kVPitch + col * 2) = u32x2{lo, hi};
       }
     };
 
