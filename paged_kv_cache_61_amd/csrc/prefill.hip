@@ -24,16 +24,21 @@
 //                     folded in; rescaling skipped when no row max moved;
 //   O^T += V^T P^T   (A = V^T from LDS, B = P from the S^T registers packed
 //                     to bf16), so O's rows are again lane-local.
-// The S^T accumulator holds keys in the order 8*(i/4) + 4*(l/32) + i%4 of the
-// tile; V is written to LDS transposed ([head_dim][key]) in that same order,
-// so one 16-byte LDS read gives a lane its PV operand.
-// K and V tiles are gathered block by block (4 cache blocks of 16 tokens)
-// with coalesced 16-byte loads into registers one tile ahead (waves 0-3 load
-// K, waves 4-7 load V), then stored to a double-buffered LDS tile; row pitches are padded (K 272 B, V^T 144 B) so
-// the 16-lane phases of the MFMA operand reads hit distinct banks.
-// Causal masks are applied only on tiles that cross a row's position; keys
-// past the chunk's last position are never loaded (zero-filled), so tail
-// garbage or NaN in the cache cannot reach the output.
+// Tiles of 64 keys stream from the cache into a 4-stage LDS ring with
+// buffer_load ... lds (no staging registers): each wave copies one cache block
+// (16 token rows) of K (waves 0-3) or V (waves 4-7), three tiles ahead of the
+// tile being computed; the buffer descriptor of a block covers only the rows
+// before the chunk's last key, so later rows read as zeros and tail garbage
+// or NaN in the cache never reaches the output.  Rows are stored as they are
+// in the cache (256 bytes for head_dim 128) with the 16-byte chunks of row r
+// XOR-swizzled by r mod 16, so the K operand reads of 16 consecutive keys and
+// the V transpose reads hit distinct banks.  The V^T operand of the second
+// product comes from ds_read_b64_tr_b16 (two 4-key transposed reads per
+// lane), in the key order of the S^T accumulator (8*(i/4) + 4*(l/32) + i%4).
+// One barrier per tile: after it, tile t is complete in LDS and every wave
+// has finished tile t-1, whose ring slot receives tile t+3 once this wave has
+// computed tile t.
+// Causal masks are applied only on tiles that cross a row's position.
 #include <math.h>
 
 #include "pkv_common.h"
@@ -50,12 +55,15 @@ constexpr int kPfRows = 256;   // MFMA rows per workgroup (8 waves x 32)
 constexpr int kPfKeys = 64;    // keys per tile (4 cache blocks)
 constexpr int kPfThreads = 512;
 constexpr int kD = 128;        // head_dim handled by this kernel
-constexpr int kKPitch = kD * 2 + 16;        // bytes per key row of the K tile
-constexpr int kVPitch = kPfKeys * 2 + 16;   // bytes per head_dim row of the V^T tile
-constexpr int kKTile = kPfKeys * kKPitch;   // 17408
-constexpr int kVTile = kD * kVPitch;        // 18432
+constexpr int kRowB = kD * 2;               // bytes of one key row (one kv head)
+constexpr int kHalfTile = kPfKeys * kRowB;  // K or V part of a tile: 16 KiB
+constexpr int kStage = 2 * kHalfTile;       // one ring slot: K then V
+constexpr int kStages = 4;                  // tiles in flight: 3 ahead + the one computed
 constexpr int kKSteps = kD / 16;            // Q.K k-steps
 constexpr int kDTiles = kD / 32;            // O^T row tiles
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define PKV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 PKV_DEV f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -73,20 +81,41 @@ PKV_DEV uint32_t pack_bf16(float lo, float hi) {
 // this (log2 units); p = exp2(s - ref) stays <= 2^8 and O is rescaled rarely.
 constexpr float kRefSlack = 8.f;
 
-// LDS row of head_dim element d in the V^T tile.  The XOR spreads both the
-// staging stores (rows 8 apart) and the MFMA operand reads (16 consecutive
-// rows) over distinct banks with the 144-byte pitch.
-PKV_DEV int vt_row(int d) { return d ^ ((d >> 4) & 7); }
+// Byte offset of 16-byte chunk c of key row `row` inside a K or V tile.
+PKV_DEV int tile_off(int row, int c) { return row * kRowB + ((c ^ (row & 15)) << 4); }
 
-// Staging registers of one thread: waves 0-3 hold K (chunk t & 15 of key
-// (t >> 4) + 16 j of the tile), waves 4-7 hold V (head_dim elements
-// 8*(u & 15) .. +7 of key 4*(u >> 4) + j, u = t - 256).
-struct TileRegs {
-  u32x4 x[4];
-};
+// Wait until at most N vector-memory operations of this wave are in flight
+// (expcnt and lgkmcnt left alone).
+template <int N>
+PKV_DEV void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * (kKTile + kVTile)];
+// buffer_load_dwordx4 ... lds: each lane copies 16 bytes at `voff` inside the
+// buffer described by `rs` (zeros past its end) to LDS address
+// M0 + 16 * lane.  Issued as inline asm so the compiler does not order its
+// own LDS reads behind these loads; completion is awaited explicitly with
+// wait_vmem before the barrier that publishes a tile.
+PKV_DEV void dma_row16(const u32x4& rs, uint32_t voff, const void* lds_dst) {
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)PKV_LDS(lds_dst));
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0v) : "memory");
+}
+
+// Descriptor words for raw (stride 0) buffer access to [base, base + bytes).
+PKV_DEV u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kRsrcWord3};
+}
+
+// The metadata arrays are passed on their own as restrict pointers so their
+// wave-uniform reads become scalar loads, which never wait on the tile stream.
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
+    PrefillParams a, const int4* __restrict__ items, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ nct, const int32_t* __restrict__ block_table) {
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
   __shared__ int tile_bad;
 
   const int tid = threadIdx.x;
@@ -98,19 +127,21 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
   const int G = a.group;
   const int BQ = kPfRows / G;        // query positions per tile
   const int Hkv = a.num_kv_heads;
-  const size_t row_bytes = (size_t)Hkv * kD * 2;           // bytes between token rows
+  const size_t row_bytes = (size_t)Hkv * kRowB;            // bytes between token rows
   const size_t blk_bytes = kBlock * row_bytes;
   const char* kbase = (const char*)a.cache;
   const char* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
   const float sl2 = a.scale_log2;
   const float csc = fabsf(sl2);
 
-  // staging roles: waves 0-3 stage K, waves 4-7 stage V
-  const bool stage_v = w >= 4;
-  const int st = tid & 255;
-  const int kchunk = st & 15, krow = st >> 4;     // K: chunk, key within a block
-  const int vdg = st & 15, vkg = st >> 4;         // V: 8-wide head_dim group, 4-key group
-  const int vwave = w - 4;                        // V: block of the tile this wave stages
+  // Copy role: wave w streams block (w & 3) of each tile, of K (w < 4) or V.
+  const int cblk = w & 3;
+  const char* cbase = w < 4 ? kbase : vbase;
+  const int ldst_half = (w < 4 ? 0 : kHalfTile) + cblk * kBlock * kRowB;
+
+  // V^T transpose-read geometry (per lane, independent of the tile).
+  const int ts = lane & 15;                            // source lane inside a 16-lane group
+  const int tdb = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);  // head_dim offset inside a 32-wide tile
 
   // Persistent grid over query tiles listed longest first, in serpentine
   // order (round k takes tile group k*NG + u or k*NG + NG-1-u) so the total
@@ -118,21 +149,19 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
   // kv heads and a grid that is a multiple of 8, workgroup b runs on XCD
   // b mod 8, so an XCD's L2 serves one head's K/V to all of its query tiles.
   const int n_entries = a.hdr[kHdrPrefillItems];
-  const int wg_head = blockIdx.x % Hkv;
+  const int g = blockIdx.x % Hkv;
   const int64_t ng = gridDim.x / Hkv;            // workgroups per head
   const int64_t u = blockIdx.x / Hkv;
-  const bool active = u < ng;                    // grid remainder stays idle
-  for (int64_t k = 0; active; ++k) {
+  for (int64_t k = 0; u < ng; ++k) {
     const int64_t e = k * ng + ((k & 1) ? ng - 1 - u : u);
     if (e >= n_entries) break;
-    const int4 item = a.items[e];
-    const int g = wg_head;
+    const int4 item = items[e];
     const int r = item.x, row0 = item.y, nrows = item.z;
-    const int c = a.nct[r];
-    const int qs = a.qsl[r];
+    const int c = nct[r];
+    const int qs = qsl[r];
     const int kv_end = c + row0 + nrows;               // keys 0 .. kv_end-1 are read
     const int ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
-    const int* bt = a.block_table + (size_t)r * a.max_blocks_per_req;
+    const int32_t* bt = block_table + (size_t)r * a.max_blocks_per_req;
 
     // this lane's row
     const int rho = w * 32 + lrow;
@@ -146,72 +175,41 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
     // With a negative scale, q's sign is flipped (exact in bf16) and |scale|
     // used, so the row max of the raw dots is the max of the scaled scores.
     const uint32_t qsign = sl2 < 0.f ? 0x80008000u : 0u;
+    // (padding rows load a valid row and zero it)
+    const uint32_t qmask = row_ok ? 0xffffffffu : 0u;
     u32x4 qf[kKSteps];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
-      qf[ks] = row_ok ? (*(const u32x4*)((const uint16_t*)a.q + qrow + ks * 16 + 8 * half) ^ qsign)
-                      : u32x4{0, 0, 0, 0};
+      qf[ks] = (*(const u32x4*)((const uint16_t*)a.q + qrow + ks * 16 + 8 * half) ^ qsign) & qmask;
+    wait_vmem<0>();  // q is in registers before the tile stream starts counting
 
     if (tid == 0) tile_bad = 0;
     bool bad = false;
 
-    // Per-lane byte offsets inside a cache block (token row, kv head g, chunk).
-    const uint32_t koff = krow * (uint32_t)row_bytes + g * kD * 2 + kchunk * 16;
-    const uint32_t voff = 4 * (vkg & 3) * (uint32_t)row_bytes + g * kD * 2 + vdg * 16;
-    // Buffer descriptor over the first `nvalid` token rows of logical block
-    // b of the request: reads of rows past the chunk's last key return 0.
-    auto block_rsrc = [&](const char* half_base, int b, int nvalid) {
-      if (nvalid <= 0) return make_rsrc(half_base, 0);
-      int phys = bt[b];
-      if (phys < 0 || phys >= a.num_blocks) {
-        bad = true;
-        phys = 0;
-      }
-      return make_rsrc(half_base + (size_t)phys * blk_bytes, (uint32_t)min(nvalid, kBlock) * (uint32_t)row_bytes);
-    };
-    auto load_tile = [&](TileRegs& tr, int tile) {
+    // Stream tile `tile` into ring slot tile % kStages: this wave's block,
+    // 4 instructions of 4 token rows; lane L of instruction j carries chunk
+    // (L & 15) ^ row of token row 4j + L/16, so LDS holds the swizzled layout.
+    auto issue_tile = [&](int tile) {
       const int kv0 = tile * kPfKeys;
-      const int b0 = kv0 / kBlock;
-      if (!stage_v) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, b0 + j, kv_end - (kv0 + 16 * j));
-          tr.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, 0);
+      const int nvalid = kv_end - (kv0 + kBlock * cblk);  // rows of this block before kv_end
+      const char* src = cbase;
+      uint32_t nbytes = 0;
+      if (nvalid > 0) {
+        int phys = bt[kv0 / kBlock + cblk];
+        if (phys < 0 || phys >= a.num_blocks) {
+          bad = true;
+          phys = 0;
         }
-      } else {
-        // V: wave 4+i stages block i of the tile (4 keys x 8 head_dim per lane).
-        const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, b0 + vwave, kv_end - (kv0 + 16 * vwave));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          tr.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + j * (uint32_t)row_bytes, 0, 0);
+        src = cbase + (size_t)phys * blk_bytes;
+        nbytes = (uint32_t)min(nvalid, kBlock) * (uint32_t)row_bytes;
       }
-    };
-
-    auto store_tile = [&](const TileRegs& tr, int buf) {
-      char* kl = lds + buf * (kKTile + kVTile);
-      char* vl = kl + kKTile;
-      if (!stage_v) {
+      const u32x4 rs = buffer_desc(src, nbytes);
+      const char* dst = lds + (tile % kStages) * kStage + ldst_half;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *(u32x4*)(kl + (16 * j + krow) * kKPitch + kchunk * 16) = tr.x[j];
-      } else {
-        // V^T: 4 keys of one head_dim element per 8-byte store, keys in the
-        // S^T accumulator order (see the file comment).
-        const int q4 = vkg & 3;
-        const int col = 16 * (vkg >> 2) + 8 * (q4 & 1) + 4 * (q4 >> 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int word = e >> 1;
-          const uint32_t x0 = tr.x[0][word], x1 = tr.x[1][word], x2 = tr.x[2][word], x3 = tr.x[3][word];
-          uint32_t lo, hi;
-          if (e & 1) {
-            lo = __builtin_amdgcn_perm(x1, x0, 0x07060302);  // high halves of x0, x1
-            hi = __builtin_amdgcn_perm(x3, x2, 0x07060302);
-          } else {
-            lo = __builtin_amdgcn_perm(x1, x0, 0x05040100);  // low halves of x0, x1
-            hi = __builtin_amdgcn_perm(x3, x2, 0x05040100);
-          }
-          *(u32x2*)(vl + vt_row(8 * vdg + e) * kVPitch + col * 2) = u32x2{lo, hi};
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int rb = 4 * j + (lane >> 4);                     // token row in the block
+        const uint32_t voff = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ rb) << 4);
+        dma_row16(rs, voff, dst + j * 4 * kRowB);
       }
     };
 
@@ -222,17 +220,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
       for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    TileRegs tr;
-    load_tile(tr, 0);
-    store_tile(tr, 0);
-    __syncthreads();
-
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int buf = tile & 1;
-      const bool more = tile + 1 < ntiles;
-      if (more) load_tile(tr, tile + 1);
-      const char* kl = lds + buf * (kKTile + kVTile);
-      const char* vl = kl + kKTile;
+    auto compute_tile = [&](int tile) {
+      const char* kl = lds + (tile % kStages) * kStage;
+      const char* vl = kl + kHalfTile;
       const int kv0 = tile * kPfKeys;
 
       // S^T = K Q^T for the two 32-key halves of the tile.
@@ -245,7 +235,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
       for (int ks = 0; ks < kKSteps; ++ks)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const u32x4 kf = *(const u32x4*)(kl + (kt * 32 + lrow) * kKPitch + (ks * 16 + 8 * half) * 2);
+          const u32x4 kf = *(const u32x4*)(kl + tile_off(kt * 32 + lrow, 2 * ks + half));
           sacc[kt] = mfma32(kf, qf[ks], sacc[kt]);
         }
 
@@ -287,8 +277,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
         }
       l_run += psum;
 
-      // P^T operands: 16 keys per k-step, 8 per lane, taken from S^T values
-      // 8*(ks & 1) .. +7 of half ks >> 1.
+      // P^T operands: k-step ks covers keys 16*ks + 8*(j/4) + 4*half + j%4,
+      // j = 0..7, i.e. S^T values 8*(ks & 1) .. +7 of half ks >> 1.
       u32x4 pf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -298,17 +288,42 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
                        pack_bf16(sacc[kt][i0 + 4], sacc[kt][i0 + 5]),
                        pack_bf16(sacc[kt][i0 + 6], sacc[kt][i0 + 7])};
       }
-      // O^T += V^T P^T
+      // O^T += V^T P^T; the V^T operand of lane l (head_dim dt*32 + l%32,
+      // keys 16*ks + 8*jj + 4*half + 0..3 for jj = 0, 1) comes from two
+      // transposed reads whose source lanes point at those keys' rows.
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int dt = 0; dt < kDTiles; ++dt) {
-          const u32x4 vf = *(const u32x4*)(vl + vt_row(dt * 32 + lrow) * kVPitch + (ks * 16 + 8 * half) * 2);
-          oacc[dt] = mfma32(vf, pf[ks], oacc[dt]);
+          const int d0 = dt * 32 + tdb;
+          i16x4 t0, t1;
+          {
+            const int key = 16 * ks + 4 * half + (ts >> 2);
+            t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(vl + tile_off(key, d0 >> 3) + (d0 & 7) * 2));
+            t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(vl + tile_off(key + 8, d0 >> 3) + (d0 & 7) * 2));
+          }
+          const u32x2 v0 = __builtin_bit_cast(u32x2, t0), v1 = __builtin_bit_cast(u32x2, t1);
+          oacc[dt] = mfma32(u32x4{v0.x, v0.y, v1.x, v1.y}, pf[ks], oacc[dt]);
         }
+    };
 
-      if (more) store_tile(tr, buf ^ 1);
-      __syncthreads();
+    // Pipeline: tiles t+1 .. t+3 are in flight while tile t is computed.
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    if (ntiles > 2) issue_tile(2);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      // this wave's loads of `tile` have landed (younger tiles may still fly)
+      if (tile + 2 < ntiles)
+        wait_vmem<8>();
+      else if (tile + 1 < ntiles)
+        wait_vmem<4>();
+      else
+        wait_vmem<0>();
+      __builtin_amdgcn_s_barrier();  // all waves: tile complete, tile-1 consumed
+      compute_tile(tile);
+      if (tile + 3 < ntiles) issue_tile(tile + 3);  // into the slot of tile - 1
     }
 
     if (bad) tile_bad = 1;
@@ -332,7 +347,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillParams a)
                                       pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv)};
         }
     }
-    __syncthreads();
+    __syncthreads();  // the ring is reused by the next item
   }
 }
 
@@ -342,7 +357,8 @@ int prefill_tile_rows(int32_t group) { return kPfRows / (group > 0 ? group : 1);
 
 int launch_prefill(const PrefillParams& p, int32_t head_dim, int64_t grid, hipStream_t stream) {
   if (head_dim != kD || grid <= 0) return 1;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.qsl,
+                     p.nct, p.block_table);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
