@@ -30,7 +30,8 @@
  *    a call says "host".  Tensors must be contiguous; q, k, v, out and the
  *    cache must be 16-byte aligned.
  *  - head_dim must be 64 or 128; num_q_heads must be a multiple of
- *    num_kv_heads with num_q_heads / num_kv_heads <= 16.
+ *    num_kv_heads with num_q_heads / num_kv_heads <= 16; paged_attention
+ *    takes at most 240 kv heads.
  *  - stream is a hipStream_t (NULL = the legacy default stream).  Work is only
  *    enqueued: the calls return before the GPU finishes, never synchronise,
  *    never allocate and never free.  The caller keeps every buffer alive until

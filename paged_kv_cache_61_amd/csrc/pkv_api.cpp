@@ -130,8 +130,8 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
   if (num_reqs < 0 || num_tokens < 0)
     return fail(PKV_ERR_DIMS, "num_reqs %lld, num_tokens %lld", num_reqs, num_tokens);
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-      num_q_heads / num_kv_heads > 16)
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_kv_heads > pkv::kMaxKvHeads ||
+      num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16)
     return fail(PKV_ERR_DIMS, "num_q_heads %lld / num_kv_heads %lld", num_q_heads, num_kv_heads);
   if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_DIMS, "head_dim %lld not 64/128", head_dim);
   if (num_blocks <= 0 || max_blocks_per_req <= 0 || max_query_len < 0 || max_seq_len < 0)

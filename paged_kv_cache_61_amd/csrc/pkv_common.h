@@ -22,8 +22,11 @@ enum HdrWord {
   kHdrReduceItems = 3,
   kHdrSlots = 4,
   kHdrRowHead = 5,      // row items in the first region (the rest are in the tail region)
+  kHdrPrefillQueue = 16,  // one prefill work-queue counter per kv head (zeroed by the plan kernel)
 };
-constexpr size_t kHdrBytes = 256;
+constexpr int kMaxKvHeads = 240;  // kv heads with a prefill queue counter in the header
+constexpr size_t kHdrBytes = 1024;
+static_assert((kHdrPrefillQueue + kMaxKvHeads) * 4 <= kHdrBytes, "header too small");
 
 // Row item (int4): x = query row, y = request, z = partition (kWholeRow: all
 // visible keys, kNanRow: metadata was bad, write NaN), w = first partial slot

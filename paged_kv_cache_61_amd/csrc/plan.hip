@@ -241,6 +241,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     }
   }
   __syncthreads();
+  for (int i = threadIdx.x; i < kMaxKvHeads; i += blockDim.x) a.hdr[kHdrPrefillQueue + i] = 0;
   if (threadIdx.x == 0) {
     // On overflow nothing past the capacity was written; run no work at all.
     a.hdr[kHdrError] = err_acc | (over ? PKV_DEVERR_CAPACITY : 0);

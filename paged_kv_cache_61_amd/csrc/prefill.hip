@@ -30,9 +30,13 @@
 // tile being computed; the buffer descriptor of a block covers only the rows
 // before the chunk's last key, so later rows read as zeros and tail garbage
 // or NaN in the cache never reaches the output.  Rows are stored as they are
-// in the cache (256 bytes for head_dim 128) with the 16-byte chunks of row r
-// XOR-swizzled by r mod 16, so the K operand reads of 16 consecutive keys and
-// the V transpose reads hit distinct banks.  The V^T operand of the second
+// in the cache (256 bytes for head_dim 128) with 16-byte chunk c of row r at
+// position c ^ swz(r mod 16), swz = rotate left by one bit in 4 bits: swz is
+// a permutation (the K operand reads of 16 consecutive keys hit 16 distinct
+// positions) that keeps bits 1-3 distinct within each aligned group of 4 rows
+// (a transposed V read, 4 rows x 2 adjacent chunks per 16 lanes, hits 8
+// distinct positions), so neither read conflicts on banks.  (A plain
+// c ^ (r mod 16) makes the transposed reads conflict two ways.)  The V^T operand of the second
 // product comes from ds_read_b64_tr_b16 (two 4-key transposed reads per
 // lane), in the key order of the S^T accumulator (8*(i/4) + 4*(l/32) + i%4).
 // One barrier per tile: after it, tile t is complete in LDS and every wave
@@ -82,7 +86,11 @@ PKV_DEV uint32_t pack_bf16(float lo, float hi) {
 constexpr float kRefSlack = 8.f;
 
 // Byte offset of 16-byte chunk c of key row `row` inside a K or V tile.
-PKV_DEV int tile_off(int row, int c) { return row * kRowB + ((c ^ (row & 15)) << 4); }
+// Chunk-position permutation of row r (mod 16): rotate left by one bit in 4
+// bits, so both the K operand reads and the transposed V reads are free of
+// bank conflicts.
+PKV_DEV int swz(int r) { return ((r << 1) | (r >> 3)) & 15; }
+PKV_DEV int tile_off(int row, int c) { return row * kRowB + ((c ^ swz(row & 15)) << 4); }
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (expcnt and lgkmcnt left alone).
@@ -143,18 +151,23 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   const int ts = lane & 15;                            // source lane inside a 16-lane group
   const int tdb = ((lane >> 4) & 1) * 16 + 4 * (ts & 3);  // head_dim offset inside a 32-wide tile
 
-  // Persistent grid over query tiles listed longest first, in serpentine
-  // order (round k takes tile group k*NG + u or k*NG + NG-1-u) so the total
-  // work per workgroup evens out.  Workgroup b keeps kv head b mod Hkv; with 8
-  // kv heads and a grid that is a multiple of 8, workgroup b runs on XCD
-  // b mod 8, so an XCD's L2 serves one head's K/V to all of its query tiles.
+  // Persistent grid over query tiles listed longest first.  Workgroup b keeps
+  // kv head b mod Hkv; with 8 kv heads and a grid that is a multiple of 8,
+  // workgroup b runs on XCD b mod 8, so an XCD's L2 serves one head's K/V to
+  // all of its query tiles.  The workgroups of a head take the head's tiles
+  // from a queue (an atomic counter that the plan kernel zeroes) in list
+  // order, each as soon as it is free, so the longest tiles are spread first
+  // and the work per workgroup evens out.  The next index is fetched while
+  // the current tile runs.
   const int n_entries = a.hdr[kHdrPrefillItems];
   const int g = blockIdx.x % Hkv;
-  const int64_t ng = gridDim.x / Hkv;            // workgroups per head
-  const int64_t u = blockIdx.x / Hkv;
-  for (int64_t k = 0; u < ng; ++k) {
-    const int64_t e = k * ng + ((k & 1) ? ng - 1 - u : u);
-    if (e >= n_entries) break;
+  int* queue = a.hdr + kHdrPrefillQueue + g;
+  __shared__ int next_item[2];
+  if (tid == 0) next_item[0] = atomicAdd(queue, 1);
+  __syncthreads();
+  int e = next_item[0];
+  for (int par = 1; e < n_entries; par ^= 1) {
+    if (tid == 0) next_item[par] = atomicAdd(queue, 1);
     const int4 item = items[e];
     const int r = item.x, row0 = item.y, nrows = item.z;
     const int c = nct[r];
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rb = 4 * j + (lane >> 4);                     // token row in the block
-        const uint32_t voff = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ rb) << 4);
+        const uint32_t voff = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ swz(rb)) << 4);
         dma_row16(rs, voff, dst + j * 4 * kRowB);
       }
     };
@@ -348,6 +361,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
         }
     }
     __syncthreads();  // the ring is reused by the next item
+    e = next_item[par];
   }
 }
 
