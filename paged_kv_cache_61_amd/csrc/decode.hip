@@ -120,6 +120,15 @@ PKV_DEV void store_out<false>(void* out, size_t idx, float x) {
   ((float*)out)[idx] = x;
 }
 
+// out[idx], out[idx + 1] = x0, x1 in one store (idx even).
+template <bool BF16>
+PKV_DEV void store_out2(void* out, size_t idx, float x0, float x1) {
+  if constexpr (BF16)
+    *(uint32_t*)((uint16_t*)out + idx) = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+  else
+    *(float2*)((float*)out + idx) = make_float2(x0, x1);
+}
+
 // Lanes that share one token's q.k: 4 (each owns a quarter of head_dim), or
 // 8 for groups of 8 heads, which halves the q registers a lane holds.
 template <int GM>
@@ -512,8 +521,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
           const float2 ml = ml_lds[w][hh];
           if (cur.slot0 < 0) {
             const float inv = wave_bad ? __builtin_nanf("") : 1.f / ml.y;
-            store_out<BF16>(a.out, out_row + hh * D + d0, o[hh][0] * inv);
-            store_out<BF16>(a.out, out_row + hh * D + d0 + 1, o[hh][1] * inv);
+            store_out2<BF16>(a.out, out_row + hh * D + d0, o[hh][0] * inv, o[hh][1] * inv);
           } else {
             const size_t sidx = (size_t)(cur.slot0 + cur.part) * a.num_q_heads + cur.h0 + hh;
             const float nan_or_0 = wave_bad ? __builtin_nanf("") : 0.f;
@@ -534,35 +542,102 @@ __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
   }
 }
 
-// Merge of split-KV partitions: one wave per (row, query head).
+// Merge of split-KV partitions: one wave per (row, query head).  With
+// M = max_p m_p and f_p = exp2(m_p - M) (log2 domain), the row's output is
+// sum_p f_p o_p / sum_p f_p l_p, o_p being partition p's un-normalised
+// numerator.  The lanes of a wave split into PPI = 256/D groups of D/4
+// lanes, each lane holding 4 consecutive head_dim elements; group j takes
+// partitions j, j+PPI, ...  The loads of U*PPI partitions are issued before
+// any is used (indices past the row's last partition are clamped to it and
+// not added).  A row of at most 4*PPI partitions takes one such round trip,
+// M included; a longer row first finds M, then merges in chunks of 4*PPI.
+// Few registers keep 8 waves per SIMD resident: the merge is a chain of
+// dependent memory round trips, hidden by the other waves.
+// The groups' sums are added with lane exchanges at the end.
+template <int U, int D>
+struct MergeChunk {
+  static constexpr int PPI = kWave / (D / 4);
+  float4 v[U];
+  float2 ml[U];
+  PKV_DEV void load(const ReduceParams& a, int p0, int np, int s0, int h, int grp, int col) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t sidx = (size_t)(s0 + min(p0 + u * PPI + grp, np - 1)) * a.num_q_heads + h;
+      v[u] = ((const float4*)(a.part_o + sidx * D))[col];
+      ml[u] = a.part_ml[sidx];
+    }
+  }
+  PKV_DEV float max_m(int p0, int np, int grp) const {
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (p0 + u * PPI + grp < np) m = fmaxf(m, ml[u].x);
+    return m;
+  }
+  PKV_DEV void add(int p0, int np, int grp, float M, float4& acc, float& den) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = p0 + u * PPI + grp < np ? fast_exp2(ml[u].x - M) : 0.f;
+      den = fmaf(f, ml[u].y, den);
+      acc.x = fmaf(f, v[u].x, acc.x);
+      acc.y = fmaf(f, v[u].y, acc.y);
+      acc.z = fmaf(f, v[u].z, acc.z);
+      acc.w = fmaf(f, v[u].w, acc.w);
+    }
+  }
+};
+
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void reduce_kernel(ReduceParams a) {
+  constexpr int kCols = D / 4;          // float4 columns of a partial row
+  constexpr int PPI = kWave / kCols;    // partitions per load instruction
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
+  const int col = lane % kCols, grp = lane / kCols;
   const int Hq = a.num_q_heads;
   const int64_t total = (int64_t)a.hdr[kHdrReduceItems] * Hq;
   for (int64_t it = (int64_t)blockIdx.x * 4 + w; it < total; it += (int64_t)gridDim.x * 4) {
     const int4 item = a.items[it / Hq];
     const int h = (int)(it % Hq);
     const int t = item.x, np = item.z, s0 = item.w;
-    float M = -INFINITY;
-    for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.part_ml[(size_t)(s0 + p) * Hq + h].x);
-    M = wave_max(M);
     float den = 0.f;
-    float acc[D / kWave];
-#pragma unroll
-    for (int e = 0; e < D / kWave; ++e) acc[e] = 0.f;
-    for (int p = 0; p < np; ++p) {
-      const size_t s = (size_t)(s0 + p) * Hq + h;
-      const float2 ml = a.part_ml[s];
-      const float f = fast_exp2(ml.x - M);
-      den = fmaf(f, ml.y, den);
-#pragma unroll
-      for (int e = 0; e < D / kWave; ++e) acc[e] = fmaf(f, a.part_o[s * D + lane + kWave * e], acc[e]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (np <= 4 * PPI) {
+      MergeChunk<4, D> c;
+      c.load(a, 0, np, s0, h, grp, col);
+      const float M = wave_max(c.max_m(0, np, grp));
+      c.add(0, np, grp, M, acc, den);
+    } else {
+      float M = -INFINITY;
+      for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.part_ml[(size_t)(s0 + p) * Hq + h].x);
+      M = wave_max(M);
+      for (int p0 = 0; p0 < np; p0 += 4 * PPI) {
+        MergeChunk<4, D> c;
+        c.load(a, p0, np, s0, h, grp, col);
+        c.add(p0, np, grp, M, acc, den);
+      }
     }
-    const size_t orow = ((size_t)t * Hq + h) * D;
+    // add the groups' partial sums (den too: each group summed its own
+    // partitions' weights)
 #pragma unroll
-    for (int e = 0; e < D / kWave; ++e) store_out<BF16>(a.out, orow + lane + kWave * e, acc[e] / den);
+    for (int off = kCols; off < kWave; off <<= 1) {
+      acc.x += __shfl_xor(acc.x, off);
+      acc.y += __shfl_xor(acc.y, off);
+      acc.z += __shfl_xor(acc.z, off);
+      acc.w += __shfl_xor(acc.w, off);
+      den += __shfl_xor(den, off);
+    }
+    if (grp == 0) {  // one 4-element store per lane, a whole row per group
+      const size_t orow = ((size_t)t * Hq + h) * D + 4 * col;
+      const float inv = 1.f / den;
+      if constexpr (BF16) {
+        *(uint2*)((uint16_t*)a.out + orow) =
+            make_uint2((uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16),
+                       (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16));
+      } else {
+        *(float4*)((float*)a.out + orow) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      }
+    }
   }
 }
 

@@ -131,9 +131,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   // Pass 1: check requests, place decode rows (full partitions) and reduce
   // items, count everything, and histogram the items that are sorted.
   Counts base{0, 0, 0, 0, 0};
+  ReqInfo first{};  // this thread's request of the first pass, reused by pass 2
   for (int r0 = 0; r0 < a.num_reqs; r0 += kPlanThreads) {
     const int r = r0 + threadIdx.x;
     const ReqInfo q = classify(a, r);
+    if (r0 == 0) first = q;
     int err = q.err;
     const bool partial_last = q.kind == 1 && q.L % kSplitTokens != 0;
     Counts mine{0, 0, 0, 0, 0};
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     int slot_base = 0;  // the split rows' partial slots, recomputed as in pass 1
     for (int r0 = 0; r0 < a.num_reqs; r0 += kPlanThreads) {
       const int r = r0 + threadIdx.x;
-      const ReqInfo q = classify(a, r);
+      const ReqInfo q = r0 == 0 ? first : classify(a, r);
       Counts mine{0, 0, 0, 0, 0};
       if (q.kind == 1 && q.nparts > 1) mine.slots = q.nparts;
       Counts tot;
