@@ -206,6 +206,108 @@ int pkv_validate_metadata_host(const int32_t* block_table, const int32_t* seq_le
                                int32_t max_blocks_per_req, int32_t max_query_len,
                                int32_t max_seq_len);
 
+/*
+ * paged_kv_copy_blocks — copy whole cache blocks (K and V, every kv head):
+ * the copy half of copy-on-write prefix sharing (lpnh.cn/news/2436702,
+ * section 2.2: sequences share prefix blocks and a block is copied only
+ * when they diverge inside it).
+ *
+ *   kv_cache_layer  device, [2][num_blocks][16][num_kv_heads][head_dim], dtype.
+ *   copies          device int32 [num_copies][2]: (source block, destination
+ *                   block).  No block may be the destination of two pairs or
+ *                   both a source and a destination (the order of the copies
+ *                   is unspecified).  A pair with an id outside
+ *                   [0, num_blocks) is skipped and sets PKV_DEVERR_BLOCK_ID.
+ *   device_error    device int32, or NULL.
+ *   num_copies      >= 0 (0 enqueues nothing).
+ * The destination gets the source's bits.  Returns PKV_OK or an argument
+ * error; enqueued on `stream`.
+ */
+int paged_kv_copy_blocks(void* kv_cache_layer, const int32_t* copies, int32_t num_copies,
+                         int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         int32_t* device_error, void* stream);
+
+/*
+ * Host block manager and step scheduler (no HIP call, no device memory):
+ * builds each step's metadata for paged_kv_write / paged_attention.
+ *
+ * The cache is a pool of num_blocks 16-token blocks allocated up front; a
+ * request's block table grows by the next free block when its last block is
+ * full, and its blocks return to the pool when it finishes
+ * (lpnh.cn/news/2436702, section 2.2; "大模型推理部署：从单卡到集群的工程化落地
+ * 路径", section 2.2).  Requests may share prefix blocks; a shared block is
+ * copied before a step writes into it (copy-on-write).  Each step schedules,
+ * per request, the tokens between num_computed_tokens and num_tokens, with
+ * no prefill / decode distinction, under four limits: max_num_seqs, the
+ * token budget, max_model_len and the free blocks ("AI Infra入门干货总结",
+ * section "连续批处理").
+ *
+ * Policy where the pages are silent: first come, first served; a request
+ * that cannot get a block this step is skipped (it waits; no preemption) and
+ * later requests may still run; a request gets as many pending tokens as the
+ * limits allow (a partial chunk is a chunked prefill); free blocks are
+ * handed out first in, first out (initially 0, 1, 2, ...; freed blocks join
+ * the back in table order); a copy-on-write takes its free block before the
+ * request's new blocks; unused block-table entries are -1.
+ *
+ * Use: add / fork / append / finish requests, then pkv_bm_schedule fills a
+ * pkv_step; the caller copies its arrays to the device, runs
+ * paged_kv_copy_blocks(step.copies) and paged_kv_write(slot_mapping) before
+ * paged_attention, then calls pkv_bm_commit.  Nothing else may change the
+ * manager between schedule and commit.  A manager is not thread-safe.
+ * Every call returns a pkv_status (PKV_ERR_METADATA for an unknown or
+ * duplicate request id or a call out of order; pkv_last_error_detail()
+ * says which).
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+typedef struct {
+  /* limits of the step, set by the caller */
+  int32_t max_num_seqs;   /* requests per step, > 0 */
+  int32_t token_budget;   /* tokens per step, > 0 */
+  int32_t max_model_len;  /* tokens per request, > 0 */
+  /* HOST output arrays owned by the caller */
+  int64_t* req_ids;              /* [max_num_seqs] request id of each row */
+  int32_t* query_start_loc;      /* [max_num_seqs + 1] */
+  int32_t* seq_lens;             /* [max_num_seqs] */
+  int32_t* num_computed_tokens;  /* [max_num_seqs] */
+  int32_t* block_table;          /* [max_num_seqs][max_blocks_per_req], -1 = unused */
+  int64_t* slot_mapping;         /* [token_budget] */
+  int32_t* copies;               /* [max_num_seqs][2] (source, destination) blocks */
+  /* results */
+  int32_t num_reqs, num_tokens, num_copies, max_query_len, max_seq_len;
+} pkv_step;
+
+/* A manager of num_blocks blocks; block tables have max_blocks_per_req
+ * columns.  *out receives the handle (free it with pkv_bm_destroy). */
+int pkv_bm_create(int32_t num_blocks, int32_t max_blocks_per_req, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+/* A new request of num_prompt_tokens (>= 1) pending tokens. */
+int pkv_bm_add_request(pkv_block_manager* bm, int64_t req_id, int32_t num_prompt_tokens);
+/* The same, sharing the first min(prefix_tokens, computed tokens of
+ * prefix_from, num_prompt_tokens - 1) / 16 full blocks of request
+ * prefix_from, which count as computed (a prefix-cache hit).  The caller
+ * guarantees that those tokens are the same. */
+int pkv_bm_add_request_with_prefix(pkv_block_manager* bm, int64_t req_id, int32_t num_prompt_tokens,
+                                   int64_t prefix_from, int32_t prefix_tokens);
+/* child_id continues from parent_id's state, sharing all of its blocks. */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
+/* n >= 0 more tokens (e.g. a sampled token) for the request. */
+int pkv_bm_append_tokens(pkv_block_manager* bm, int64_t req_id, int32_t n);
+/* The request leaves; blocks no other request shares return to the pool. */
+int pkv_bm_finish(pkv_block_manager* bm, int64_t req_id);
+/* Free blocks (-1 for a NULL manager). */
+int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+/* A request's num_tokens, num_computed_tokens and block count; its first
+ * min(max_blocks, count) block ids go to `blocks` (HOST, may be NULL). */
+int pkv_bm_request_state(const pkv_block_manager* bm, int64_t req_id, int32_t* num_tokens,
+                         int32_t* num_computed, int32_t* blocks, int32_t max_blocks, int32_t* num_blocks);
+/* Schedule one step into *step (see pkv_step); allocates blocks and records
+ * the step's copy-on-write pairs. */
+int pkv_bm_schedule(pkv_block_manager* bm, pkv_step* step);
+/* The scheduled step ran: its tokens count as computed. */
+int pkv_bm_commit(pkv_block_manager* bm);
+
 /* Static text of a pkv_status. */
 const char* pkv_status_string(int status);
 

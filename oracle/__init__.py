@@ -90,6 +90,17 @@ def kv_write(pool: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out
 
 
+def copy_blocks(pool: np.ndarray, copies) -> np.ndarray:
+    """Return a copy of ``pool`` where each destination block holds its source
+    block's K and V (every slot, every head): the copy step of copy-on-write
+    prefix sharing (lpnh.cn/news/2436702, section 2.2).  ``copies``: pairs
+    (source, destination); no block is both, or twice a destination."""
+    out = pool.copy()
+    for src, dst in np.asarray(copies, dtype=np.int64).reshape(-1, 2):
+        out[:, dst] = pool[:, src]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Reading one request's K/V through its block table.
 

@@ -11,6 +11,8 @@ Functions keep the C names:
 * ``paged_kv_write(k, v, slot_mapping, kv_cache_layer)``
 * ``paged_attention(q, kv_cache_layer, block_table, seq_lens, query_start_loc,
   num_computed_tokens, scale, ...)``
+* ``paged_kv_copy_blocks(kv_cache_layer, copies)``
+* ``BlockManager`` — the host block manager / step scheduler (``pkv_bm_*``)
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ __all__ = [
     "PagedKVError", "paged_kv_write", "paged_attention", "paged_attention_workspace_size",
     "pkv_read_device_error", "pkv_validate_metadata_host", "lib_path", "load_library",
     "DEVERR_SEQ_LEN", "DEVERR_LIMITS", "DEVERR_QSL", "DEVERR_BLOCK_ID", "DEVERR_SLOT",
-    "DEVERR_CAPACITY", "BLOCK_SIZE",
+    "DEVERR_CAPACITY", "BLOCK_SIZE", "paged_kv_copy_blocks", "BlockManager", "Step",
 ]
 
 BLOCK_SIZE = 16
@@ -47,6 +49,19 @@ class PagedKVError(RuntimeError):
         detail = _lib.pkv_last_error_detail().decode()
         text = _lib.pkv_status_string(status).decode()
         super().__init__(f"{where}: {text} ({status}){': ' + detail if detail else ''}")
+
+
+class _PkvStep(ctypes.Structure):
+    """Mirror of pkv_step (include/paged_kv.h)."""
+    _fields_ = [("max_num_seqs", ctypes.c_int32), ("token_budget", ctypes.c_int32),
+                ("max_model_len", ctypes.c_int32),
+                ("req_ids", ctypes.c_void_p), ("query_start_loc", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("num_computed_tokens", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("slot_mapping", ctypes.c_void_p),
+                ("copies", ctypes.c_void_p),
+                ("num_reqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("num_copies", ctypes.c_int32), ("max_query_len", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32)]
 
 
 def load_library() -> ctypes.CDLL:
@@ -72,6 +87,26 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error_detail.argtypes = []
     lib.pkv_last_error_detail.restype = ctypes.c_char_p
+    lib.paged_kv_copy_blocks.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.paged_kv_copy_blocks.restype = ctypes.c_int
+    pbm = ctypes.c_void_p
+    lib.pkv_bm_create.argtypes = [i32, i32, ctypes.POINTER(pbm)]
+    lib.pkv_bm_create.restype = ctypes.c_int
+    lib.pkv_bm_destroy.argtypes = [pbm]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_add_request.argtypes = [pbm, i64, i32]
+    lib.pkv_bm_add_request_with_prefix.argtypes = [pbm, i64, i32, i64, i32]
+    lib.pkv_bm_fork.argtypes = [pbm, i64, i64]
+    lib.pkv_bm_append_tokens.argtypes = [pbm, i64, i32]
+    lib.pkv_bm_finish.argtypes = [pbm, i64]
+    lib.pkv_bm_num_free_blocks.argtypes = [pbm]
+    lib.pkv_bm_num_free_blocks.restype = i32
+    lib.pkv_bm_request_state.argtypes = [pbm, i64, vp, vp, vp, i32, vp]
+    lib.pkv_bm_schedule.argtypes = [pbm, ctypes.POINTER(_PkvStep)]
+    lib.pkv_bm_commit.argtypes = [pbm]
+    for f in ("pkv_bm_add_request", "pkv_bm_add_request_with_prefix", "pkv_bm_fork", "pkv_bm_append_tokens",
+              "pkv_bm_finish", "pkv_bm_request_state", "pkv_bm_schedule", "pkv_bm_commit"):
+        getattr(lib, f).restype = ctypes.c_int
     return lib
 
 
@@ -80,7 +115,11 @@ _lib = load_library()
 EXPORTED_SYMBOLS = ("paged_kv_write", "paged_attention", "paged_attention_profiled",
                     "paged_attention_workspace_size",
                     "pkv_read_device_error", "pkv_validate_metadata_host", "pkv_status_string",
-                    "pkv_last_error_detail")
+                    "pkv_last_error_detail", "paged_kv_copy_blocks",
+                    "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_request",
+                    "pkv_bm_add_request_with_prefix", "pkv_bm_fork", "pkv_bm_append_tokens",
+                    "pkv_bm_finish", "pkv_bm_num_free_blocks", "pkv_bm_request_state",
+                    "pkv_bm_schedule", "pkv_bm_commit")
 
 
 def _dtype_code(t: torch.dtype) -> int:
@@ -218,3 +257,117 @@ def pkv_validate_metadata_host(block_table, seq_lens, query_start_loc, num_compu
 
 def last_error_detail() -> str:
     return _lib.pkv_last_error_detail().decode()
+
+
+def paged_kv_copy_blocks(kv_cache_layer: torch.Tensor, copies: torch.Tensor,
+                         device_error: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Copy whole blocks of ``kv_cache_layer`` (K and V): ``copies [C, 2]`` int32
+    on the device holds (source, destination) block ids.  Enqueued on ``stream``."""
+    _check_dev("kv_cache_layer", kv_cache_layer)
+    _check_dev("copies", copies, torch.int32)
+    if device_error is not None:
+        _check_dev("device_error", device_error, torch.int32)
+    if copies.dim() != 2 or copies.shape[1] != 2:
+        raise ValueError("copies must be [C, 2]")
+    _, nb, _, hkv, d = kv_cache_layer.shape
+    st = _lib.paged_kv_copy_blocks(_ptr(kv_cache_layer), _ptr(copies), copies.shape[0], nb, hkv, d,
+                                   _dtype_code(kv_cache_layer.dtype), _ptr(device_error),
+                                   _stream_ptr(stream))
+    if st != 0:
+        raise PagedKVError(st, "paged_kv_copy_blocks")
+
+
+class Step:
+    """One scheduled step (host numpy arrays, trimmed to the step's sizes)."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+    @property
+    def num_reqs(self) -> int:
+        return int(self.req_ids.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.slot_mapping.shape[0])
+
+
+class BlockManager:
+    """Host block manager and step scheduler of libpagedkv (``pkv_bm_*``).
+
+    Method names follow the C calls: ``add_request``, ``fork``,
+    ``append_tokens``, ``finish``, ``schedule`` (returns a :class:`Step` of
+    numpy arrays), ``commit``, ``num_free_blocks``, ``request_state``."""
+
+    def __init__(self, num_blocks: int, max_blocks_per_req: int):
+        h = ctypes.c_void_p()
+        self._check(_lib.pkv_bm_create(num_blocks, max_blocks_per_req, ctypes.byref(h)), "pkv_bm_create")
+        self._h = h
+        self._destroy = _lib.pkv_bm_destroy  # kept: module globals may be gone at exit
+        self.num_blocks = num_blocks
+        self.max_blocks_per_req = max_blocks_per_req
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._destroy(h)
+            self._h = None
+
+    @staticmethod
+    def _check(st: int, where: str) -> None:
+        if st != 0:
+            raise PagedKVError(st, where)
+
+    def add_request(self, req_id: int, num_prompt_tokens: int, prefix_from: Optional[int] = None,
+                    prefix_tokens: int = 0) -> None:
+        if prefix_from is None:
+            self._check(_lib.pkv_bm_add_request(self._h, req_id, num_prompt_tokens), "pkv_bm_add_request")
+        else:
+            self._check(_lib.pkv_bm_add_request_with_prefix(self._h, req_id, num_prompt_tokens, prefix_from,
+                                                            prefix_tokens), "pkv_bm_add_request_with_prefix")
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        self._check(_lib.pkv_bm_fork(self._h, parent_id, child_id), "pkv_bm_fork")
+
+    def append_tokens(self, req_id: int, n: int = 1) -> None:
+        self._check(_lib.pkv_bm_append_tokens(self._h, req_id, n), "pkv_bm_append_tokens")
+
+    def finish(self, req_id: int) -> None:
+        self._check(_lib.pkv_bm_finish(self._h, req_id), "pkv_bm_finish")
+
+    def num_free_blocks(self) -> int:
+        return int(_lib.pkv_bm_num_free_blocks(self._h))
+
+    def request_state(self, req_id: int):
+        """(num_tokens, num_computed_tokens, [block ids])"""
+        import numpy as np
+        nt, nc, nb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        blocks = np.zeros(self.max_blocks_per_req, np.int32)
+        self._check(_lib.pkv_bm_request_state(self._h, req_id, ctypes.byref(nt), ctypes.byref(nc),
+                                              blocks.ctypes.data_as(ctypes.c_void_p), blocks.shape[0],
+                                              ctypes.byref(nb)), "pkv_bm_request_state")
+        return nt.value, nc.value, blocks[:nb.value].tolist()
+
+    def schedule(self, max_num_seqs: int, token_budget: int, max_model_len: int) -> Step:
+        import numpy as np
+        a = dict(req_ids=np.zeros(max_num_seqs, np.int64),
+                 query_start_loc=np.zeros(max_num_seqs + 1, np.int32),
+                 seq_lens=np.zeros(max_num_seqs, np.int32),
+                 num_computed_tokens=np.zeros(max_num_seqs, np.int32),
+                 block_table=np.zeros((max_num_seqs, self.max_blocks_per_req), np.int32),
+                 slot_mapping=np.zeros(token_budget, np.int64),
+                 copies=np.zeros((max_num_seqs, 2), np.int32))
+        p = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+        st = _PkvStep(max_num_seqs, token_budget, max_model_len, p(a["req_ids"]), p(a["query_start_loc"]),
+                      p(a["seq_lens"]), p(a["num_computed_tokens"]), p(a["block_table"]),
+                      p(a["slot_mapping"]), p(a["copies"]), 0, 0, 0, 0, 0)
+        self._check(_lib.pkv_bm_schedule(self._h, ctypes.byref(st)), "pkv_bm_schedule")
+        R, T, C = st.num_reqs, st.num_tokens, st.num_copies
+        return Step(req_ids=a["req_ids"][:R].copy(), query_start_loc=a["query_start_loc"][:R + 1].copy(),
+                    seq_lens=a["seq_lens"][:R].copy(), num_computed_tokens=a["num_computed_tokens"][:R].copy(),
+                    block_table=a["block_table"][:R].copy(), slot_mapping=a["slot_mapping"][:T].copy(),
+                    copies=a["copies"][:C].copy(), max_query_len=st.max_query_len,
+                    max_seq_len=st.max_seq_len)
+
+    def commit(self) -> None:
+        self._check(_lib.pkv_bm_commit(self._h), "pkv_bm_commit")

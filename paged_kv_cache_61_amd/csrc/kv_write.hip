@@ -55,4 +55,38 @@ int launch_kv_write(const void* k, const void* v, const int64_t* slot_mapping, v
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
+// paged_kv_copy_blocks: destination block <- source block, K and V halves
+// (copy-on-write of a shared prefix block, lpnh.cn/news/2436702, section
+// 2.2).  A block of one half is 16 * num_kv_heads * head_dim contiguous
+// elements, so a pair is two contiguous runs; workgroup (pair, half) copies
+// one run with 16-byte chunks, consecutive threads on consecutive chunks.
+__global__ __launch_bounds__(256) void kv_copy_blocks_kernel(u32x4* __restrict__ cache,
+                                                             const int32_t* __restrict__ copies,
+                                                             int32_t num_copies, int32_t num_blocks,
+                                                             int32_t chunks_per_block,
+                                                             int32_t* __restrict__ device_error) {
+  const int32_t pair = blockIdx.x >> 1;
+  const int32_t kv = blockIdx.x & 1;
+  if (pair >= num_copies) return;
+  const int32_t src = copies[2 * pair], dst = copies[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) {
+    if (device_error != nullptr && threadIdx.x == 0 && kv == 0) atomicOr(device_error, PKV_DEVERR_BLOCK_ID);
+    return;
+  }
+  const int64_t half = (int64_t)num_blocks * chunks_per_block;
+  const u32x4* s = cache + kv * half + (int64_t)src * chunks_per_block;
+  u32x4* d = cache + kv * half + (int64_t)dst * chunks_per_block;
+  for (int32_t i = threadIdx.x; i < chunks_per_block; i += blockDim.x) d[i] = s[i];
+}
+
+int launch_kv_copy_blocks(void* cache, const int32_t* copies, int32_t num_copies, int32_t num_blocks,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
+                          hipStream_t stream) {
+  if (num_copies == 0) return 0;
+  const int32_t chunks = kBlock * num_kv_heads * head_dim * elem_bytes / 16;
+  hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3(2u * (unsigned)num_copies), dim3(256), 0, stream,
+                     (u32x4*)cache, copies, num_copies, num_blocks, chunks, device_error);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 }  // namespace pkv

@@ -15,10 +15,12 @@
 #include "pkv_internal.h"
 
 namespace {
-
 thread_local std::string g_detail;
+}  // namespace
 
-int fail(int status, const char* fmt, long long a = 0, long long b = 0, long long c = 0) {
+namespace pkv {
+
+int fail(int status, const char* fmt, long long a, long long b, long long c) {
   char buf[256];
   std::snprintf(buf, sizeof(buf), fmt, a, b, c);
   g_detail = buf;
@@ -29,6 +31,13 @@ int ok() {
   g_detail.clear();
   return PKV_OK;
 }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+using pkv::ok;
 
 int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : dtype == PKV_F32 ? 4 : 0; }
 
@@ -96,6 +105,26 @@ int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
   if (pkv::launch_kv_write(k, v, slot_mapping, kv_cache_layer, num_tokens, num_blocks, num_kv_heads,
                            head_dim, eb, device_error, (hipStream_t)stream))
     return fail(PKV_ERR_LAUNCH, "kv_write launch: %lld", (long long)hipGetLastError());
+  return ok();
+}
+
+int paged_kv_copy_blocks(void* kv_cache_layer, const int32_t* copies, int32_t num_copies,
+                         int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         int32_t* device_error, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
+  if (num_copies < 0) return fail(PKV_ERR_DIMS, "num_copies %lld < 0", num_copies);
+  if (num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_DIMS, "num_blocks %lld, num_kv_heads %lld", num_blocks, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_DIMS, "head_dim %lld not 64/128", head_dim);
+  if (kv_cache_layer == nullptr) return fail(PKV_ERR_NULL, "kv_cache_layer is NULL");
+  if (num_copies == 0) return ok();
+  if (!copies) return fail(PKV_ERR_NULL, "copies is NULL");
+  if (!aligned(kv_cache_layer, 16) || !aligned(copies, 4))
+    return fail(PKV_ERR_ALIGN, "cache must be 16-byte aligned, copies 4-byte");
+  if (pkv::launch_kv_copy_blocks(kv_cache_layer, copies, num_copies, num_blocks, num_kv_heads, head_dim, eb,
+                                 device_error, (hipStream_t)stream))
+    return fail(PKV_ERR_LAUNCH, "copy_blocks launch: %lld", (long long)hipGetLastError());
   return ok();
 }
 

@@ -9,6 +9,12 @@
 
 namespace pkv {
 
+// Status helpers shared by the host entry points: set the calling thread's
+// error detail (printf format with up to three long long arguments) and
+// return `status`; ok() clears the detail and returns PKV_OK.
+int fail(int status, const char* fmt, long long a = 0, long long b = 0, long long c = 0);
+int ok();
+
 struct PlanParams {
   const int32_t* qsl;
   const int32_t* seq_lens;
@@ -71,6 +77,9 @@ int launch_kv_write(const void* k, const void* v, const int64_t* slot_mapping, v
                     int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
                     int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
                     hipStream_t stream);
+int launch_kv_copy_blocks(void* cache, const int32_t* copies, int32_t num_copies, int32_t num_blocks,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
+                          hipStream_t stream);
 int launch_plan(const PlanParams& p, hipStream_t stream);
 // bound_waves: upper bound on row work items (one wave each); cus: compute units.
 int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bound_waves, int cus,

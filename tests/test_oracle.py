@@ -412,3 +412,30 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oracle, "gather_kv", wrong_gather)
     bad = _run(case, 0.5, "f32")
     assert not np.allclose(bad[1:7], brute(1), atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# copy_blocks (copy-on-write): pointing a request's table at a copy of one of
+# its blocks leaves what the request reads unchanged; nothing else changes.
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_copy_blocks_preserves_logical_content(dtype):
+    rng = np.random.default_rng(21)
+    case = _ragged_case(21, dtype, 4, 2, 16, [(37, 1), (20, 5)])
+    pool, bt = case["pool"], case["bt"].copy()
+    NB = pool.shape[1]
+    used = set(int(b) for r in range(2) for b in bt[r, : (int(case["L"][r]) + 15) // 16])
+    spare = [b for b in range(NB) if b not in used][:2]
+    pairs = [(int(bt[0, 1]), spare[0]), (int(bt[1, 0]), spare[1])]
+    pool2 = oracle.copy_blocks(pool, pairs)
+    bt2 = bt.copy()
+    bt2[0, 1], bt2[1, 0] = spare
+    for r in range(2):
+        K1, V1 = oracle.gather_kv(pool, bt[r], int(case["L"][r]), dtype)
+        K2, V2 = oracle.gather_kv(pool2, bt2[r], int(case["L"][r]), dtype)
+        assert np.array_equal(K1, K2, equal_nan=True) and np.array_equal(V1, V2, equal_nan=True)
+    untouched = [b for b in range(NB) if b not in spare]
+    assert pool2[:, untouched].tobytes() == pool[:, untouched].tobytes()
+    out1 = _run(case, 0.3, dtype)
+    case2 = dict(case, pool=pool2, bt=bt2)
+    assert np.array_equal(out1, _run(case2, 0.3, dtype))
