@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope", action="store_true",
+                    help="write the step's tokens with paged_kv_write_rope (RoPE on K, and on q in place)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="CPU seconds the oracle baseline may spend on its sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -75,6 +77,7 @@ def accounting(wl):
     a["prefill_bytes"] = int(L[pre].sum()) * kv_token_bytes + 2 * int(ql[pre].sum()) * Hq * D * s
     T = wl.num_tokens
     a["write_bytes"] = 2 * (2 * T * Hkv * D * s) + 8 * T
+    a["write_rope_bytes"] = a["write_bytes"] + 2 * T * Hq * D * s + 8 * T + T * D * 4  # + q in/out, positions, cos/sin
     a["step_bytes"] = a["decode_bytes"] + a["prefill_bytes"] + a["write_bytes"]
     return a
 
@@ -203,17 +206,32 @@ def main():
     out = torch.empty_like(q)
 
     nph = pkv.NUM_PHASES
-    step_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nph)]
+    step_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nph + 2)]
                    for _ in range(args.steps)]
+    if args.rope:
+        positions = torch.from_numpy(np.concatenate(
+            [np.arange(int(wl.num_computed_tokens[r]), int(wl.seq_lens[r])) for r in range(wl.num_reqs)]
+        ).astype(np.int64)).to(dev)
+        inv = 10000.0 ** (-np.arange(0, wl.head_dim, 2, dtype=np.float64) / wl.head_dim)
+        ang = np.arange(wl.max_seq_len + 1, dtype=np.float64)[:, None] * inv[None, :]
+        cos_sin = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)).to(dev)
     for evs in step_events:          # create the underlying hipEvents
         for e in evs:
             e.record()
     torch.cuda.synchronize()
 
     def step(evs=None):
-        pkv.paged_kv_write(k_new, v_new, slot_mapping, pool)
+        if evs is not None:
+            evs[2 * nph].record()
+        if args.rope:
+            pkv.paged_kv_write_rope(k_new, v_new, positions, cos_sin, slot_mapping, pool, q=q)
+        else:
+            pkv.paged_kv_write(k_new, v_new, slot_mapping, pool)
+        if evs is not None:
+            evs[2 * nph + 1].record()
         pkv.paged_attention(q, pool, bt, sl, qsl, nct, wl.scale, max_query_len=wl.max_query_len,
-                            max_seq_len=wl.max_seq_len, out=out, workspace=ws, phase_events=evs)
+                            max_seq_len=wl.max_seq_len, out=out, workspace=ws,
+                            phase_events=None if evs is None else evs[:2 * nph])
 
     for _ in range(args.warmup):
         step()
@@ -249,7 +267,10 @@ def main():
     for p, nm in enumerate(names):
         phase_ms[nm] = float(np.mean([evs[2 * p].elapsed_time(evs[2 * p + 1]) for evs in step_events]))
 
-    value = acct["step_bytes"] / (ms_per_step * 1e-3) / 1e9
+    write_ms = float(np.mean([evs[2 * nph].elapsed_time(evs[2 * nph + 1]) for evs in step_events]))
+    write_bytes = acct["write_rope_bytes"] if args.rope else acct["write_bytes"]
+    step_bytes = acct["step_bytes"] - acct["write_bytes"] + write_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
     rows_gbs = acct["decode_bytes"] / (phase_ms["rows"] * 1e-3) / 1e9 if phase_ms["rows"] > 0 else 0.0
     result = {
         "metric": METRIC,
@@ -283,7 +304,10 @@ def main():
             "avg_launch_ms": round(phase_ms["rows"], 5),
         },
         "phases_ms": {k: round(v, 5) for k, v in phase_ms.items()},
-        "step_algorithmic_bytes": acct["step_bytes"],
+        "write": {"kernel": "kv_write_rope_kernel (RoPE on K and q)" if args.rope else "kv_write_kernel",
+                  "ms": round(write_ms, 5), "bytes": write_bytes,
+                  "GB/s": round(write_bytes / (write_ms * 1e-3) / 1e9, 1) if write_ms > 0 else None},
+        "step_algorithmic_bytes": step_bytes,
         "wall_s_timed": round(wall_s, 4),
         "input_gen_s": round(gen_s, 2),
     }

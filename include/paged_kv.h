@@ -79,6 +79,7 @@ typedef enum {
 #define PKV_DEVERR_BLOCK_ID    0x8  /* a block_table entry read is outside [0, num_blocks) */
 #define PKV_DEVERR_SLOT        0x10 /* a slot_mapping entry is < -1 or >= 16 * num_blocks */
 #define PKV_DEVERR_CAPACITY    0x20 /* the workspace was too small for this step's split-KV partials */
+#define PKV_DEVERR_POSITION    0x40 /* a position given to paged_kv_write_rope is outside [0, max_position) */
 
 /*
  * paged_kv_write — store the step's new K/V in the cache (a "slot_mapping"
@@ -205,6 +206,42 @@ int pkv_validate_metadata_host(const int32_t* block_table, const int32_t* seq_le
                                int32_t num_reqs, int64_t num_tokens, int32_t num_blocks,
                                int32_t max_blocks_per_req, int32_t max_query_len,
                                int32_t max_seq_len);
+
+/*
+ * paged_kv_write_rope — paged_kv_write with the rotary position embedding
+ * applied to K on its way into the cache, and optionally to q in place
+ * ("AI Infra入门干货总结", section "LLM 推理全流程" / "RoPE": positions are
+ * rotation angles read from a precomputed cos_sin_cache of shape
+ * [max_position_embeddings, rotary_dim]).
+ *
+ *   q               device, [num_tokens][num_q_heads][head_dim], dtype, or
+ *                   NULL.  When given, every row is rotated in place.
+ *   k, v            device, [num_tokens][num_kv_heads][head_dim], dtype
+ *                   (not modified).
+ *   positions       device, int64 [num_tokens]: absolute position of each
+ *                   token in its sequence.  A token whose position is
+ *                   outside [0, max_position) is left alone entirely (no q
+ *                   rotation, no cache write) and sets PKV_DEVERR_POSITION.
+ *   cos_sin_cache   device, float32 [max_position][rotary_dim]: row p holds
+ *                   cos of the rotary_dim/2 angles of position p, then their
+ *                   sin.
+ *   rotary_dim      even, 2 .. head_dim; dims from rotary_dim on are not
+ *                   rotated.
+ *   is_neox         1: angle i rotates the pair (i, i + rotary_dim/2);
+ *                   0: the pair (2i, 2i+1).  x' = x cos - y sin,
+ *                   y' = y cos + x sin, in fp32, rounded to dtype (nearest
+ *                   even).
+ *   slot_mapping, kv_cache_layer, num_blocks, num_kv_heads, head_dim, dtype,
+ *   device_error    as for paged_kv_write (V is copied unchanged; slot -1
+ *                   skips the cache write but q is still rotated).
+ * Returns PKV_OK or an argument error; enqueued on `stream`.
+ */
+int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* positions,
+                        const float* cos_sin_cache, int32_t max_position, int32_t rotary_dim,
+                        int32_t is_neox, const int64_t* slot_mapping, void* kv_cache_layer,
+                        int64_t num_tokens, int32_t num_q_heads, int32_t num_blocks,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        int32_t* device_error, void* stream);
 
 /*
  * paged_kv_copy_blocks — copy whole cache blocks (K and V, every kv head):

@@ -90,6 +90,43 @@ def kv_write(pool: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out
 
 
+def rope(x: np.ndarray, positions: np.ndarray, cos_sin_cache: np.ndarray, rotary_dim: int,
+         is_neox: bool, dtype: str) -> np.ndarray:
+    """Rotary position embedding of ``x [T, H, D]`` (storage values), in float64.
+
+    "AI Infra入门干货总结", section "LLM 推理全流程" / "RoPE": a token's position is
+    encoded as rotation angles, read from a precomputed ``cos_sin_cache`` of shape
+    ``[max_position_embeddings, rotary_dim]``.  Readings (the page gives only that
+    much): row ``p`` holds ``cos`` of the ``rotary_dim/2`` angles of position ``p``
+    followed by their ``sin``; angle ``i`` rotates the pair (``i``, ``i + rotary_dim/2``)
+    when ``is_neox`` (the two halves of the rotary dims) and (``2i``, ``2i+1``)
+    otherwise, as ``x' = x cos - y sin``, ``y' = y cos + x sin``; dims from
+    ``rotary_dim`` on pass through.  Returns float64; the caller rounds to storage."""
+    v = to_f64(x, dtype).copy()
+    half = rotary_dim // 2
+    cs = np.asarray(cos_sin_cache, dtype=np.float32).astype(np.float64)[np.asarray(positions, dtype=np.int64)]
+    c, s = cs[:, None, :half], cs[:, None, half:rotary_dim]
+    if is_neox:
+        ix, iy = np.arange(half), np.arange(half) + half
+    else:
+        ix, iy = 2 * np.arange(half), 2 * np.arange(half) + 1
+    xs, ys = v[:, :, ix].copy(), v[:, :, iy].copy()
+    v[:, :, ix] = xs * c - ys * s
+    v[:, :, iy] = ys * c + xs * s
+    return v
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> storage values: float32, or bf16 bit patterns (nearest even,
+    through float32: the two roundings agree except on exact float32 ties,
+    which the product's own fp32 arithmetic cannot avoid either)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return f
+    u = f.view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
 def copy_blocks(pool: np.ndarray, copies) -> np.ndarray:
     """Return a copy of ``pool`` where each destination block holds its source
     block's K and V (every slot, every head): the copy step of copy-on-write

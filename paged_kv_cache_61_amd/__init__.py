@@ -11,6 +11,7 @@ Functions keep the C names:
 * ``paged_kv_write(k, v, slot_mapping, kv_cache_layer)``
 * ``paged_attention(q, kv_cache_layer, block_table, seq_lens, query_start_loc,
   num_computed_tokens, scale, ...)``
+* ``paged_kv_write_rope(k, v, positions, cos_sin_cache, slot_mapping, kv_cache_layer, ...)``
 * ``paged_kv_copy_blocks(kv_cache_layer, copies)``
 * ``BlockManager`` — the host block manager / step scheduler (``pkv_bm_*``)
 """
@@ -26,7 +27,8 @@ __all__ = [
     "PagedKVError", "paged_kv_write", "paged_attention", "paged_attention_workspace_size",
     "pkv_read_device_error", "pkv_validate_metadata_host", "lib_path", "load_library",
     "DEVERR_SEQ_LEN", "DEVERR_LIMITS", "DEVERR_QSL", "DEVERR_BLOCK_ID", "DEVERR_SLOT",
-    "DEVERR_CAPACITY", "BLOCK_SIZE", "paged_kv_copy_blocks", "BlockManager", "Step",
+    "DEVERR_CAPACITY", "DEVERR_POSITION", "BLOCK_SIZE", "paged_kv_copy_blocks", "paged_kv_write_rope",
+    "BlockManager", "Step",
 ]
 
 BLOCK_SIZE = 16
@@ -35,6 +37,7 @@ PHASE_PLAN, PHASE_PREFILL, PHASE_ROWS, PHASE_REDUCE = 0, 1, 2, 3
 NUM_PHASES = 4
 DEVERR_SEQ_LEN, DEVERR_LIMITS, DEVERR_QSL = 0x1, 0x2, 0x4
 DEVERR_BLOCK_ID, DEVERR_SLOT, DEVERR_CAPACITY = 0x8, 0x10, 0x20
+DEVERR_POSITION = 0x40
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -87,6 +90,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error_detail.argtypes = []
     lib.pkv_last_error_detail.restype = ctypes.c_char_p
+    lib.paged_kv_write_rope.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, i32, i32, i32,
+                                        i32, vp, vp]
+    lib.paged_kv_write_rope.restype = ctypes.c_int
     lib.paged_kv_copy_blocks.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     pbm = ctypes.c_void_p
@@ -115,7 +121,7 @@ _lib = load_library()
 EXPORTED_SYMBOLS = ("paged_kv_write", "paged_attention", "paged_attention_profiled",
                     "paged_attention_workspace_size",
                     "pkv_read_device_error", "pkv_validate_metadata_host", "pkv_status_string",
-                    "pkv_last_error_detail", "paged_kv_copy_blocks",
+                    "pkv_last_error_detail", "paged_kv_copy_blocks", "paged_kv_write_rope",
                     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_request",
                     "pkv_bm_add_request_with_prefix", "pkv_bm_fork", "pkv_bm_append_tokens",
                     "pkv_bm_finish", "pkv_bm_num_free_blocks", "pkv_bm_request_state",
@@ -257,6 +263,39 @@ def pkv_validate_metadata_host(block_table, seq_lens, query_start_loc, num_compu
 
 def last_error_detail() -> str:
     return _lib.pkv_last_error_detail().decode()
+
+
+def paged_kv_write_rope(k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+                        cos_sin_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                        kv_cache_layer: torch.Tensor, *, rotary_dim: Optional[int] = None,
+                        is_neox: bool = True, q: Optional[torch.Tensor] = None,
+                        device_error: Optional[torch.Tensor] = None, stream=None) -> None:
+    """``paged_kv_write`` with RoPE applied to K (and to ``q [T, Hq, D]`` in place
+    when given).  ``positions [T]`` int64; ``cos_sin_cache [max_position,
+    rotary_dim]`` float32, row p = cos of the rotary_dim/2 angles, then sin."""
+    for n, x in (("k", k), ("v", v), ("kv_cache_layer", kv_cache_layer)):
+        _check_dev(n, x, kv_cache_layer.dtype)
+    _check_dev("slot_mapping", slot_mapping, torch.int64)
+    _check_dev("positions", positions, torch.int64)
+    _check_dev("cos_sin_cache", cos_sin_cache, torch.float32)
+    if q is not None:
+        _check_dev("q", q, kv_cache_layer.dtype)
+    if device_error is not None:
+        _check_dev("device_error", device_error, torch.int32)
+    _, nb, _, hkv, d = kv_cache_layer.shape
+    T = k.shape[0]
+    if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d) or slot_mapping.shape != (T,) \
+            or positions.shape != (T,):
+        raise ValueError("k, v must be [T, num_kv_heads, head_dim], slot_mapping and positions [T]")
+    if q is not None and (q.dim() != 3 or q.shape[0] != T or q.shape[2] != d):
+        raise ValueError("q must be [T, num_q_heads, head_dim]")
+    rd = cos_sin_cache.shape[1] if rotary_dim is None else rotary_dim
+    st = _lib.paged_kv_write_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(cos_sin_cache),
+                                  cos_sin_cache.shape[0], rd, int(bool(is_neox)), _ptr(slot_mapping),
+                                  _ptr(kv_cache_layer), T, 0 if q is None else q.shape[1], nb, hkv, d,
+                                  _dtype_code(kv_cache_layer.dtype), _ptr(device_error), _stream_ptr(stream))
+    if st != 0:
+        raise PagedKVError(st, "paged_kv_write_rope")
 
 
 def paged_kv_copy_blocks(kv_cache_layer: torch.Tensor, copies: torch.Tensor,

@@ -55,6 +55,96 @@ int launch_kv_write(const void* k, const void* v, const int64_t* slot_mapping, v
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
+// paged_kv_write_rope: the same scatter with the rotary position embedding
+// applied to K on the way ("AI Infra入门干货总结", section "LLM 推理全流程" /
+// "RoPE": positions are rotation angles read from a precomputed
+// cos_sin_cache [max_position, rotary_dim]; row p = cos of the rotary_dim/2
+// angles of position p, then their sin).  Angle i rotates the pair
+// (i, i + rotary_dim/2) when is_neox, else (2i, 2i+1):
+// x' = x cos - y sin, y' = y cos + x sin, in fp32, rounded to the storage
+// type; dims from rotary_dim on and all of V are copied unchanged.  When q is
+// given, its rows are rotated in place the same way, so one launch does the
+// step's whole rotary work.  One workgroup per token (grid-stride): the
+// token's cos/sin row is read once; consecutive threads take consecutive
+// pairs (neox: both halves are contiguous runs; interleaved: adjacent
+// elements), so every access is coalesced.
+template <bool BF16>
+struct RopeElem;
+template <>
+struct RopeElem<true> {
+  using T = uint16_t;
+  PKV_DEV static float ld(const T* p) { return __uint_as_float((uint32_t)*p << 16); }
+  PKV_DEV static void st(T* p, float x) { *p = f32_to_bf16(x); }
+};
+template <>
+struct RopeElem<false> {
+  using T = float;
+  PKV_DEV static float ld(const T* p) { return *p; }
+  PKV_DEV static void st(T* p, float x) { *p = x; }
+};
+
+template <bool BF16>
+PKV_DEV void rope_rows(const typename RopeElem<BF16>::T* src, typename RopeElem<BF16>::T* dst, int heads,
+                       int head_dim, int half, bool neox, const float* cs) {
+  using E = RopeElem<BF16>;
+  for (int u = threadIdx.x; u < heads * half; u += blockDim.x) {
+    const int h = u / half, i = u - h * half;
+    const int ix = neox ? i : 2 * i, iy = neox ? i + half : 2 * i + 1;
+    const float c = cs[i], s = cs[half + i];
+    const float x = E::ld(src + h * head_dim + ix), y = E::ld(src + h * head_dim + iy);
+    E::st(dst + h * head_dim + ix, x * c - y * s);
+    E::st(dst + h * head_dim + iy, y * c + x * s);
+  }
+  const int pass = head_dim - 2 * half;  // dims past rotary_dim
+  if (pass > 0 && src != dst)
+    for (int u = threadIdx.x; u < heads * pass; u += blockDim.x) {
+      const int h = u / pass, e = 2 * half + (u - h * pass);
+      dst[h * head_dim + e] = src[h * head_dim + e];
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void kv_write_rope_kernel(RopeParams a) {
+  using T = typename RopeElem<BF16>::T;
+  const int half = a.rotary_dim / 2;
+  const int64_t num_slots = (int64_t)a.num_blocks * kBlock;
+  const int row = a.num_kv_heads * a.head_dim;           // elements of a token's K (or V) row
+  const int vchunks = row * (int)sizeof(T) / 16;
+  for (int64_t t = blockIdx.x; t < a.num_tokens; t += gridDim.x) {
+    const int64_t pos = a.positions[t];
+    if (pos < 0 || pos >= a.max_position) {  // nothing of this token is touched
+      if (threadIdx.x == 0 && a.device_error != nullptr) atomicOr(a.device_error, PKV_DEVERR_POSITION);
+      continue;
+    }
+    const float* cs = a.cos_sin_cache + pos * a.rotary_dim;
+    if (a.q != nullptr) {
+      T* qrow = (T*)a.q + t * (int64_t)a.num_q_heads * a.head_dim;
+      rope_rows<BF16>(qrow, qrow, a.num_q_heads, a.head_dim, half, a.is_neox, cs);
+    }
+    const int64_t slot = a.slot_mapping[t];
+    if (slot == -1) continue;  // padding token: no cache write
+    if (slot < 0 || slot >= num_slots) {
+      if (threadIdx.x == 0 && a.device_error != nullptr) atomicOr(a.device_error, PKV_DEVERR_SLOT);
+      continue;
+    }
+    T* kc = (T*)a.cache + slot * row;
+    rope_rows<BF16>((const T*)a.k + t * row, kc, a.num_kv_heads, a.head_dim, half, a.is_neox, cs);
+    const u32x4* vs = (const u32x4*)((const T*)a.v + t * row);
+    u32x4* vd = (u32x4*)((T*)a.cache + (num_slots + slot) * row);
+    for (int i = threadIdx.x; i < vchunks; i += blockDim.x) vd[i] = vs[i];
+  }
+}
+
+int launch_kv_write_rope(const RopeParams& p, bool bf16, hipStream_t stream) {
+  if (p.num_tokens == 0) return 0;
+  const int64_t grid = p.num_tokens < 65536 ? p.num_tokens : 65536;
+  if (bf16)
+    hipLaunchKernelGGL(kv_write_rope_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(kv_write_rope_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 // paged_kv_copy_blocks: destination block <- source block, K and V halves
 // (copy-on-write of a shared prefix block, lpnh.cn/news/2436702, section
 // 2.2).  A block of one half is 16 * num_kv_heads * head_dim contiguous

@@ -108,6 +108,36 @@ int paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
   return ok();
 }
 
+int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* positions,
+                        const float* cos_sin_cache, int32_t max_position, int32_t rotary_dim,
+                        int32_t is_neox, const int64_t* slot_mapping, void* kv_cache_layer,
+                        int64_t num_tokens, int32_t num_q_heads, int32_t num_blocks,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        int32_t* device_error, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
+  if (num_tokens < 0) return fail(PKV_ERR_DIMS, "num_tokens %lld < 0", num_tokens);
+  if (num_blocks <= 0 || num_kv_heads <= 0 || (q != nullptr && num_q_heads <= 0))
+    return fail(PKV_ERR_DIMS, "num_blocks %lld, num_kv_heads %lld, num_q_heads %lld", num_blocks, num_kv_heads,
+                num_q_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_DIMS, "head_dim %lld not 64/128", head_dim);
+  if (rotary_dim < 2 || rotary_dim > head_dim || rotary_dim % 2 != 0 || max_position <= 0)
+    return fail(PKV_ERR_DIMS, "rotary_dim %lld, max_position %lld", rotary_dim, max_position);
+  if (kv_cache_layer == nullptr) return fail(PKV_ERR_NULL, "kv_cache_layer is NULL");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !positions || !cos_sin_cache)
+    return fail(PKV_ERR_NULL, "k, v, slot_mapping, positions or cos_sin_cache is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kv_cache_layer, 16) || (q && !aligned(q, 16)) ||
+      !aligned(slot_mapping, 8) || !aligned(positions, 8) || !aligned(cos_sin_cache, 4))
+    return fail(PKV_ERR_ALIGN, "q, k, v, cache must be 16-byte aligned, slot_mapping / positions 8-byte");
+  pkv::RopeParams p{q, k, v, positions, cos_sin_cache, slot_mapping, kv_cache_layer, num_tokens,
+                    max_position, rotary_dim, is_neox != 0, num_q_heads, num_blocks, num_kv_heads, head_dim,
+                    device_error};
+  if (pkv::launch_kv_write_rope(p, dtype == PKV_BF16, (hipStream_t)stream))
+    return fail(PKV_ERR_LAUNCH, "kv_write_rope launch: %lld", (long long)hipGetLastError());
+  return ok();
+}
+
 int paged_kv_copy_blocks(void* kv_cache_layer, const int32_t* copies, int32_t num_copies,
                          int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                          int32_t* device_error, void* stream) {

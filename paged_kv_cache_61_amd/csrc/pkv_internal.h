@@ -77,6 +77,21 @@ int launch_kv_write(const void* k, const void* v, const int64_t* slot_mapping, v
                     int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
                     int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
                     hipStream_t stream);
+struct RopeParams {
+  void* q;                      // [T][num_q_heads][head_dim] or nullptr, rotated in place
+  const void* k;
+  const void* v;
+  const int64_t* positions;
+  const float* cos_sin_cache;   // [max_position][rotary_dim]
+  const int64_t* slot_mapping;
+  void* cache;
+  int64_t num_tokens;
+  int32_t max_position, rotary_dim, is_neox;
+  int32_t num_q_heads, num_blocks, num_kv_heads, head_dim;
+  int32_t* device_error;
+};
+int launch_kv_write_rope(const RopeParams& p, bool bf16, hipStream_t stream);
+
 int launch_kv_copy_blocks(void* cache, const int32_t* copies, int32_t num_copies, int32_t num_blocks,
                           int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
                           hipStream_t stream);

@@ -439,3 +439,59 @@ def test_copy_blocks_preserves_logical_content(dtype):
     out1 = _run(case, 0.3, dtype)
     case2 = dict(case, pool=pool2, bt=bt2)
     assert np.array_equal(out1, _run(case2, 0.3, dtype))
+
+
+# ---------------------------------------------------------------------------
+# RoPE: hand-worked cases, the complex-number form, relative positions.
+
+def _rope_cache(max_pos, rotary_dim, base=10000.0):
+    inv = base ** (-np.arange(0, rotary_dim, 2, dtype=np.float64) / rotary_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def test_golden_rope():
+    g = json.load(open(os.path.join(GOLDEN, "rope_cases.json")))
+    cache = np.array([g["cos_sin_row"]], dtype=np.float32)
+    for c in g["cases"]:
+        x = np.array([[c["x"]]], dtype=np.float32)
+        got = oracle.rope(x, np.array([0]), cache, g["rotary_dim"], c["is_neox"], "f32")[0, 0]
+        assert np.allclose(got, c["expect"], atol=1e-6), (c, got)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_rope_matches_complex_rotation_and_keeps_norms(is_neox):
+    rng = np.random.default_rng(5)
+    T, H, D, r = 7, 3, 16, 12
+    x = rng.standard_normal((T, H, D)).astype(np.float32)
+    pos = rng.integers(0, 50, T)
+    cache = _rope_cache(64, r)
+    got = oracle.rope(x, pos, cache, r, is_neox, "f32")
+    half = r // 2
+    ix = np.arange(half) if is_neox else 2 * np.arange(half)
+    iy = ix + half if is_neox else ix + 1
+    z = x[:, :, ix].astype(np.float64) + 1j * x[:, :, iy].astype(np.float64)
+    e = cache[pos, :half].astype(np.float64) + 1j * cache[pos, half:r].astype(np.float64)
+    zr = z * e[:, None, :]
+    assert np.allclose(got[:, :, ix], zr.real, atol=1e-12) and np.allclose(got[:, :, iy], zr.imag, atol=1e-12)
+    assert np.array_equal(got[:, :, r:], x[:, :, r:].astype(np.float64))
+    assert np.allclose(np.abs(zr), np.abs(z) * np.abs(e[:, None, :]), atol=1e-12)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_rope_scores_depend_on_relative_position_only(is_neox):
+    rng = np.random.default_rng(6)
+    D = r = 32
+    cache = _rope_cache(256, r)
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    k = rng.standard_normal((1, 1, D)).astype(np.float32)
+    dots = []
+    for m, n in [(10, 3), (40, 33), (200, 193)]:
+        qm = oracle.rope(q, np.array([m]), cache, r, is_neox, "f32")
+        kn = oracle.rope(k, np.array([n]), cache, r, is_neox, "f32")
+        dots.append(float((qm * kn).sum()))
+    assert max(dots) - min(dots) < 1e-4 * max(1.0, abs(dots[0]))
+    # a different offset changes the score
+    q0 = oracle.rope(q, np.array([10]), cache, r, is_neox, "f32")
+    k0 = oracle.rope(k, np.array([2]), cache, r, is_neox, "f32")
+    assert abs(float((q0 * k0).sum()) - dots[0]) > 1e-3
