@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-int8", action="store_true",
+                    help="INT8 KV cache (paged_kv_write_int8 + paged_attention_int8)")
     ap.add_argument("--rope", action="store_true",
                     help="write the step's tokens with paged_kv_write_rope (RoPE on K, and on q in place)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
@@ -72,6 +74,9 @@ def accounting(wl):
     a["decode_io_bytes"] = 2 * int(dec.sum()) * Hq * D * s            # q read + out written
     a["decode_table_bytes"] = int(((L[dec] + 15) // 16).sum()) * 4
     a["decode_bytes"] = a["decode_kv_bytes"] + a["decode_io_bytes"] + a["decode_table_bytes"]
+    # INT8 cache: one byte per element plus a float32 scale per (token, kv head) row
+    a["decode_kv_bytes_int8"] = int(L[dec].sum()) * 2 * Hkv * (D + 4)
+    a["decode_bytes_int8"] = a["decode_kv_bytes_int8"] + a["decode_io_bytes"] + a["decode_table_bytes"]
     a["prefill_pairs_per_head"] = int((ql[pre] * c[pre] + ql[pre] * (ql[pre] + 1) // 2).sum())
     a["prefill_flops"] = 4 * D * Hq * a["prefill_pairs_per_head"]
     a["prefill_bytes"] = int(L[pre].sum()) * kv_token_bytes + 2 * int(ql[pre].sum()) * Hq * D * s
@@ -220,9 +225,31 @@ def main():
             e.record()
     torch.cuda.synchronize()
 
+    if args.kv_int8:
+        if args.rope:
+            raise SystemExit("--kv-int8 and --rope are separate modes")
+        # quantise every slot of the pool once (unused slots hold NaN: their
+        # codes and scales are never read)
+        nb = pool.shape[1]
+        codes = torch.empty(pool.shape, dtype=torch.int8, device=dev)
+        kv_scales = torch.empty(pool.shape[:4], dtype=torch.float32, device=dev)
+        pkv.paged_kv_write_int8(pool[0].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
+                                pool[1].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
+                                torch.arange(nb * 16, dtype=torch.int64, device=dev), codes, kv_scales)
+        del pool
+        torch.cuda.synchronize()
+
     def step(evs=None):
         if evs is not None:
             evs[2 * nph].record()
+        if args.kv_int8:
+            pkv.paged_kv_write_int8(k_new, v_new, slot_mapping, codes, kv_scales)
+            if evs is not None:
+                evs[2 * nph + 1].record()
+            pkv.paged_attention_int8(q, codes, kv_scales, bt, sl, qsl, nct, wl.scale,
+                                     max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, out=out,
+                                     workspace=ws, phase_events=None if evs is None else evs[:2 * nph])
+            return
         if args.rope:
             pkv.paged_kv_write_rope(k_new, v_new, positions, cos_sin, slot_mapping, pool, q=q)
         else:
@@ -270,8 +297,14 @@ def main():
     write_ms = float(np.mean([evs[2 * nph].elapsed_time(evs[2 * nph + 1]) for evs in step_events]))
     write_bytes = acct["write_rope_bytes"] if args.rope else acct["write_bytes"]
     step_bytes = acct["step_bytes"] - acct["write_bytes"] + write_bytes
+    dec_bytes = acct["decode_bytes"]
+    if args.kv_int8:   # k/v read in their dtype, written as codes + scales
+        T_, s_ = wl.num_tokens, 2 if wl.dtype == "bf16" else 4
+        write_bytes = 2 * T_ * wl.num_kv_heads * (wl.head_dim * s_ + wl.head_dim + 4) + 8 * T_
+        dec_bytes = acct["decode_bytes_int8"]
+        step_bytes = dec_bytes + acct["prefill_bytes"] + write_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    rows_gbs = acct["decode_bytes"] / (phase_ms["rows"] * 1e-3) / 1e9 if phase_ms["rows"] > 0 else 0.0
+    rows_gbs = dec_bytes / (phase_ms["rows"] * 1e-3) / 1e9 if phase_ms["rows"] > 0 else 0.0
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -291,20 +324,23 @@ def main():
             "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
             "head_dim": wl.head_dim, "block_size": 16, "num_blocks": wl.num_blocks,
             "decode_kv_tokens": acct["decode_kv_tokens"], "max_seq_len": wl.max_seq_len,
+            "kv_cache": "int8 codes + float32 scale per (token, kv head)" if args.kv_int8 else wl.dtype,
         },
         "roofline": {
-            "kernel": "row_attn_kernel (decode rows + split-KV partitions)",
+            "kernel": ("row_attn_i8_kernel (INT8 cache: decode rows + split-KV partitions)" if args.kv_int8
+                       else "row_attn_kernel (decode rows + split-KV partitions)"),
             "bound": "hbm",
             "achieved": round(rows_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload),
-            "algorithmic_bytes_per_launch": acct["decode_bytes"],
+            "traffic": None if args.kv_int8 else measured_traffic(args.workload),
+            "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": round(phase_ms["rows"], 5),
         },
         "phases_ms": {k: round(v, 5) for k, v in phase_ms.items()},
-        "write": {"kernel": "kv_write_rope_kernel (RoPE on K and q)" if args.rope else "kv_write_kernel",
+        "write": {"kernel": ("kv_write_rope_kernel (RoPE on K and q)" if args.rope else
+                             "kv_write_i8_kernel (quantising)" if args.kv_int8 else "kv_write_kernel"),
                   "ms": round(write_ms, 5), "bytes": write_bytes,
                   "GB/s": round(write_bytes / (write_ms * 1e-3) / 1e9, 1) if write_ms > 0 else None},
         "step_algorithmic_bytes": step_bytes,

@@ -244,6 +244,41 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
                         int32_t* device_error, void* stream);
 
 /*
+ * INT8 KV cache (online quantisation of the cache as it is written and
+ * dequantisation as it is read: lpnh.cn/news/2436702, section 4.2, "KV
+ * Cache 量化").  The cache of one layer is
+ *   kv_cache_layer  int8 [2][num_blocks][16][num_kv_heads][head_dim] codes,
+ *   kv_scales       float32 [2][num_blocks][16][num_kv_heads] scales,
+ * value = code * scale.  Each (token, K or V, kv head) row of head_dim
+ * values is quantised on its own: scale = max|x| / 127, code =
+ * round-half-even(x / scale) clamped to [-127, 127], both divisions IEEE
+ * float32; an all-zero row has scale 0 and codes 0.  Half the bytes of a
+ * bf16 cache, plus 4 bytes per row.
+ *
+ * paged_kv_write_int8 — quantise and store the step's new K/V (k, v in
+ *   dtype, [num_tokens][num_kv_heads][head_dim]) at slot_mapping, like
+ *   paged_kv_write; codes and scales of the addressed slots change.
+ * paged_attention_int8 — paged_attention over such a cache: the keys and
+ *   values are the dequantised rows; q and out are in dtype (bf16 or fp32).
+ *   Every query row (decode rows and the rows of prefill chunks) runs on the
+ *   row kernel, with split-KV partitions for rows past 512 tokens.
+ *   phase_events as for paged_attention_profiled, or NULL.
+ * Other arguments, the workspace and the error conventions are those of
+ * paged_kv_write / paged_attention.
+ */
+int paged_kv_write_int8(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
+                        float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream);
+int paged_attention_int8(void* out, const void* q, const void* kv_cache_layer, const float* kv_scales,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                         float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                         int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* phase_events);
+
+/*
  * paged_kv_copy_blocks — copy whole cache blocks (K and V, every kv head):
  * the copy half of copy-on-write prefix sharing (lpnh.cn/news/2436702,
  * section 2.2: sequences share prefix blocks and a block is copied only

@@ -61,7 +61,48 @@ def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
         return bf16_bits_to_f64(x)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":   # values already decoded (e.g. a dequantised cache)
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache: online quantisation of each new token as it is written
+# (lpnh.cn/news/2436702, section 4.2: the KV cache is produced at run time, so
+# it is quantised and dequantised online; FP16 -> INT8 halves its size).
+# Readings (the page gives no scheme): symmetric, one float32 scale per
+# (token, kv head) row of head_dim values, scale = max|x| / 127 (float32
+# division), code = round-half-even(x / scale) in float32, clamped to
+# [-127, 127]; an all-zero row has scale 0 and codes 0.  A value is read back
+# as code * scale.  Both divisions are float32 so that the codes, integers
+# decided by floating point, are taken in one stated precision.
+
+def quantize_int8(x: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """``x [..., D]`` storage values -> (int8 codes ``[..., D]``, float32 scales ``[...]``)."""
+    xf = to_f64(x, dtype).astype(np.float32)          # exact: bf16 and f32 values are float32
+    amax = np.abs(xf).max(axis=-1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint((xf / safe[..., None]).astype(np.float32))
+    codes = np.clip(q, -127, 127).astype(np.int8)
+    codes[scale == 0] = 0
+    return codes, scale
+
+
+def dequantize_int8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    return codes.astype(np.float64) * scales.astype(np.float64)[..., None]
+
+
+def kv_write_int8(codes: np.ndarray, scales: np.ndarray, k: np.ndarray, v: np.ndarray,
+                  slot_mapping: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """INT8 cache write: ``codes [2, NB, 16, Hkv, D]`` int8 and ``scales
+    [2, NB, 16, Hkv]`` float32 get token ``t``'s quantised K and V at
+    ``slot_mapping[t]`` (-1 = skip), as ``kv_write`` places bf16 / fp32 rows."""
+    kc, ks = quantize_int8(k, dtype)
+    vc, vs = quantize_int8(v, dtype)
+    codes = kv_write(codes, kc, vc, slot_mapping)
+    scales = kv_write(scales[..., None], ks[..., None], vs[..., None], slot_mapping)[..., 0]
+    return codes, scales
 
 
 # ---------------------------------------------------------------------------
@@ -212,6 +253,16 @@ def attention(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
         Vh = V[:, np.arange(Hq) // (Hq // Hkv), :]             # [L, Hq, D]
         out[qs:qe] = np.einsum("iht,thd->ihd", w, Vh)
     return out
+
+
+def attention_int8(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, block_table: np.ndarray,
+                   seq_lens: np.ndarray, query_start_loc: np.ndarray,
+                   num_computed_tokens: np.ndarray, scale: float, dtype: str,
+                   requests: Optional[Iterable[int]] = None) -> np.ndarray:
+    """``attention`` over an INT8 cache: the keys and values are the
+    dequantised ``code * scale`` (q in ``dtype``)."""
+    return attention(to_f64(q, dtype), dequantize_int8(codes, scales), block_table, seq_lens,
+                     query_start_loc, num_computed_tokens, scale, "f64", requests=requests)
 
 
 def attention_rows(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,

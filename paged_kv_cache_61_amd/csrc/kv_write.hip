@@ -145,6 +145,79 @@ int launch_kv_write_rope(const RopeParams& p, bool bf16, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
+// paged_kv_write_int8: quantise each new token's K and V rows, per kv head,
+// to int8 codes with one float32 scale, and store both at the token's slot
+// (online KV-cache quantisation, lpnh.cn/news/2436702 section 4.2).  Per
+// (token, K or V, head) row of head_dim values: scale = max|x| / 127,
+// code = round-half-even(x / scale) clamped to [-127, 127]; an all-zero row
+// gets scale 0 and codes 0.  Both divisions are IEEE float32 so the codes
+// are reproducible.  One wave per row: each lane holds head_dim / 64 values,
+// the row max is a wave reduction, lane 0 stores the scale.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void kv_write_i8_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                          const int64_t* __restrict__ slot_mapping,
+                                                          int8_t* __restrict__ cache, float* __restrict__ scales,
+                                                          int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                                                          int32_t* __restrict__ device_error) {
+  constexpr int E = D / kWave;  // values per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t rows = num_tokens * 2 * num_kv_heads;
+  const int64_t num_slots = (int64_t)num_blocks * kBlock;
+  for (int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave; row < rows;
+       row += (int64_t)gridDim.x * blockDim.x / kWave) {
+    const int64_t t = row / (2 * num_kv_heads);
+    const int rem = (int)(row - t * 2 * num_kv_heads);
+    const int kv = rem / num_kv_heads, h = rem - kv * num_kv_heads;
+    const int64_t slot = slot_mapping[t];
+    if (slot == -1) continue;
+    if (slot < 0 || slot >= num_slots) {
+      if (device_error != nullptr && lane == 0 && kv == 0 && h == 0) atomicOr(device_error, PKV_DEVERR_SLOT);
+      continue;
+    }
+    const size_t src = ((size_t)t * num_kv_heads + h) * D + lane * E;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if constexpr (BF16)
+        x[e] = __uint_as_float((uint32_t)((const uint16_t*)(kv ? v : k))[src + e] << 16);
+      else
+        x[e] = ((const float*)(kv ? v : k))[src + e];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = wave_max(amax);
+    const float scale = amax / 127.f;
+    int8_t c[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) c[e] = scale > 0.f ? (int8_t)fminf(fmaxf(rintf(x[e] / scale), -127.f), 127.f) : 0;
+    int8_t* dst = cache + ((size_t)kv * num_slots + slot) * num_kv_heads * D + (size_t)h * D + lane * E;
+    if constexpr (E == 2)
+      *(uint16_t*)dst = (uint16_t)((uint8_t)c[0] | ((uint16_t)(uint8_t)c[1] << 8));
+    else
+      dst[0] = c[0];
+    if (lane == 0) scales[((size_t)kv * num_slots + slot) * num_kv_heads + h] = scale;
+  }
+}
+
+int launch_kv_write_i8(const void* k, const void* v, const int64_t* slot_mapping, void* cache, float* scales,
+                       int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, bool bf16,
+                       int32_t* device_error, hipStream_t stream) {
+  if (num_tokens == 0) return 0;
+  const int64_t rows = num_tokens * 2 * num_kv_heads;
+  int64_t grid = (rows + 3) / 4;
+  if (grid > 65536) grid = 65536;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, k, v, slot_mapping, (int8_t*)cache,
+                       scales, num_tokens, num_blocks, num_kv_heads, device_error);
+  };
+  if (head_dim == 64)
+    bf16 ? go(kv_write_i8_kernel<true, 64>) : go(kv_write_i8_kernel<false, 64>);
+  else
+    bf16 ? go(kv_write_i8_kernel<true, 128>) : go(kv_write_i8_kernel<false, 128>);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 // paged_kv_copy_blocks: destination block <- source block, K and V halves
 // (copy-on-write of a shared prefix block, lpnh.cn/news/2436702, section
 // 2.2).  A block of one half is 16 * num_kv_heads * head_dim contiguous

@@ -184,7 +184,8 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                           int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
                           int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                          void* const* phase_events) {
+                          void* const* phase_events, const float* kv_scales = nullptr) {
+  const bool i8 = kv_scales != nullptr;   // int8 cache + per-(token, head) scales
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
   if (num_reqs < 0 || num_tokens < 0)
@@ -206,11 +207,12 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(kv_cache_layer, 16) ||
       !aligned(workspace, 256))
     return fail(PKV_ERR_ALIGN, "out, q, cache need 16-byte alignment, workspace 256-byte");
-  if ((int64_t)num_blocks * pkv::kBlock * num_kv_heads * head_dim * eb > (int64_t)1 << 46)
+  if ((int64_t)num_blocks * pkv::kBlock * num_kv_heads * head_dim * (i8 ? 1 : eb) > (int64_t)1 << 46)
     return fail(PKV_ERR_DIMS, "cache too large");
+  if (i8 && !aligned(kv_scales, 4)) return fail(PKV_ERR_ALIGN, "kv_scales needs 4-byte alignment");
 
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t tile_rows = tile_rows_for(dtype, head_dim, group);
+  const int64_t tile_rows = i8 ? 1 : tile_rows_for(dtype, head_dim, group);
   const pkv::WsLayout ws =
       pkv::ws_layout(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len, max_seq_len, tile_rows);
   if (workspace_bytes < ws.total)
@@ -235,7 +237,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   pp.max_seq_len = max_seq_len;
   pp.max_blocks_per_req = max_blocks_per_req;
   pp.split_decode = 1;
-  pp.mfma_prefill = prefill_on_mfma(dtype, head_dim) ? 1 : 0;
+  pp.mfma_prefill = !i8 && prefill_on_mfma(dtype, head_dim) ? 1 : 0;
   pp.prefill_tile_rows = (int32_t)tile_rows;
   pp.hdr = hdr;
   pp.row_items = (int4*)(wsb + ws.row_items);
@@ -296,13 +298,15 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   rp.num_q_heads = num_q_heads;
   rp.num_kv_heads = num_kv_heads;
   rp.group = group;
-  rp.head_groups = (group + pkv::kMaxGroupRegs - 1) / pkv::kMaxGroupRegs;
+  const int gmax = i8 ? pkv::max_group_regs_i8(dtype) : pkv::kMaxGroupRegs;
+  rp.head_groups = (group + gmax - 1) / gmax;
   rp.num_blocks = num_blocks;
   rp.max_blocks_per_req = max_blocks_per_req;
   {
     const int64_t bound_waves = ws.cap_row_items * num_kv_heads * rp.head_groups;
     mark(PKV_PHASE_ROWS, 0);
-    if (pkv::launch_rows(rp, dtype, head_dim, bound_waves, cus, s))
+    if (i8 ? pkv::launch_rows_i8(rp, kv_scales, dtype, head_dim, bound_waves, cus, s)
+           : pkv::launch_rows(rp, dtype, head_dim, bound_waves, cus, s))
       return fail(PKV_ERR_LAUNCH, "row launch failed");
     mark(PKV_PHASE_ROWS, 1);
   }
@@ -349,6 +353,42 @@ int paged_attention_profiled(void* out, const void* q, const void* kv_cache_laye
                         num_computed_tokens, scale, num_reqs, num_tokens, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, max_blocks_per_req, max_query_len, max_seq_len, dtype,
                         workspace, workspace_bytes, stream, phase_events);
+}
+
+int paged_attention_int8(void* out, const void* q, const void* kv_cache_layer, const float* kv_scales,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                         float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                         int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* phase_events) {
+  if (!kv_scales) return fail(PKV_ERR_NULL, "kv_scales is NULL");
+  return attention_impl(out, q, kv_cache_layer, block_table, seq_lens, query_start_loc,
+                        num_computed_tokens, scale, num_reqs, num_tokens, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, max_blocks_per_req, max_query_len, max_seq_len, dtype,
+                        workspace, workspace_bytes, stream, phase_events, kv_scales);
+}
+
+int paged_kv_write_int8(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
+                        float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
+  if (num_tokens < 0) return fail(PKV_ERR_DIMS, "num_tokens %lld < 0", num_tokens);
+  if (num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_DIMS, "num_blocks %lld, num_kv_heads %lld", num_blocks, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_DIMS, "head_dim %lld not 64/128", head_dim);
+  if (!kv_cache_layer || !kv_scales) return fail(PKV_ERR_NULL, "kv_cache_layer or kv_scales is NULL");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping) return fail(PKV_ERR_NULL, "k, v or slot_mapping is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kv_cache_layer, 16) || !aligned(kv_scales, 4) ||
+      !aligned(slot_mapping, 8))
+    return fail(PKV_ERR_ALIGN, "k, v, cache must be 16-byte aligned, scales 4-byte, slot_mapping 8-byte");
+  if (pkv::launch_kv_write_i8(k, v, slot_mapping, kv_cache_layer, kv_scales, num_tokens, num_blocks, num_kv_heads,
+                              head_dim, dtype == PKV_BF16, device_error, (hipStream_t)stream))
+    return fail(PKV_ERR_LAUNCH, "kv_write_int8 launch: %lld", (long long)hipGetLastError());
+  return ok();
 }
 
 int32_t pkv_read_device_error(const void* workspace, void* stream) {

@@ -92,6 +92,14 @@ struct RopeParams {
 };
 int launch_kv_write_rope(const RopeParams& p, bool bf16, hipStream_t stream);
 
+int launch_kv_write_i8(const void* k, const void* v, const int64_t* slot_mapping, void* cache, float* scales,
+                       int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, bool bf16,
+                       int32_t* device_error, hipStream_t stream);
+// Row kernel over an int8 cache (decode_i8.hip); query heads per wave:
+int max_group_regs_i8(int32_t dtype);
+int launch_rows_i8(const RowParams& p, const float* kv_scales, int32_t dtype, int32_t head_dim,
+                   int64_t bound_waves, int cus, hipStream_t stream);
+
 int launch_kv_copy_blocks(void* cache, const int32_t* copies, int32_t num_copies, int32_t num_blocks,
                           int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
                           hipStream_t stream);

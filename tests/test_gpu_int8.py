@@ -1,0 +1,99 @@
+"""INT8 KV cache on the GPU against the fp64 oracle.
+
+* paged_kv_write_int8: codes and scales bit for bit (both sides take the
+  rounding decisions in IEEE float32), untouched slots unchanged.
+* paged_attention_int8: decode rows, prefill rows and split-KV rows over
+  the dequantised cache within the output tolerance, for bf16 and fp32 q,
+  head_dim 64 / 128 and several GQA groups; unused slots hold garbage codes
+  and NaN scales, which must never reach the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import assert_close, from_dev, out_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _quantised_pool(wl):
+    """The workload's cache quantised row by row; NaN (unused) slots get
+    garbage codes and NaN scales."""
+    with np.errstate(invalid="ignore"):
+        f = oracle.to_f64(wl.pool, wl.dtype)
+    bad = np.isnan(f).any(axis=-1)
+    clean = np.where(np.isnan(f), 0.0, f).astype(np.float32)
+    codes, scales = oracle.quantize_int8(clean, "f32")
+    codes[bad] = np.int8(0x5A)
+    scales = scales.copy()
+    scales[bad] = np.nan
+    return codes, scales
+
+
+def _run(wl, dtype_q):
+    import paged_kv_cache_61_amd as pkv
+    codes, scales = _quantised_pool(wl)
+    d_codes = torch.from_numpy(codes).cuda()
+    d_scales = torch.from_numpy(scales).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.paged_kv_write_int8(to_dev(wl.k_new, wl.dtype), to_dev(wl.v_new, wl.dtype),
+                            torch.from_numpy(wl.slot_mapping).cuda(), d_codes, d_scales, device_error=err)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    ws = torch.empty(max(256, pkv.paged_attention_workspace_size(wl.num_reqs, wl.num_tokens, wl.num_q_heads,
+                                                                 wl.head_dim, wl.max_query_len, wl.max_seq_len)),
+                     dtype=torch.uint8, device="cuda")
+    out = pkv.paged_attention_int8(to_dev(wl.q, dtype_q), d_codes, d_scales, i32(wl.block_table),
+                                   i32(wl.seq_lens), i32(wl.query_start_loc), i32(wl.num_computed_tokens),
+                                   wl.scale, max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and pkv.pkv_read_device_error(ws) == 0
+    ref_codes, ref_scales = oracle.kv_write_int8(codes, scales, wl.k_new, wl.v_new, wl.slot_mapping, wl.dtype)
+    return out, d_codes.cpu().numpy(), d_scales.cpu().numpy(), ref_codes, ref_scales
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 8, 8), ("bf16", 128, 32, 8), ("bf16", 64, 16, 2),
+                                            ("f32", 64, 8, 2), ("f32", 128, 4, 4), ("bf16", 128, 64, 8)])
+def test_int8_write_and_attention(dtype, D, Hq, Hkv):
+    _gpu()
+    reqs = [(0, 1), (37, 1), (600, 1), (1500, 1), (15, 9), (40, 33), (0, 70), (511, 1), (512, 1), (2100, 2)]
+    wl = workloads.build(workloads.small_spec(f"int8 {dtype} {D} {Hq}/{Hkv}", 31, dtype, Hq, Hkv, D, reqs))
+    out, got_codes, got_scales, ref_codes, ref_scales = _run(wl, dtype)
+    # write: bit for bit (NaN scales of untouched slots compared as bits)
+    assert np.array_equal(got_codes, ref_codes)
+    assert got_scales.tobytes() == ref_scales.astype(np.float32).tobytes()
+    ref = oracle.attention_int8(wl.q, ref_codes, np.nan_to_num(ref_scales, nan=0.0), wl.block_table,
+                                wl.seq_lens, wl.query_start_loc, wl.num_computed_tokens, wl.scale, dtype)
+    assert_close(out_f64(out), ref, dtype, f"int8 cache attention {D} {Hq}/{Hkv}")
+    # for information: distance from attention over the unquantised cache
+    plain = oracle.attention(wl.q, oracle.kv_write(wl.pool, wl.k_new, wl.v_new, wl.slot_mapping), wl.block_table,
+                             wl.seq_lens, wl.query_start_loc, wl.num_computed_tokens, wl.scale, dtype)
+    print(f"[int8] quantisation effect on the output: max abs {np.abs(out_f64(out) - plain).max():.4f}", flush=True)
+
+
+def test_int8_write_zero_rows_and_padding():
+    _gpu()
+    import paged_kv_cache_61_amd as pkv
+    T, Hkv, D, NB = 6, 2, 128, 4
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    k[1] = 0.0                      # all-zero rows: scale 0, codes 0
+    v[2, 1] = 0.0
+    slots = np.array([3, 17, -1, 40, 63, 0], np.int64)   # one padding token
+    codes = np.full((2, NB, 16, Hkv, D), 7, np.int8)
+    scales = np.full((2, NB, 16, Hkv), 5.0, np.float32)
+    d_codes, d_scales = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    pkv.paged_kv_write_int8(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda(),
+                            d_codes, d_scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.kv_write_int8(codes, scales, k, v, slots, "f32")
+    assert np.array_equal(d_codes.cpu().numpy(), rc) and d_scales.cpu().numpy().tobytes() == rs.tobytes()
+    assert rs[0, 1, 1].tolist() == [0.0, 0.0]

@@ -495,3 +495,56 @@ def test_rope_scores_depend_on_relative_position_only(is_neox):
     q0 = oracle.rope(q, np.array([10]), cache, r, is_neox, "f32")
     k0 = oracle.rope(k, np.array([2]), cache, r, is_neox, "f32")
     assert abs(float((q0 * k0).sum()) - dots[0]) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache: hand-worked codes, the error bound of the rounding, and
+# attention over exactly representable values equals the unquantised oracle.
+
+def test_golden_int8_quantisation():
+    g = json.load(open(os.path.join(GOLDEN, "int8_quant.json")))
+    x = np.array([r["x"] for r in g["rows"]], np.float32)
+    codes, scales = oracle.quantize_int8(x, "f32")
+    assert codes.tolist() == [r["codes"] for r in g["rows"]]
+    assert scales.tolist() == [r["scale"] for r in g["rows"]]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_int8_rounding_error_bound(dtype):
+    rng = np.random.default_rng(8)
+    x = _draw(rng, (50, 4, 128), dtype)
+    codes, scales = oracle.quantize_int8(x, dtype)
+    xf = oracle.to_f64(x, dtype)
+    err = np.abs(oracle.dequantize_int8(codes, scales) - xf)
+    # half a step, plus float32 rounding of the quotient
+    assert np.all(err <= scales[..., None] * (0.5 + 1e-5) + 1e-30)
+    amax_idx = np.abs(xf).argmax(axis=-1)
+    assert np.all(np.abs(np.take_along_axis(codes, amax_idx[..., None], -1)) == 127)
+    assert codes.min() >= -127
+
+
+def test_int8_attention_equals_plain_on_representable_values():
+    # values k * 2^-4 with |k| <= 127 and every row's max exactly 127 * 2^-4:
+    # quantisation is then exact and INT8 attention must equal the plain one
+    rng = np.random.default_rng(9)
+    Hq, Hkv, D = 8, 2, 64
+    reqs = [(30, 1), (0, 20), (60, 5)]
+    def rep(shape):
+        v = rng.integers(-126, 127, shape).astype(np.float32)
+        v[..., 0] = 127.0
+        return (v / 16).astype(np.float32)
+    Ks = [rep((c + ql, Hkv, D)) for c, ql in reqs]
+    Vs = [rep((c + ql, Hkv, D)) for c, ql in reqs]
+    case = _ragged_case(9, "f32", Hq, Hkv, D, reqs)
+    pool, bt = _scatter_requests(rng, Ks, Vs, [c for c, _ in reqs], Hkv, D, "f32")
+    case = dict(case, Ks=Ks, Vs=Vs, pool=pool, bt=bt)
+    NB = pool.shape[1]
+    codes = np.zeros((2, NB, 16, Hkv, D), np.int8)
+    scales = np.zeros((2, NB, 16, Hkv), np.float32)
+    for r, (K, V) in enumerate(zip(Ks, Vs)):
+        slots = np.array([bt[r, t // 16] * 16 + t % 16 for t in range(len(K))], np.int64)
+        codes, scales = oracle.kv_write_int8(codes, scales, K, V, slots, "f32")
+    ref = _run(case, 0.2, "f32")
+    got = oracle.attention_int8(case["q"], codes, scales, bt, case["L"], case["qsl"], case["nct"], 0.2, "f32")
+    assert np.allclose(got, ref, atol=1e-12, rtol=0)
+    assert np.all(scales[:, bt[0, 0]][:, 0] == np.float32(1 / 16))   # max 127/16 over 127
