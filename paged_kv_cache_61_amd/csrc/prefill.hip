@@ -24,26 +24,30 @@
 //                     folded in; rescaling skipped when no row max moved;
 //   O^T += V^T P^T   (A = V^T from LDS, B = P from the S^T registers packed
 //                     to bf16), so O's rows are again lane-local.
-// Tiles of 64 keys stream from the cache into a 4-stage LDS ring with
-// buffer_load ... lds (no staging registers): each wave copies one cache block
-// (16 token rows) of K (waves 0-3) or V (waves 4-7), three tiles ahead of the
-// tile being computed; the buffer descriptor of a block covers only the rows
-// before the chunk's last key, so later rows read as zeros and tail garbage
-// or NaN in the cache never reaches the output.  Rows are stored as they are
-// in the cache (256 bytes for head_dim 128) with 16-byte chunk c of row r at
-// position c ^ swz(r mod 16), swz = rotate left by one bit in 4 bits: swz is
-// a permutation (the K operand reads of 16 consecutive keys hit 16 distinct
-// positions) that keeps bits 1-3 distinct within each aligned group of 4 rows
-// (a transposed V read, 4 rows x 2 adjacent chunks per 16 lanes, hits 8
-// distinct positions), so neither read conflicts on banks.  (A plain
-// c ^ (r mod 16) makes the transposed reads conflict two ways.)  The V^T operand of the second
-// product comes from ds_read_b64_tr_b16 (two 4-key transposed reads per
-// lane), in the key order of the S^T accumulator (8*(i/4) + 4*(l/32) + i%4).
-// One barrier per tile: after it, tile t is complete in LDS and every wave
-// has finished tile t-1, whose ring slot receives tile t+3 once this wave has
-// computed tile t.
+// Tiles of 64 keys stream from the cache into a 4-slot LDS ring with
+// buffer_load ... lds (no staging registers): each wave copies one cache
+// block (16 token rows) of K (waves 0-3) or V (waves 4-7), two tiles ahead of
+// the tile being computed; the buffer descriptor of a block covers only the
+// rows before the chunk's last key, so later rows read as zeros and tail
+// garbage or NaN in the cache never reaches the output.  Rows are stored as
+// they are in the cache (256 bytes for head_dim 128) with 16-byte chunk c of
+// row r at position c ^ swz(r mod 16), swz = rotate left by one bit in 4
+// bits: swz is a permutation (the K operand reads of 16 consecutive keys hit
+// 16 distinct positions) that keeps bits 1-3 distinct within each aligned
+// group of 4 rows (a transposed V read, 4 rows x 2 adjacent chunks per 16
+// lanes, hits 8 distinct positions), so neither read conflicts on banks.
+// (A plain c ^ (r mod 16) makes the transposed reads conflict two ways.)  The
+// V^T operand of the second product comes from ds_read_b64_tr_b16 (two 4-key
+// transposed reads per lane), in the key order of the S^T accumulator
+// (8*(i/4) + 4*(l/32) + i%4).
+// The two waves on each SIMD alternate ("ping-pong"): while one issues the
+// MFMAs of a tile (PV of the previous tile, QK of this one) the other runs
+// its softmax; workgroup barriers between the phases keep the two groups
+// half a tile apart (see the slot schedule in the kernel).
 // Causal masks are applied only on tiles that cross a row's position.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pkv_common.h"
 #include "pkv_internal.h"
@@ -68,6 +72,16 @@ constexpr int kDTiles = kD / 32;            // O^T row tiles
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define PKV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define PKV_INLINE __attribute__((always_inline))
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, class Fn>
+PKV_DEV void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 PKV_DEV f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -202,7 +216,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     // Stream tile `tile` into ring slot tile % kStages: this wave's block,
     // 4 instructions of 4 token rows; lane L of instruction j carries chunk
     // (L & 15) ^ row of token row 4j + L/16, so LDS holds the swizzled layout.
-    auto issue_tile = [&](int tile) {
+    auto issue_tile = [&](int tile) PKV_INLINE {
       const int kv0 = tile * kPfKeys;
       const int nvalid = kv_end - (kv0 + kBlock * cblk);  // rows of this block before kv_end
       const char* src = cbase;
@@ -233,25 +247,93 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    auto compute_tile = [&](int tile) {
-      const char* kl = lds + (tile % kStages) * kStage;
-      const char* vl = kl + kHalfTile;
-      const int kv0 = tile * kPfKeys;
+    // Ping-pong over two wave groups, waves 0-3 and 4-7 (every SIMD runs one
+    // wave of each).  A tile's work is cut into an MFMA phase,
+    //   mfma(t): O^T += V(t-1)^T P(t-1) (t >= 1), then S^T(t) = K(t) Q^T (t < n),
+    // and a VALU phase,
+    //   vec(t):  causal mask, online softmax of S(t) -> P(t) (and the rare O
+    //            rescale, after PV(t-1) and before PV(t)).
+    // Workgroup barriers cut time into slots; in slot s group 0 runs entry s
+    // and group 1 entry s-1 of mfma(0), vec(0), mfma(1), vec(1), ..., mfma(n),
+    // so on every SIMD one wave issues MFMAs while the other runs its
+    // softmax.  Tile u must be in LDS from slot 2u on: its copies are issued
+    // at slot 2u-4 (two tiles ahead) into ring slot u % 4, whose previous
+    // tile u-4 was last read in slot 2u-5.
+    const int grp = w >> 2;
+    f32x16 sacc[2];   // S^T(t) from its MFMA phase to its softmax
+    u32x4 pf[4];      // P^T(t) from its softmax to its PV
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pf[ks] = u32x4{0, 0, 0, 0};
 
-      // S^T = K Q^T for the two 32-key halves of the tile.
-      f32x16 sacc[2];
+    // The MFMA phase is 32 units (16 of PV, 16 of QK), each one LDS operand
+    // fragment and one MFMA; with one wave per SIMD in this phase nothing
+    // hides an LDS read's latency, so fragment u + kAhead is read while unit
+    // u runs (a ring of kAhead + 1 fragments).  Lane offsets inside a tile:
+    // a K fragment of k-step ks, key half kt is row kt*32 + lrow, chunk
+    // (2ks + half) ^ swz(lrow & 15); a V^T fragment of k-step ks, head_dim
+    // tile dt reads rows 16ks + key0 (+8), chunk 4dt + (tdb >> 3), where the
+    // swizzle depends only on the row mod 16, so ks and kt enter as constants.
+    constexpr int kAhead = 5;
+    const int kswz = swz(lrow & 15);
+    const int key0 = 4 * half + (ts >> 2);
+    const int vsw0 = swz(key0 & 15), vsw1 = swz((key0 + 8) & 15);
+    const int kbase_off = lrow * kRowB;
+    const int vbase0 = key0 * kRowB + (tdb & 7) * 2, vbase1 = (key0 + 8) * kRowB + (tdb & 7) * 2;
+    auto read_k = [&](const char* kl, int q) PKV_INLINE -> u32x4 {  // unit 16 + q
+      const int ks = q >> 1, kt = q & 1;
+      return *(const u32x4*)(kl + kbase_off + kt * 32 * kRowB + (((2 * ks + half) ^ kswz) << 4));
+    };
+    auto read_v = [&](const char* vl, int u) PKV_INLINE -> u32x4 {  // unit u < 16
+      const int ks = u >> 2, c = 4 * (u & 3) + (tdb >> 3);
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vl + ks * 16 * kRowB + vbase0 + ((c ^ vsw0) << 4)));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vl + ks * 16 * kRowB + vbase1 + ((c ^ vsw1) << 4)));
+      const u32x2 v0 = __builtin_bit_cast(u32x2, t0), v1 = __builtin_bit_cast(u32x2, t1);
+      return u32x4{v0.x, v0.y, v1.x, v1.y};
+    };
+    auto mfma_phase = [&](int t) PKV_INLINE {
+      __builtin_amdgcn_s_setprio(1);  // the MFMA stream issues first on its SIMD
+      if (t >= 1) {
+        // O^T += V^T P^T: the V^T operand of lane l (head_dim dt*32 + l%32,
+        // keys 16*ks + 8*jj + 4*half + 0..3, jj = 0, 1) comes from two
+        // transposed reads whose source lanes point at those keys' rows.
+        const char* vl = lds + ((t - 1) % kStages) * kStage + kHalfTile;
+        u32x4 ring[kAhead + 1];
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) ring[j] = read_v(vl, j);
+        static_for<0, 16>([&](auto uc) PKV_INLINE {
+          constexpr int u = decltype(uc)::value;
+          if constexpr (u + kAhead < 16) ring[(u + kAhead) % (kAhead + 1)] = read_v(vl, u + kAhead);
+          oacc[u & 3] = mfma32(ring[u % (kAhead + 1)], pf[u >> 2], oacc[u & 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      // S^T = K Q^T for the two 32-key halves of the tile (also run on the
+      // last entry, t = n, where it reads a stale slot and is never used).
+      const char* kl = lds + (t % kStages) * kStage;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+      u32x4 ring[kAhead + 1];
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const u32x4 kf = *(const u32x4*)(kl + tile_off(kt * 32 + lrow, 2 * ks + half));
-          sacc[kt] = mfma32(kf, qf[ks], sacc[kt]);
-        }
+      for (int j = 0; j < kAhead; ++j) ring[j] = read_k(kl, j);
+      static_for<0, 16>([&](auto uc) PKV_INLINE {
+        constexpr int q = decltype(uc)::value;
+        if constexpr (q + kAhead < 16) ring[(q + kAhead) % (kAhead + 1)] = read_k(kl, q + kAhead);
+        sacc[q & 1] = mfma32(ring[q % (kAhead + 1)], qf[q >> 1], sacc[q & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      __builtin_amdgcn_s_setprio(0);
+    };
 
+    auto vec_phase = [&](int t) PKV_INLINE {
+      const int kv0 = t * kPfKeys;
       // Causal mask only on tiles that reach past the first row's position,
       // then the online softmax on raw dots: p = exp2(dot*|scale|*log2 e - ref).
       if (kv0 + kPfKeys - 1 > c + row0) {
@@ -289,10 +371,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
           psum += p;
         }
       l_run += psum;
-
       // P^T operands: k-step ks covers keys 16*ks + 8*(j/4) + 4*half + j%4,
       // j = 0..7, i.e. S^T values 8*(ks & 1) .. +7 of half ks >> 1.
-      u32x4 pf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kt = ks >> 1, i0 = 8 * (ks & 1);
@@ -301,42 +381,43 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
                        pack_bf16(sacc[kt][i0 + 4], sacc[kt][i0 + 5]),
                        pack_bf16(sacc[kt][i0 + 6], sacc[kt][i0 + 7])};
       }
-      // O^T += V^T P^T; the V^T operand of lane l (head_dim dt*32 + l%32,
-      // keys 16*ks + 8*jj + 4*half + 0..3 for jj = 0, 1) comes from two
-      // transposed reads whose source lanes point at those keys' rows.
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt) {
-          const int d0 = dt * 32 + tdb;
-          i16x4 t0, t1;
-          {
-            const int key = 16 * ks + 4 * half + (ts >> 2);
-            t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vl + tile_off(key, d0 >> 3) + (d0 & 7) * 2));
-            t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vl + tile_off(key + 8, d0 >> 3) + (d0 & 7) * 2));
-          }
-          const u32x2 v0 = __builtin_bit_cast(u32x2, t0), v1 = __builtin_bit_cast(u32x2, t1);
-          oacc[dt] = mfma32(u32x4{v0.x, v0.y, v1.x, v1.y}, pf[ks], oacc[dt]);
-        }
     };
 
-    // Pipeline: tiles t+1 .. t+3 are in flight while tile t is computed.
+    // Slot s starts with every wave waiting for its copies of tile s/2 (even
+    // s), the barrier, and the copies of tile s/2 + 2.  The two groups run
+    // their sequences in loops of their own, so each loop carries only the
+    // state its next phase needs (P^T into group 0's MFMA phase, S^T into
+    // group 1's softmax); both loops pass the same barriers.
+    auto sync_slot = [&](int s) PKV_INLINE {
+      const int u = s >> 1;
+      if ((s & 1) == 0 && u < ntiles) {  // this wave's copies of tile u have landed
+        if (u + 1 < ntiles)
+          wait_vmem<4>();
+        else
+          wait_vmem<0>();
+      }
+      // nothing moves across the barrier: a phase's work stays in its slot
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();  // ... for every wave; slot s-1 is done everywhere
+      __builtin_amdgcn_sched_barrier(0);
+      if ((s & 1) == 0 && u + 2 < ntiles) issue_tile(u + 2);
+    };
     issue_tile(0);
     if (ntiles > 1) issue_tile(1);
-    if (ntiles > 2) issue_tile(2);
-    for (int tile = 0; tile < ntiles; ++tile) {
-      // this wave's loads of `tile` have landed (younger tiles may still fly)
-      if (tile + 2 < ntiles)
-        wait_vmem<8>();
-      else if (tile + 1 < ntiles)
-        wait_vmem<4>();
-      else
-        wait_vmem<0>();
-      __builtin_amdgcn_s_barrier();  // all waves: tile complete, tile-1 consumed
-      compute_tile(tile);
-      if (tile + 3 < ntiles) issue_tile(tile + 3);  // into the slot of tile - 1
+    if (grp == 0) {
+      for (int t = 0; t <= ntiles; ++t) {
+        sync_slot(2 * t);
+        mfma_phase(t);
+        sync_slot(2 * t + 1);
+        if (t < ntiles) vec_phase(t);
+      }
+    } else {
+      for (int t = 0; t <= ntiles; ++t) {
+        sync_slot(2 * t);
+        if (t >= 1) vec_phase(t - 1);
+        sync_slot(2 * t + 1);
+        mfma_phase(t);
+      }
     }
 
     if (bad) tile_bad = 1;
