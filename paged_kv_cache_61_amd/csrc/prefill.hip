@@ -20,7 +20,8 @@
 //   S^T = K Q^T      (v_mfma_f32_32x32x16_bf16: A = K from LDS, B = Q from
 //                     registers), so lane l holds the scores of row l % 32;
 //   online softmax   per lane: the row max needs one exchange with lane l^32
-//                     (the other 32 keys of the tile); exp2 with scale*log2 e
+//                     (the other 32 keys of the tile; v_permlane32_swap, no
+//                     LDS round trip); exp2 with scale*log2 e
 //                     folded in; rescaling skipped when no row max moved;
 //   O^T += V^T P^T   (A = V^T from LDS, B = P from the S^T registers packed
 //                     to bf16), so O's rows are again lane-local.
@@ -31,12 +32,15 @@
 // rows before the chunk's last key, so later rows read as zeros and tail
 // garbage or NaN in the cache never reaches the output.  Rows are stored as
 // they are in the cache (256 bytes for head_dim 128) with 16-byte chunk c of
-// row r at position c ^ swz(r mod 16), swz = rotate left by one bit in 4
-// bits: swz is a permutation (the K operand reads of 16 consecutive keys hit
-// 16 distinct positions) that keeps bits 1-3 distinct within each aligned
-// group of 4 rows (a transposed V read, 4 rows x 2 adjacent chunks per 16
-// lanes, hits 8 distinct positions), so neither read conflicts on banks.
-// (A plain c ^ (r mod 16) makes the transposed reads conflict two ways.)  The
+// row r at position c ^ swz(r mod 16), swz = the two 2-bit halves of r
+// swapped.  The LDS serves 256 bytes (all 64 banks) per clock: 16 lanes of a
+// 16-byte read or 32 lanes of an 8-byte one.  swz is a permutation, so the K
+// operand reads (16 consecutive keys, one chunk) hit 16 distinct positions;
+// and its upper two bits differ within each aligned group of 4 rows, so a
+// transposed V read (32 lanes: 4 rows x 4 adjacent chunks of an aligned
+// group of 4) also hits 16 distinct positions.  Neither read conflicts on
+// banks.  (A swizzle that only keeps 16-lane halves apart, or a plain
+// c ^ (r mod 16), makes the transposed reads conflict two or four ways.)  The
 // V^T operand of the second product comes from ds_read_b64_tr_b16 (two 4-key
 // transposed reads per lane), in the key order of the S^T accumulator
 // (8*(i/4) + 4*(l/32) + i%4).
@@ -95,6 +99,15 @@ PKV_DEV uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// max(x[l], x[l ^ 32]) for every lane l.  v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second (a VALU
+// op, no LDS round trip): with x in both, one result holds each lane's own
+// value and the other its partner's.
+PKV_DEV float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // A row's reference max moves only when a tile's max exceeds it by more than
 // this (log2 units); p = exp2(s - ref) stays <= 2^8 and O is rescaled rarely.
 constexpr float kRefSlack = 8.f;
@@ -103,7 +116,7 @@ constexpr float kRefSlack = 8.f;
 // Chunk-position permutation of row r (mod 16): rotate left by one bit in 4
 // bits, so both the K operand reads and the transposed V reads are free of
 // bank conflicts.
-PKV_DEV int swz(int r) { return ((r << 1) | (r >> 3)) & 15; }
+PKV_DEV int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 PKV_DEV int tile_off(int row, int c) { return row * kRowB + ((c ^ swz(row & 15)) << 4); }
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -114,14 +127,42 @@ PKV_DEV void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// buffer_load_dwordx4 ... lds: each lane copies 16 bytes at `voff` inside the
-// buffer described by `rs` (zeros past its end) to LDS address
-// M0 + 16 * lane.  Issued as inline asm so the compiler does not order its
-// own LDS reads behind these loads; completion is awaited explicitly with
-// wait_vmem before the barrier that publishes a tile.
-PKV_DEV void dma_row16(const u32x4& rs, uint32_t voff, const void* lds_dst) {
-  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)PKV_LDS(lds_dst));
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0v) : "memory");
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for this wave's global stores to complete.
+PKV_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One cache block into LDS: four buffer_load_dwordx4 ... lds, instruction j
+// copying 16 bytes per lane at voff[j] inside the buffer described by `rs`
+// (zeros past its end) to LDS byte offset m0v + 1024 j + 16 * lane (m0v
+// wave-uniform).  Inline asm, so the compiler does not order its own LDS
+// reads behind these loads (completion is awaited explicitly with wait_vmem
+// before the barrier that publishes a tile).  The compiler does not insert
+// hazard waits inside inline asm, so the asm carries its own: the descriptor
+// words may have been written by VALU instructions (readfirstlane), which a
+// vector memory instruction may read only five wait states later, and an
+// M0 write needs one wait state before an LDS-DMA instruction uses it.
+PKV_DEV void dma_block(const u32x4& rs, const uint32_t (&voff)[4], uint32_t m0v) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
+      "s_add_u32 m0, %5, 0x400\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %4, 0 offen lds\n\t"
+      "s_add_u32 m0, %5, 0x800\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+      "s_add_u32 m0, %5, 0xc00\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %4, 0 offen lds"
+      :
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs), "s"(m0v)
+      : "memory", "m0", "scc");
 }
 
 // Descriptor words for raw (stride 0) buffer access to [base, base + bytes).
@@ -175,13 +216,29 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // the current tile runs.
   const int n_entries = a.hdr[kHdrPrefillItems];
   const int g = blockIdx.x % Hkv;
+
+  // Copy geometry, the same for every tile: instruction j, lane L of this
+  // wave's block copy carries token row 4j + L/16 of the block and the chunk
+  // that lands at LDS position L mod 16 (chunk (L mod 16) ^ swz(row)); the
+  // destination is this wave's quarter of a ring slot's K or V half.
+  uint32_t voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rb = 4 * j + (lane >> 4);
+    voff[j] = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ swz(rb)) << 4);
+  }
+  const uint32_t ldst = (uint32_t)(uintptr_t)PKV_LDS(lds) + (uint32_t)ldst_half;
+  const uint32_t blk_bytes32 = (uint32_t)blk_bytes;
   int* queue = a.hdr + kHdrPrefillQueue + g;
   __shared__ int next_item[2];
   if (tid == 0) next_item[0] = atomicAdd(queue, 1);
   __syncthreads();
   int e = next_item[0];
   for (int par = 1; e < n_entries; par ^= 1) {
-    if (tid == 0) next_item[par] = atomicAdd(queue, 1);
+    // (thread 0 publishes the next index after the q loads below, so the
+    // atomic's round trip overlaps them)
+    int nxt = 0;
+    if (tid == 0) nxt = atomicAdd(queue, 1);
     const int4 item = items[e];
     const int r = item.x, row0 = item.y, nrows = item.z;
     const int c = nct[r];
@@ -189,6 +246,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     const int kv_end = c + row0 + nrows;               // keys 0 .. kv_end-1 are read
     const int ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
     const int32_t* bt = block_table + (size_t)r * a.max_blocks_per_req;
+    // This wave's block ids for tiles 0..127 (tile l in lane l of ids0, tile
+    // 64 + l in ids1), read once per item so that issuing a tile's copies
+    // never waits for a table read.  Block 4*tile + cblk is read only when
+    // it holds keys before kv_end, as in issue_tile.
+    const int kb0 = (kPfKeys / kBlock) * lane + cblk;
+    const int kb1 = kb0 + 64 * (kPfKeys / kBlock);
+    int ids0 = kBlock * kb0 < kv_end ? bt[kb0] : 0;
+    int ids1 = kBlock * kb1 < kv_end ? bt[kb1] : 0;
 
     // this lane's row
     const int rho = w * 32 + lrow;
@@ -209,35 +274,41 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     for (int ks = 0; ks < kKSteps; ++ks)
       qf[ks] = (*(const u32x4*)((const uint16_t*)a.q + qrow + ks * 16 + 8 * half) ^ qsign) & qmask;
     wait_vmem<0>();  // q is in registers before the tile stream starts counting
+    if (tid == 0) next_item[par] = nxt;
 
     if (tid == 0) tile_bad = 0;
-    bool bad = false;
+    // Ids outside the pool are reported once per item and replaced by block
+    // 0, so the tile stream never copies from outside the cache.
+    const bool bad0 = ids0 < 0 || ids0 >= a.num_blocks, bad1 = ids1 < 0 || ids1 >= a.num_blocks;
+    bool bad = __any(bad0 || bad1);
+    ids0 = bad0 ? 0 : ids0;
+    ids1 = bad1 ? 0 : ids1;
 
     // Stream tile `tile` into ring slot tile % kStages: this wave's block,
     // 4 instructions of 4 token rows; lane L of instruction j carries chunk
     // (L & 15) ^ row of token row 4j + L/16, so LDS holds the swizzled layout.
+    // Straight-line: the id comes from a lane of ids0 / ids1 (blocks past
+    // kv_end hold id 0 and get a zero-length buffer, which reads as zeros).
     auto issue_tile = [&](int tile) PKV_INLINE {
-      const int kv0 = tile * kPfKeys;
-      const int nvalid = kv_end - (kv0 + kBlock * cblk);  // rows of this block before kv_end
-      const char* src = cbase;
-      uint32_t nbytes = 0;
-      if (nvalid > 0) {
-        int phys = bt[kv0 / kBlock + cblk];
-        if (phys < 0 || phys >= a.num_blocks) {
+      const int nvalid = kv_end - (tile * kPfKeys + kBlock * cblk);  // rows of this block before kv_end
+      const uint32_t nbytes = (uint32_t)min(max(nvalid, 0), kBlock) * (uint32_t)row_bytes;
+      uint32_t phys;
+      if (tile < 128) {
+        const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(ids0, tile & 63);
+        const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane(ids1, tile & 63);
+        phys = tile < 64 ? p0 : p1;
+      } else {  // items longer than 8192 keys: the table is read here
+        int p = nvalid > 0 ? bt[tile * (kPfKeys / kBlock) + cblk] : 0;
+        if (p < 0 || p >= a.num_blocks) {
           bad = true;
-          phys = 0;
+          p = 0;
         }
-        src = cbase + (size_t)phys * blk_bytes;
-        nbytes = (uint32_t)min(nvalid, kBlock) * (uint32_t)row_bytes;
+        phys = (uint32_t)p;
       }
-      const u32x4 rs = buffer_desc(src, nbytes);
-      const char* dst = lds + (tile % kStages) * kStage + ldst_half;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rb = 4 * j + (lane >> 4);                     // token row in the block
-        const uint32_t voff = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ swz(rb)) << 4);
-        dma_row16(rs, voff, dst + j * 4 * kRowB);
-      }
+      const u32x4 rs = buffer_desc(cbase + (uint64_t)phys * blk_bytes32, nbytes);
+      const uint32_t m0 = ldst + (uint32_t)(tile & (kStages - 1)) * kStage;
+      static_assert(4 * kRowB == 0x400, "dma_block steps M0 by 1 KiB (4 token rows)");
+      dma_block(rs, voff, m0);
     };
 
     f32x16 oacc[kDTiles];
@@ -256,9 +327,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     // Workgroup barriers cut time into slots; in slot s group 0 runs entry s
     // and group 1 entry s-1 of mfma(0), vec(0), mfma(1), vec(1), ..., mfma(n),
     // so on every SIMD one wave issues MFMAs while the other runs its
-    // softmax.  Tile u must be in LDS from slot 2u on: its copies are issued
-    // at slot 2u-4 (two tiles ahead) into ring slot u % 4, whose previous
-    // tile u-4 was last read in slot 2u-5.
+    // softmax.  Tile u must be in LDS from slot 2u on: every wave issues its
+    // copies of it in slot 2u-4 (two tiles ahead), after its phase there (so
+    // the copies never delay an MFMA phase's start), into ring slot u % 4,
+    // whose previous tile u-4 was last read in slot 2u-5.
     const int grp = w >> 2;
     f32x16 sacc[2];   // S^T(t) from its MFMA phase to its softmax
     u32x4 pf[4];      // P^T(t) from its softmax to its PV
@@ -349,7 +421,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kt][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * csc;
+      tmax = pair_max(tmax) * csc;
       if (__any(tmax > m_run + kRefSlack)) {  // move the reference max (rare)
         const float m_new = fmaxf(m_run, tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -384,13 +456,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     };
 
     // Slot s starts with every wave waiting for its copies of tile s/2 (even
-    // s), the barrier, and the copies of tile s/2 + 2.  The two groups run
+    // s) and the barrier.  The two groups run
     // their sequences in loops of their own, so each loop carries only the
     // state its next phase needs (P^T into group 0's MFMA phase, S^T into
     // group 1's softmax); both loops pass the same barriers.
     auto sync_slot = [&](int s) PKV_INLINE {
       const int u = s >> 1;
-      if ((s & 1) == 0 && u < ntiles) {  // this wave's copies of tile u have landed
+      if ((s & 1) == 0) {  // this wave's copies of tile u have landed
         if (u + 1 < ntiles)
           wait_vmem<4>();
         else
@@ -400,7 +472,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();  // ... for every wave; slot s-1 is done everywhere
       __builtin_amdgcn_sched_barrier(0);
-      if ((s & 1) == 0 && u + 2 < ntiles) issue_tile(u + 2);
     };
     issue_tile(0);
     if (ntiles > 1) issue_tile(1);
@@ -408,6 +479,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       for (int t = 0; t <= ntiles; ++t) {
         sync_slot(2 * t);
         mfma_phase(t);
+        if (t + 2 < ntiles) issue_tile(t + 2);
         sync_slot(2 * t + 1);
         if (t < ntiles) vec_phase(t);
       }
@@ -415,13 +487,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       for (int t = 0; t <= ntiles; ++t) {
         sync_slot(2 * t);
         if (t >= 1) vec_phase(t - 1);
+        if (t + 2 < ntiles) issue_tile(t + 2);
         sync_slot(2 * t + 1);
         mfma_phase(t);
       }
     }
 
     if (bad) tile_bad = 1;
-    __syncthreads();
+    lds_barrier();
     const bool any_bad = tile_bad != 0;
     if (any_bad && tid == 0) atomicOr(a.err, PKV_DEVERR_BLOCK_ID);
 
@@ -441,7 +514,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
                                       pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv)};
         }
     }
-    __syncthreads();  // the ring is reused by the next item
+    lds_barrier();  // the ring is reused by the next item (the stores need not land first)
     e = next_item[par];
   }
 }
