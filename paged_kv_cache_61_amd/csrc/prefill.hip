@@ -108,6 +108,12 @@ PKV_DEV float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// x[l] + x[l ^ 32] for every lane l (v_permlane32_swap, as in pair_max).
+PKV_DEV float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // A row's reference max moves only when a tile's max exceeds it by more than
 // this (log2 units); p = exp2(s - ref) stays <= 2^8 and O is rescaled rarely.
 constexpr float kRefSlack = 8.f;
@@ -143,26 +149,27 @@ PKV_DEV void lds_barrier() {
 // before the barrier that publishes a tile).  The compiler does not insert
 // hazard waits inside inline asm, so the asm carries its own: the descriptor
 // words may have been written by VALU instructions (readfirstlane), which a
-// vector memory instruction may read only five wait states later, and an
-// M0 write needs one wait state before an LDS-DMA instruction uses it.
+// vector memory instruction may read only five wait states later (the leading
+// s_nop 4, which also covers the compiler's M0 write), and an M0 write needs
+// one wait state before an LDS-DMA instruction uses it.
 PKV_DEV void dma_block(const u32x4& rs, const uint32_t (&voff)[4], uint32_t m0v) {
+  // M0 is an in/out operand: the compiler loads it before the asm and knows
+  // the asm leaves it stepped by 3 KiB.
   asm volatile(
       "s_nop 4\n\t"
-      "s_mov_b32 m0, %5\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
-      "s_add_u32 m0, %5, 0x400\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %4, 0 offen lds\n\t"
-      "s_add_u32 m0, %5, 0x800\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
-      "s_add_u32 m0, %5, 0xc00\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %3, %4, 0 offen lds"
-      :
-      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs), "s"(m0v)
-      : "memory", "m0", "scc");
+      "buffer_load_dwordx4 %4, %5, 0 offen lds"
+      : "+{m0}"(m0v)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs)
+      : "memory", "scc");
 }
 
 // Descriptor words for raw (stride 0) buffer access to [base, base + bytes).
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     PrefillParams a, const int4* __restrict__ items, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ nct, const int32_t* __restrict__ block_table) {
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
-  __shared__ int tile_bad;
+  __shared__ int tile_bad[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -233,83 +240,96 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   __shared__ int next_item[2];
   if (tid == 0) next_item[0] = atomicAdd(queue, 1);
   __syncthreads();
-  int e = next_item[0];
-  for (int par = 1; e < n_entries; par ^= 1) {
-    // (thread 0 publishes the next index after the q loads below, so the
-    // atomic's round trip overlaps them)
-    int nxt = 0;
+
+  // State of the item being run, set by begin_item.
+  int r = 0, row0 = 0, nrows = 0, c = 0, qs = 0, kv_end = 0, ntiles = 0, pos_abs = 0, nxt = 0;
+  const int32_t* bt = block_table;
+  int ids0 = 0, ids1 = 0;   // block ids, see begin_item
+  bool bad = false, row_ok = false;
+  size_t qrow = 0;
+  u32x4 qf[kKSteps];
+  const int rho = w * 32 + lrow;  // this lane's MFMA row inside a tile
+  // With a negative scale, q's sign is flipped (exact in bf16) and |scale|
+  // used, so the row max of the raw dots is the max of the scaled scores.
+  const uint32_t qsign = sl2 < 0.f ? 0x80008000u : 0u;
+
+  // Stream tile `tile` into ring slot tile % kStages: this wave's block,
+  // 4 instructions of 4 token rows; lane L of instruction j carries chunk
+  // (L & 15) ^ row of token row 4j + L/16, so LDS holds the swizzled layout.
+  // Straight-line: the id comes from a lane of ids0 / ids1 (blocks past
+  // kv_end hold id 0 and get a zero-length buffer, which reads as zeros).
+  auto issue_tile = [&](int tile) PKV_INLINE {
+    const int nvalid = kv_end - (tile * kPfKeys + kBlock * cblk);  // rows of this block before kv_end
+    const uint32_t nbytes = (uint32_t)min(max(nvalid, 0), kBlock) * (uint32_t)row_bytes;
+    uint32_t phys;
+    if (tile < 128) {
+      const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(ids0, tile & 63);
+      const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane(ids1, tile & 63);
+      phys = tile < 64 ? p0 : p1;
+    } else {  // items longer than 8192 keys: the table is read here
+      int p = nvalid > 0 ? bt[tile * (kPfKeys / kBlock) + cblk] : 0;
+      if (p < 0 || p >= a.num_blocks) {
+        bad = true;
+        p = 0;
+      }
+      phys = (uint32_t)p;
+    }
+    const u32x4 rs = buffer_desc(cbase + (uint64_t)phys * blk_bytes32, nbytes);
+    const uint32_t m0 = ldst + (uint32_t)(tile & (kStages - 1)) * kStage;
+    static_assert(4 * kRowB == 0x400, "dma_block steps M0 by 1 KiB (4 token rows)");
+    dma_block(rs, voff, m0);
+  };
+
+  // Start item ee: thread 0 takes the next queue index (published when this
+  // item starts running), then the descriptor, this wave's block ids for
+  // tiles 0..127 (tile l in lane l of ids0, tile 64 + l in ids1; block
+  // 4*tile + cblk is read only when it holds keys before kv_end; ids outside
+  // the pool are reported once per item and replaced by block 0, so the tile
+  // stream never copies from outside the cache), the q rows (loads left in
+  // flight) and the copies of the first two tiles.  For every item but the
+  // first this runs right after the previous item's tile loop, so these
+  // latencies overlap that item's epilogue.
+  auto begin_item = [&](int ee) PKV_INLINE {
     if (tid == 0) nxt = atomicAdd(queue, 1);
-    const int4 item = items[e];
-    const int r = item.x, row0 = item.y, nrows = item.z;
-    const int c = nct[r];
-    const int qs = qsl[r];
-    const int kv_end = c + row0 + nrows;               // keys 0 .. kv_end-1 are read
-    const int ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
-    const int32_t* bt = block_table + (size_t)r * a.max_blocks_per_req;
-    // This wave's block ids for tiles 0..127 (tile l in lane l of ids0, tile
-    // 64 + l in ids1), read once per item so that issuing a tile's copies
-    // never waits for a table read.  Block 4*tile + cblk is read only when
-    // it holds keys before kv_end, as in issue_tile.
+    const int4 item = items[ee];
+    r = item.x;
+    row0 = item.y;
+    nrows = item.z;
+    c = nct[r];
+    qs = qsl[r];
+    kv_end = c + row0 + nrows;  // keys 0 .. kv_end-1 are read
+    ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
+    bt = block_table + (size_t)r * a.max_blocks_per_req;
     const int kb0 = (kPfKeys / kBlock) * lane + cblk;
     const int kb1 = kb0 + 64 * (kPfKeys / kBlock);
-    int ids0 = kBlock * kb0 < kv_end ? bt[kb0] : 0;
-    int ids1 = kBlock * kb1 < kv_end ? bt[kb1] : 0;
-
-    // this lane's row
-    const int rho = w * 32 + lrow;
+    int i0 = kBlock * kb0 < kv_end ? bt[kb0] : 0;
+    int i1 = kBlock * kb1 < kv_end ? bt[kb1] : 0;
     int pos = rho / G;
     const int head = rho - pos * G;
-    const bool row_ok = rho < BQ * G && pos < nrows;
-    if (!row_ok) pos = nrows - 1;                       // padding rows: any visible row
-    const int pos_abs = c + row0 + pos;
-    const size_t qrow = ((size_t)(qs + row0 + pos) * a.num_q_heads + g * G + head) * kD;
-
-    // With a negative scale, q's sign is flipped (exact in bf16) and |scale|
-    // used, so the row max of the raw dots is the max of the scaled scores.
-    const uint32_t qsign = sl2 < 0.f ? 0x80008000u : 0u;
-    // (padding rows load a valid row and zero it)
+    row_ok = rho < BQ * G && pos < nrows;
+    if (!row_ok) pos = nrows - 1;  // padding rows: any visible row, loaded and zeroed
+    pos_abs = c + row0 + pos;
+    qrow = ((size_t)(qs + row0 + pos) * a.num_q_heads + g * G + head) * kD;
     const uint32_t qmask = row_ok ? 0xffffffffu : 0u;
-    u32x4 qf[kKSteps];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
       qf[ks] = (*(const u32x4*)((const uint16_t*)a.q + qrow + ks * 16 + 8 * half) ^ qsign) & qmask;
-    wait_vmem<0>();  // q is in registers before the tile stream starts counting
-    if (tid == 0) next_item[par] = nxt;
+    const bool bad0 = i0 < 0 || i0 >= a.num_blocks, bad1 = i1 < 0 || i1 >= a.num_blocks;
+    bad = __any(bad0 || bad1);
+    ids0 = bad0 ? 0 : i0;
+    ids1 = bad1 ? 0 : i1;
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+  };
 
-    if (tid == 0) tile_bad = 0;
-    // Ids outside the pool are reported once per item and replaced by block
-    // 0, so the tile stream never copies from outside the cache.
-    const bool bad0 = ids0 < 0 || ids0 >= a.num_blocks, bad1 = ids1 < 0 || ids1 >= a.num_blocks;
-    bool bad = __any(bad0 || bad1);
-    ids0 = bad0 ? 0 : ids0;
-    ids1 = bad1 ? 0 : ids1;
-
-    // Stream tile `tile` into ring slot tile % kStages: this wave's block,
-    // 4 instructions of 4 token rows; lane L of instruction j carries chunk
-    // (L & 15) ^ row of token row 4j + L/16, so LDS holds the swizzled layout.
-    // Straight-line: the id comes from a lane of ids0 / ids1 (blocks past
-    // kv_end hold id 0 and get a zero-length buffer, which reads as zeros).
-    auto issue_tile = [&](int tile) PKV_INLINE {
-      const int nvalid = kv_end - (tile * kPfKeys + kBlock * cblk);  // rows of this block before kv_end
-      const uint32_t nbytes = (uint32_t)min(max(nvalid, 0), kBlock) * (uint32_t)row_bytes;
-      uint32_t phys;
-      if (tile < 128) {
-        const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(ids0, tile & 63);
-        const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane(ids1, tile & 63);
-        phys = tile < 64 ? p0 : p1;
-      } else {  // items longer than 8192 keys: the table is read here
-        int p = nvalid > 0 ? bt[tile * (kPfKeys / kBlock) + cblk] : 0;
-        if (p < 0 || p >= a.num_blocks) {
-          bad = true;
-          p = 0;
-        }
-        phys = (uint32_t)p;
-      }
-      const u32x4 rs = buffer_desc(cbase + (uint64_t)phys * blk_bytes32, nbytes);
-      const uint32_t m0 = ldst + (uint32_t)(tile & (kStages - 1)) * kStage;
-      static_assert(4 * kRowB == 0x400, "dma_block steps M0 by 1 KiB (4 token rows)");
-      dma_block(rs, voff, m0);
-    };
+  int e = next_item[0];
+  if (e < n_entries) begin_item(e);
+  for (int par = 1; e < n_entries; par ^= 1) {
+    wait_vmem<0>();  // q and the first two tiles are in (and earlier stores done)
+    if (tid == 0) {
+      next_item[par] = nxt;
+      tile_bad[par] = 0;
+    }
 
     f32x16 oacc[kDTiles];
 #pragma unroll
@@ -473,8 +493,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       __builtin_amdgcn_s_barrier();  // ... for every wave; slot s-1 is done everywhere
       __builtin_amdgcn_sched_barrier(0);
     };
-    issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
     if (grp == 0) {
       for (int t = 0; t <= ntiles; ++t) {
         sync_slot(2 * t);
@@ -493,29 +511,37 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       }
     }
 
-    if (bad) tile_bad = 1;
-    lds_barrier();
-    const bool any_bad = tile_bad != 0;
+    if (bad) tile_bad[par] = 1;
+    lds_barrier();  // every wave is done with the ring; tile_bad and next_item are visible
+    const bool any_bad = tile_bad[par] != 0;
     if (any_bad && tid == 0) atomicOr(a.err, PKV_DEVERR_BLOCK_ID);
+    const float inv = any_bad ? __builtin_nanf("") : 1.f / pair_sum(l_run);
+    const size_t qrow_done = qrow;
+    const bool row_ok_done = row_ok;
+    e = next_item[par];
+    if (e < n_entries) begin_item(e);
 
     // Normalise and store: lane holds row lrow, head_dim elements
-    // dt*32 + 8*(i/4) + 4*half + i%4.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = any_bad ? __builtin_nanf("") : 1.f / l_tot;
-    if (row_ok) {
-      uint16_t* orow = (uint16_t*)a.out + qrow;
+    // dt*32 + 8*q4 + 4*half + 0..3 (q4 = 0..3).  For each pair q4 = 2p, 2p+1
+    // the two halves of the wave swap one group (v_permlane32_swap), so a
+    // lane of the lower half holds dims 8*(2p) + 0..7 and a lane of the upper
+    // half dims 8*(2p+1) + 0..7 of its row: one 16-byte store each.
+    // (tile_bad[par] is cleared again only two items later, after barriers
+    // every wave has passed.)
+    uint16_t* orow = (uint16_t*)a.out + qrow_done;
 #pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt)
+    for (int dt = 0; dt < kDTiles; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = dt * 32 + 8 * q4 + 4 * half;
-          const f32x16& o = oacc[dt];
-          *(u32x2*)(orow + d) = u32x2{pack_bf16(o[4 * q4 + 0] * inv, o[4 * q4 + 1] * inv),
-                                      pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv)};
-        }
-    }
-    lds_barrier();  // the ring is reused by the next item (the stores need not land first)
-    e = next_item[par];
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const f32x16& o = oacc[dt];
+        const int i0 = 8 * p2, i1 = 8 * p2 + 4;   // q4 = 2p2 and 2p2 + 1
+        const uint32_t a0 = pack_bf16(o[i0 + 0] * inv, o[i0 + 1] * inv), a1 = pack_bf16(o[i0 + 2] * inv, o[i0 + 3] * inv);
+        const uint32_t b0 = pack_bf16(o[i1 + 0] * inv, o[i1 + 1] * inv), b1 = pack_bf16(o[i1 + 2] * inv, o[i1 + 3] * inv);
+        const auto x = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        const int d = dt * 32 + 8 * (2 * p2 + half);
+        if (row_ok_done) *(u32x4*)(orow + d) = u32x4{x[0], y[0], x[1], y[1]};
+      }
   }
 }
 
