@@ -46,8 +46,8 @@
 // (8*(i/4) + 4*(l/32) + i%4).
 // The two waves on each SIMD alternate ("ping-pong"): while one issues the
 // MFMAs of a tile (PV of the previous tile, QK of this one) the other runs
-// its softmax; workgroup barriers between the phases keep the two groups
-// half a tile apart (see the slot schedule in the kernel).
+// its softmax; one workgroup barrier per tile starts the two groups half a
+// tile apart (see the schedule in the kernel).
 // Causal masks are applied only on tiles that cross a row's position.
 #include <math.h>
 
@@ -344,13 +344,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     // and a VALU phase,
     //   vec(t):  causal mask, online softmax of S(t) -> P(t) (and the rare O
     //            rescale, after PV(t-1) and before PV(t)).
-    // Workgroup barriers cut time into slots; in slot s group 0 runs entry s
-    // and group 1 entry s-1 of mfma(0), vec(0), mfma(1), vec(1), ..., mfma(n),
-    // so on every SIMD one wave issues MFMAs while the other runs its
-    // softmax.  Tile u must be in LDS from slot 2u on: every wave issues its
-    // copies of it in slot 2u-4 (two tiles ahead), after its phase there (so
-    // the copies never delay an MFMA phase's start), into ring slot u % 4,
-    // whose previous tile u-4 was last read in slot 2u-5.
+    // A workgroup barrier starts every tile period; in period t group 0 runs
+    // mfma(t) then vec(t), group 1 vec(t-1) then mfma(t), so on every SIMD one
+    // wave starts the period with its MFMAs while the other runs its softmax.
+    // Inside a period the two waves are not synchronised again (a barrier
+    // between the phases costs more than the alternation it enforces).  Tile
+    // u must be in LDS from period u on: every wave issues its copies of it in
+    // period u-2, after its first phase there (so the copies never delay the
+    // start of an MFMA phase), into ring slot u % 4, whose previous tile u-4
+    // was last read in period u-3 (PV(u-4) in mfma(u-3)).
     const int grp = w >> 2;
     f32x16 sacc[2];   // S^T(t) from its MFMA phase to its softmax
     u32x4 pf[4];      // P^T(t) from its softmax to its PV
@@ -475,38 +477,35 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       }
     };
 
-    // Slot s starts with every wave waiting for its copies of tile s/2 (even
-    // s) and the barrier.  The two groups run
-    // their sequences in loops of their own, so each loop carries only the
-    // state its next phase needs (P^T into group 0's MFMA phase, S^T into
-    // group 1's softmax); both loops pass the same barriers.
-    auto sync_slot = [&](int s) PKV_INLINE {
-      const int u = s >> 1;
-      if ((s & 1) == 0) {  // this wave's copies of tile u have landed
-        if (u + 1 < ntiles)
-          wait_vmem<4>();
-        else
-          wait_vmem<0>();
-      }
-      // nothing moves across the barrier: a phase's work stays in its slot
+    // Period t starts with every wave waiting for its own copies of tile t
+    // and the barrier: after it tile t is complete in LDS for every wave, and
+    // every wave has left period t-1.  The two groups run their sequences in
+    // loops of their own, so each loop carries only the state its next phase
+    // needs (P^T into group 0's MFMA phase, S^T into group 1's softmax).
+    auto tile_barrier = [&](int t) PKV_INLINE {
+      if (t + 1 < ntiles)
+        wait_vmem<4>();
+      else
+        wait_vmem<0>();
+      // nothing moves across the barrier or a phase boundary
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();  // ... for every wave; slot s-1 is done everywhere
+      __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
     if (grp == 0) {
       for (int t = 0; t <= ntiles; ++t) {
-        sync_slot(2 * t);
+        tile_barrier(t);
         mfma_phase(t);
         if (t + 2 < ntiles) issue_tile(t + 2);
-        sync_slot(2 * t + 1);
+        __builtin_amdgcn_sched_barrier(0);
         if (t < ntiles) vec_phase(t);
       }
     } else {
       for (int t = 0; t <= ntiles; ++t) {
-        sync_slot(2 * t);
+        tile_barrier(t);
         if (t >= 1) vec_phase(t - 1);
         if (t + 2 < ntiles) issue_tile(t + 2);
-        sync_slot(2 * t + 1);
+        __builtin_amdgcn_sched_barrier(0);
         mfma_phase(t);
       }
     }
