@@ -129,13 +129,15 @@ PKV_DEV void store_out2(void* out, size_t idx, float x0, float x1) {
     *(float2*)((float*)out + idx) = make_float2(x0, x1);
 }
 
-// Lanes that share one token's q.k: 4 (each owns a quarter of head_dim), or
-// 8 for groups of 8 heads, which halves the q registers a lane holds.
+// Lanes that share one token's q.k: 4, each owning a quarter of head_dim.  A
+// wave holds 1, 2 or 4 query heads of a group (wider groups are split into
+// several waves of 4 heads by the host).
 template <int GM>
 struct Lanes {
-  static constexpr int kPerToken = GM == 8 ? 8 : 4;
-  static constexpr int kTokensPerPass = kWave / kPerToken;   // 16 or 8
-  static constexpr int kPasses = kBlock / kTokensPerPass;      // 1 or 2
+  static_assert(GM == 1 || GM == 2 || GM == 4, "a wave holds 1, 2 or 4 heads");
+  static constexpr int kPerToken = 4;
+  static constexpr int kTokensPerPass = kWave / kPerToken;   // 16
+  static constexpr int kPasses = kBlock / kTokensPerPass;      // 1
   static constexpr int kHeadsPerLane = GM > kPerToken ? GM / kPerToken : 1;
   // head held by lane quarter/eighth c in slot k after the reduce-scatter
   PKV_DEV static int head(int c, int k) {
@@ -158,24 +160,13 @@ PKV_DEV void reduce_scatter(const float (&x)[GM], float (&y)[Lanes<GM>::kHeadsPe
     const bool b = c & 1;
     const float v = (b ? x[1] : x[0]) + dpp_mov<kDppQuadSwap1>(b ? x[0] : x[1]);
     y[0] = v + dpp_mov<kDppQuadSwap2>(v);
-  } else if constexpr (GM == 4) {
+  } else {  // GM == 4
     const bool b0 = c & 1, b1 = (c >> 1) & 1;
     float x1[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       x1[j] = (b0 ? x[2 * j + 1] : x[2 * j]) + dpp_mov<kDppQuadSwap1>(b0 ? x[2 * j] : x[2 * j + 1]);
     y[0] = (b1 ? x1[1] : x1[0]) + dpp_mov<kDppQuadSwap2>(b1 ? x1[0] : x1[1]);
-  } else {  // GM == 8 over 8 lanes: bit 2 (half-row mirror), then bits 0 and 1
-    const bool b2 = (c >> 2) & 1, b0 = c & 1, b1 = (c >> 1) & 1;
-    float x1[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      x1[h] = (b2 ? x[h + 4] : x[h]) + dpp_mov<kDppRowHalfMirror>(b2 ? x[h] : x[h + 4]);
-    float x2[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      x2[j] = (b0 ? x1[2 * j + 1] : x1[2 * j]) + dpp_mov<kDppQuadSwap1>(b0 ? x1[2 * j] : x1[2 * j + 1]);
-    y[0] = (b1 ? x2[1] : x2[0]) + dpp_mov<kDppQuadSwap2>(b1 ? x2[0] : x2[1]);
   }
 }
 
@@ -665,11 +656,13 @@ int launch_rows_g(const RowParams& p, int64_t bound_waves, int cus, hipStream_t 
 
 template <bool BF16, int D>
 int launch_rows_d(const RowParams& p, int64_t bound_waves, int cus, hipStream_t s) {
+  // (wider groups arrive split into head_groups of kMaxGroupRegs heads)
+  static_assert(kMaxGroupRegs == 4, "instantiations below cover 1, 2 and 4 heads per wave");
   const int gm = p.head_groups > 1 ? kMaxGroupRegs : p.group;
   if (gm <= 1) return launch_rows_g<BF16, D, 1>(p, bound_waves, cus, s);
   if (gm <= 2) return launch_rows_g<BF16, D, 2>(p, bound_waves, cus, s);
   if (gm <= 4) return launch_rows_g<BF16, D, 4>(p, bound_waves, cus, s);
-  return launch_rows_g<BF16, D, 8>(p, bound_waves, cus, s);
+  return 1;
 }
 
 }  // namespace

@@ -99,7 +99,6 @@ constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;   // rotate right by 4 inside each row of 16 lanes
 constexpr int kDppRowRor8 = 0x128;
-constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i inside each group of 8
 
 template <int CTRL>
 PKV_DEV float dpp_mov(float x) {

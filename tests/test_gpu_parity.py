@@ -45,9 +45,13 @@ def _full_step(wl, what):
 # ---------------------------------------------------------------------------
 # small ragged batches: decode rows, split-KV rows, prefill chunks
 
+# Every row-kernel instantiation (dtype x head_dim x heads per wave 1 / 2 / 4,
+# and groups wider than 4 split over several waves) meets at least one case.
 SMALL = [
     ("f32", 64, 8, 2), ("f32", 128, 4, 4), ("bf16", 64, 8, 2), ("bf16", 128, 4, 1),
     ("bf16", 128, 32, 8), ("bf16", 128, 12, 4), ("bf16", 64, 16, 1), ("f32", 64, 6, 2),
+    ("bf16", 64, 4, 4), ("bf16", 64, 8, 4), ("bf16", 128, 8, 4), ("f32", 64, 4, 4),
+    ("f32", 64, 4, 2), ("f32", 128, 8, 4), ("f32", 128, 8, 2), ("f32", 128, 16, 2),
 ]
 
 
