@@ -255,6 +255,28 @@ def test_prefill_group_sizes(Hq, Hkv):
     _full_step(wl, f"prefill G={Hq // Hkv}")
 
 
+def test_prefill_long_context_reads_table_per_tile():
+    # chunks whose keys run past 128 tiles of 64 (8192 keys): the prefill
+    # kernel reads those tiles' block ids from the table per tile instead of
+    # from the per-item registers
+    import paged_kv_cache_61_amd as pkv
+    reqs = [(9000, 70), (8150, 100), (8190, 2), (20, 1)]
+    wl = workloads.build(workloads.small_spec("long-prefill", 41, "bf16", 8, 2, 128, reqs))
+    s, good = _full_step(wl, "prefill past 8192 keys")
+    # a bad id in a tile past 128 of request 0 is reported and poisons only
+    # that request's rows
+    s3 = upload(wl)
+    run_write(s3)
+    bt = s3.block_table.clone()
+    bt[0, 4 * 130 + 1] = wl.num_blocks + 3
+    s3.block_table = bt
+    out = out_f64(run_attention(s3))
+    assert device_error(s3) & pkv.DEVERR_BLOCK_ID
+    assert np.isnan(out[0:70]).all()
+    ref = out_f64(s.out)
+    assert np.array_equal(out[70:], ref[70:])
+
+
 def test_prefill_chunk_split_and_decode_consistency():
     # one 300-token chunk on a 100-token prefix, the same tokens as two chunks,
     # and the last token as a decode: all agree with the oracle and each other
