@@ -70,7 +70,7 @@ constexpr int kD = 128;        // head_dim handled by this kernel
 constexpr int kRowB = kD * 2;               // bytes of one key row (one kv head)
 constexpr int kHalfTile = kPfKeys * kRowB;  // K or V part of a tile: 16 KiB
 constexpr int kStage = 2 * kHalfTile;       // one ring slot: K then V
-constexpr int kStages = 4;                  // tiles in flight: 3 ahead + the one computed
+constexpr int kStages = 4;                  // ring slots: tiles t-1 (PV), t (QK), t+1 and t+2 (in flight)
 constexpr int kKSteps = kD / 16;            // Q.K k-steps
 constexpr int kDTiles = kD / 32;            // O^T row tiles
 
@@ -118,12 +118,11 @@ PKV_DEV float pair_sum(float x) {
 // this (log2 units); p = exp2(s - ref) stays <= 2^8 and O is rescaled rarely.
 constexpr float kRefSlack = 8.f;
 
-// Byte offset of 16-byte chunk c of key row `row` inside a K or V tile.
-// Chunk-position permutation of row r (mod 16): rotate left by one bit in 4
-// bits, so both the K operand reads and the transposed V reads are free of
-// bank conflicts.
+// Chunk-position permutation of key row r (mod 16) inside a K or V tile:
+// 16-byte chunk c of the row sits at position c ^ swz(r), swz swapping the
+// two 2-bit halves of r, so both the K operand reads and the transposed V
+// reads are free of bank conflicts.
 PKV_DEV int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-PKV_DEV int tile_off(int row, int c) { return row * kRowB + ((c ^ swz(row & 15)) << 4); }
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (expcnt and lgkmcnt left alone).
