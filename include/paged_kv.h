@@ -260,8 +260,11 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  *   paged_kv_write; codes and scales of the addressed slots change.
  * paged_attention_int8 — paged_attention over such a cache: the keys and
  *   values are the dequantised rows; q and out are in dtype (bf16 or fp32).
- *   Every query row (decode rows and the rows of prefill chunks) runs on the
- *   row kernel, with split-KV partitions for rows past 512 tokens.
+ *   With bf16 q and head_dim 128, prefill chunks run on the matrix-core
+ *   prefill kernel, which dequantises each streamed tile in LDS (code *
+ *   scale in float32, rounded to bf16) before both products; every other
+ *   row runs on the row kernel, which applies the scales in float32, with
+ *   split-KV partitions for rows past 512 tokens.
  *   phase_events as for paged_attention_profiled, or NULL.
  * Other arguments, the workspace and the error conventions are those of
  * paged_kv_write / paged_attention.

@@ -212,7 +212,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   if (i8 && !aligned(kv_scales, 4)) return fail(PKV_ERR_ALIGN, "kv_scales needs 4-byte alignment");
 
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t tile_rows = i8 ? 1 : tile_rows_for(dtype, head_dim, group);
+  const int64_t tile_rows = tile_rows_for(dtype, head_dim, group);
   const pkv::WsLayout ws =
       pkv::ws_layout(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len, max_seq_len, tile_rows);
   if (workspace_bytes < ws.total)
@@ -237,7 +237,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   pp.max_seq_len = max_seq_len;
   pp.max_blocks_per_req = max_blocks_per_req;
   pp.split_decode = 1;
-  pp.mfma_prefill = !i8 && prefill_on_mfma(dtype, head_dim) ? 1 : 0;
+  pp.mfma_prefill = prefill_on_mfma(dtype, head_dim) ? 1 : 0;
   pp.prefill_tile_rows = (int32_t)tile_rows;
   pp.hdr = hdr;
   pp.row_items = (int4*)(wsb + ws.row_items);
@@ -260,6 +260,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.out = out;
     fp.q = q;
     fp.cache = kv_cache_layer;
+    fp.kv_scales = kv_scales;
     fp.block_table = block_table;
     fp.qsl = query_start_loc;
     fp.nct = num_computed_tokens;

@@ -69,6 +69,7 @@ struct PrefillParams {
   const int4* items;
   int32_t* hdr;
   int32_t* err;
+  const float* kv_scales;  // int8 cache: [2][num_blocks][16][num_kv_heads] scales; else nullptr
   float scale_log2;
   int32_t num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_req;
 };

@@ -72,6 +72,18 @@ constexpr int kHalfTile = kPfKeys * kRowB;  // K or V part of a tile: 16 KiB
 constexpr int kStage = 2 * kHalfTile;       // one ring slot: K then V
 constexpr int kStages = 4;                  // ring slots: tiles t-1 (PV), t (QK), t+1 and t+2 (in flight)
 constexpr int kKSteps = kD / 16;            // Q.K k-steps
+// INT8 cache: the copies bring codes (128-byte rows) and per-row scales into
+// a 4-slot ring, three tiles ahead; every period the waves dequantise K(t+1)
+// and V(t) (code * scale, rounded to bf16) into two K and two V tiles laid
+// out like the bf16 ring's halves, which the MFMA phases read.
+constexpr int kRowB8 = kD;                        // bytes of one int8 key row
+constexpr int kHalf8 = kPfKeys * kRowB8;          // codes of K or V of a tile: 8 KiB
+constexpr int kScl = kPfKeys * 4;                 // scales of K or V of a tile
+constexpr int kStage8 = 2 * kHalf8 + 2 * kScl;    // one int8 ring slot
+constexpr int kStages8 = 4;
+constexpr int kConv = kStages8 * kStage8;         // offset of the bf16 tiles K0, K1, V0, V1
+constexpr int kLdsI8 = kConv + 4 * kHalfTile;
+static_assert(kLdsI8 + 64 <= 160 * 1024, "INT8 prefill LDS");
 constexpr int kDTiles = kD / 32;            // O^T row tiles
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -171,6 +183,26 @@ PKV_DEV void dma_block(const u32x4& rs, const uint32_t (&voff)[4], uint32_t m0v)
       : "memory", "scc");
 }
 
+// Two buffer_load_dwordx4 ... lds (LDS offsets m0v and m0v + 1 KiB), with
+// the same hazard waits as dma_block.
+PKV_DEV void dma_pair(const u32x4& rs, uint32_t v0, uint32_t v1, uint32_t m0v) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds"
+      : "+{m0}"(m0v)
+      : "v"(v0), "v"(v1), "s"(rs)
+      : "memory", "scc");
+}
+// buffer_load_dword ... lds: each active lane copies 4 bytes at voff to LDS
+// offset m0v + 4 * lane.
+PKV_DEV void dma_dword(const u32x4& rs, uint32_t voff, uint32_t m0v) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds" : "+{m0}"(m0v) : "v"(voff), "s"(rs) : "memory");
+}
+
+
 // Descriptor words for raw (stride 0) buffer access to [base, base + bytes).
 PKV_DEV u32x4 buffer_desc(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
@@ -181,10 +213,11 @@ PKV_DEV u32x4 buffer_desc(const void* base, uint32_t bytes) {
 
 // The metadata arrays are passed on their own as restrict pointers so their
 // wave-uniform reads become scalar loads, which never wait on the tile stream.
+template <bool I8>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     PrefillParams a, const int4* __restrict__ items, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ nct, const int32_t* __restrict__ block_table) {
-  __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) char lds[I8 ? kLdsI8 : kStages * kStage];
   __shared__ int tile_bad[2];
 
   const int tid = threadIdx.x;
@@ -196,7 +229,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   const int G = a.group;
   const int BQ = kPfRows / G;        // query positions per tile
   const int Hkv = a.num_kv_heads;
-  const size_t row_bytes = (size_t)Hkv * kRowB;            // bytes between token rows
+  const size_t row_bytes = (size_t)Hkv * (I8 ? kRowB8 : kRowB);  // bytes between token rows
   const size_t blk_bytes = kBlock * row_bytes;
   const char* kbase = (const char*)a.cache;
   const char* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
@@ -206,7 +239,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // Copy role: wave w streams block (w & 3) of each tile, of K (w < 4) or V.
   const int cblk = w & 3;
   const char* cbase = w < 4 ? kbase : vbase;
-  const int ldst_half = (w < 4 ? 0 : kHalfTile) + cblk * kBlock * kRowB;
+  const int ldst_half = I8 ? (w < 4 ? 0 : kHalf8) + cblk * kBlock * kRowB8 : (w < 4 ? 0 : kHalfTile) + cblk * kBlock * kRowB;
+  // (INT8) this wave's block of scales: [2][num_blocks][16][Hkv] fp32
+  const float* sbase = a.kv_scales + (w < 4 ? 0 : (size_t)a.num_blocks * kBlock * Hkv);
 
   // V^T transpose-read geometry (per lane, independent of the tile).
   const int ts = lane & 15;                            // source lane inside a 16-lane group
@@ -227,13 +262,29 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // wave's block copy carries token row 4j + L/16 of the block and the chunk
   // that lands at LDS position L mod 16 (chunk (L mod 16) ^ swz(row)); the
   // destination is this wave's quarter of a ring slot's K or V half.
+  // (INT8: instruction j < 2 fills LDS rows s = 8j + L/8 of the block, 16
+  // codes of token row s ^ bit2(s) each, so rows r and r + 4 sit in opposite
+  // bank halves for the dequantisation reads; voff[2] is the scale of token
+  // row L of the block, L < 16, stored in row order.)
   uint32_t voff[4];
+  if constexpr (I8) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rb = 4 * j + (lane >> 4);
-    voff[j] = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ swz(rb)) << 4);
+    for (int j = 0; j < 2; ++j) {
+      const int sr = 8 * j + (lane >> 3);      // LDS row inside the block
+      const int tr = sr ^ ((sr >> 2) & 1);     // token row it holds
+      voff[j] = tr * (uint32_t)row_bytes + g * kRowB8 + ((lane & 7) << 4);
+    }
+    voff[2] = (uint32_t)(lane & 15) * (uint32_t)Hkv * 4u + (uint32_t)g * 4u;
+    voff[3] = 0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rb = 4 * j + (lane >> 4);
+      voff[j] = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ swz(rb)) << 4);
+    }
   }
   const uint32_t ldst = (uint32_t)(uintptr_t)PKV_LDS(lds) + (uint32_t)ldst_half;
+  const uint32_t ldsc = (uint32_t)(uintptr_t)PKV_LDS(lds) + (uint32_t)(2 * kHalf8 + (w < 4 ? 0 : kScl) + cblk * kBlock * 4);
   const uint32_t blk_bytes32 = (uint32_t)blk_bytes;
   int* queue = a.hdr + kHdrPrefillQueue + g;
   __shared__ int next_item[2];
@@ -274,9 +325,19 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       phys = (uint32_t)p;
     }
     const u32x4 rs = buffer_desc(cbase + (uint64_t)phys * blk_bytes32, nbytes);
-    const uint32_t m0 = ldst + (uint32_t)(tile & (kStages - 1)) * kStage;
-    static_assert(4 * kRowB == 0x400, "dma_block steps M0 by 1 KiB (4 token rows)");
-    dma_block(rs, voff, m0);
+    if constexpr (I8) {
+      // codes (2 instructions) and scales (1): three vector-memory operations per tile
+      const uint32_t sbytes = (uint32_t)min(max(nvalid, 0), kBlock) * (uint32_t)Hkv * 4u;
+      const u32x4 rss = buffer_desc(sbase + (size_t)phys * kBlock * Hkv, sbytes);
+      const uint32_t slot = (uint32_t)(tile & (kStages8 - 1)) * kStage8;
+      static_assert(8 * kRowB8 == 0x400, "dma_pair steps M0 by 1 KiB (8 token rows)");
+      dma_pair(rs, voff[0], voff[1], ldst + slot);
+      if (lane < kBlock) dma_dword(rss, voff[2], ldsc + slot);
+    } else {
+      const uint32_t m0 = ldst + (uint32_t)(tile & (kStages - 1)) * kStage;
+      static_assert(4 * kRowB == 0x400, "dma_block steps M0 by 1 KiB (4 token rows)");
+      dma_block(rs, voff, m0);
+    }
   };
 
   // Start item ee: thread 0 takes the next queue index (published when this
@@ -319,15 +380,45 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     ids1 = bad1 ? 0 : i1;
     issue_tile(0);
     if (ntiles > 1) issue_tile(1);
+    if (I8 && ntiles > 2) issue_tile(2);
+  };
+
+  // (INT8) Dequantisation role: lane L = 16a + 8b + k of wave w handles
+  // tile row r = 8w + 4b + a, codes 16k .. 16k+15 (LDS row r ^ b of the int8
+  // slot), and writes them as bf16 chunks 2k and 2k+1 of row r at their
+  // swizzled positions; each 16-lane group covers rows of opposite bank
+  // halves (reads) and opposite chunk parity (writes), so neither conflicts.
+  const int cv_r = 8 * w + 4 * ((lane >> 3) & 1) + (lane >> 4);
+  const int cv_rd = (cv_r ^ ((lane >> 3) & 1)) * kRowB8 + (lane & 7) * 16;
+  const int cv_w0 = cv_r * kRowB + (((2 * (lane & 7)) ^ swz(cv_r & 15)) << 4);
+  const int cv_w1 = cv_r * kRowB + (((2 * (lane & 7) + 1) ^ swz(cv_r & 15)) << 4);
+  auto dequant = [&](int tile, int kv) PKV_INLINE {  // kv 0: K, 1: V
+    const char* slot = lds + (tile & (kStages8 - 1)) * kStage8;
+    const u32x4 cw = *(const u32x4*)(slot + kv * kHalf8 + cv_rd);
+    const float sc = *(const float*)(slot + 2 * kHalf8 + kv * kScl + cv_r * 4);
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int x = (int)cw[d];
+      o[2 * d] = pack_bf16((float)((x << 24) >> 24) * sc, (float)((x << 16) >> 24) * sc);
+      o[2 * d + 1] = pack_bf16((float)((x << 8) >> 24) * sc, (float)(x >> 24) * sc);
+    }
+    char* dst = lds + kConv + (2 * kv + (tile & 1)) * kHalfTile;
+    *(u32x4*)(dst + cv_w0) = u32x4{o[0], o[1], o[2], o[3]};
+    *(u32x4*)(dst + cv_w1) = u32x4{o[4], o[5], o[6], o[7]};
   };
 
   int e = next_item[0];
   if (e < n_entries) begin_item(e);
   for (int par = 1; e < n_entries; par ^= 1) {
-    wait_vmem<0>();  // q and the first two tiles are in (and earlier stores done)
+    wait_vmem<0>();  // q and the first tiles are in (and earlier stores done)
     if (tid == 0) {
       next_item[par] = nxt;
       tile_bad[par] = 0;
+    }
+    if constexpr (I8) {  // K(0) is needed in period 0
+      __builtin_amdgcn_s_barrier();
+      dequant(0, 0);
     }
 
     f32x16 oacc[kDTiles];
@@ -395,7 +486,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
         // O^T += V^T P^T: the V^T operand of lane l (head_dim dt*32 + l%32,
         // keys 16*ks + 8*jj + 4*half + 0..3, jj = 0, 1) comes from two
         // transposed reads whose source lanes point at those keys' rows.
-        const char* vl = lds + ((t - 1) % kStages) * kStage + kHalfTile;
+        const char* vl = I8 ? lds + kConv + (2 + ((t - 1) & 1)) * kHalfTile : lds + ((t - 1) % kStages) * kStage + kHalfTile;
         u32x4 ring[kAhead + 1];
 #pragma unroll
         for (int j = 0; j < kAhead; ++j) ring[j] = read_v(vl, j);
@@ -408,7 +499,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       }
       // S^T = K Q^T for the two 32-key halves of the tile (also run on the
       // last entry, t = n, where it reads a stale slot and is never used).
-      const char* kl = lds + (t % kStages) * kStage;
+      const char* kl = I8 ? lds + kConv + (t & 1) * kHalfTile : lds + (t % kStages) * kStage;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -482,6 +573,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     // loops of their own, so each loop carries only the state its next phase
     // needs (P^T into group 0's MFMA phase, S^T into group 1's softmax).
     auto tile_barrier = [&](int t) PKV_INLINE {
+      if constexpr (I8) {  // tile t+1's codes are in; last period's bf16 writes are done
+        if (t + 2 < ntiles)
+          wait_vmem<3>();
+        else
+          wait_vmem<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+      }
       if (t + 1 < ntiles)
         wait_vmem<4>();
       else
@@ -491,7 +592,33 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
-    if (grp == 0) {
+    if constexpr (I8) {
+      // As below, with the copies three tiles ahead and each wave's share of
+      // the dequantisation of K(t+1) and V(t) in its VALU phase.
+      if (grp == 0) {
+        for (int t = 0; t <= ntiles; ++t) {
+          tile_barrier(t);
+          mfma_phase(t);
+          if (t + 3 < ntiles) issue_tile(t + 3);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t + 1 < ntiles) dequant(t + 1, 0);
+          if (t < ntiles) {
+            dequant(t, 1);
+            vec_phase(t);
+          }
+        }
+      } else {
+        for (int t = 0; t <= ntiles; ++t) {
+          tile_barrier(t);
+          if (t >= 1) vec_phase(t - 1);
+          if (t + 3 < ntiles) issue_tile(t + 3);
+          if (t + 1 < ntiles) dequant(t + 1, 0);
+          if (t < ntiles) dequant(t, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_phase(t);
+        }
+      }
+    } else if (grp == 0) {
       for (int t = 0; t <= ntiles; ++t) {
         tile_barrier(t);
         mfma_phase(t);
@@ -549,8 +676,12 @@ int prefill_tile_rows(int32_t group) { return kPfRows / (group > 0 ? group : 1);
 
 int launch_prefill(const PrefillParams& p, int32_t head_dim, int64_t grid, hipStream_t stream) {
   if (head_dim != kD || grid <= 0) return 1;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.qsl,
-                     p.nct, p.block_table);
+  if (p.kv_scales)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.qsl,
+                       p.nct, p.block_table);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items,
+                       p.qsl, p.nct, p.block_table);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -37,8 +37,9 @@ def _quantised_pool(wl):
     return codes, scales
 
 
-def _run(wl, dtype_q):
+def _run(wl, dtype_q, block_table=None, expect_error=0):
     import paged_kv_cache_61_amd as pkv
+    bt = wl.block_table if block_table is None else block_table
     codes, scales = _quantised_pool(wl)
     d_codes = torch.from_numpy(codes).cuda()
     d_scales = torch.from_numpy(scales).cuda()
@@ -49,12 +50,12 @@ def _run(wl, dtype_q):
     ws = torch.empty(max(256, pkv.paged_attention_workspace_size(wl.num_reqs, wl.num_tokens, wl.num_q_heads,
                                                                  wl.head_dim, wl.max_query_len, wl.max_seq_len)),
                      dtype=torch.uint8, device="cuda")
-    out = pkv.paged_attention_int8(to_dev(wl.q, dtype_q), d_codes, d_scales, i32(wl.block_table),
+    out = pkv.paged_attention_int8(to_dev(wl.q, dtype_q), d_codes, d_scales, i32(bt),
                                    i32(wl.seq_lens), i32(wl.query_start_loc), i32(wl.num_computed_tokens),
                                    wl.scale, max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
                                    workspace=ws)
     torch.cuda.synchronize()
-    assert int(err.item()) == 0 and pkv.pkv_read_device_error(ws) == 0
+    assert int(err.item()) == 0 and pkv.pkv_read_device_error(ws) == expect_error
     ref_codes, ref_scales = oracle.kv_write_int8(codes, scales, wl.k_new, wl.v_new, wl.slot_mapping, wl.dtype)
     return out, d_codes.cpu().numpy(), d_scales.cpu().numpy(), ref_codes, ref_scales
 
@@ -76,6 +77,42 @@ def test_int8_write_and_attention(dtype, D, Hq, Hkv):
     plain = oracle.attention(wl.q, oracle.kv_write(wl.pool, wl.k_new, wl.v_new, wl.slot_mapping), wl.block_table,
                              wl.seq_lens, wl.query_start_loc, wl.num_computed_tokens, wl.scale, dtype)
     print(f"[int8] quantisation effect on the output: max abs {np.abs(out_f64(out) - plain).max():.4f}", flush=True)
+
+
+@pytest.mark.parametrize("Hq,Hkv,neg", [(32, 8, False), (8, 8, False), (64, 8, False), (16, 1, True),
+                                         (8, 2, False)])
+def test_int8_prefill_chunks_on_matrix_cores(Hq, Hkv, neg):
+    # bf16 q, head_dim 128: prefill chunks run on the MFMA kernel, which
+    # dequantises the streamed int8 tiles in LDS.  Chunks of many 64-key
+    # tiles (the int8 ring and both dequantised K/V buffers wrap), ragged
+    # tails, a prefix past 8192 keys (ids read per tile), a negative scale.
+    _gpu()
+    reqs = [(1000, 300), (0, 517), (3000, 64), (130, 1), (8200, 40), (63, 65), (5, 2)]
+    wl = workloads.build(workloads.small_spec(f"int8 prefill {Hq}/{Hkv}", 57, "bf16", Hq, Hkv, 128, reqs))
+    if neg:
+        wl.scale = -wl.scale
+    out, _, _, ref_codes, ref_scales = _run(wl, "bf16")
+    ref = oracle.attention_int8(wl.q, ref_codes, np.nan_to_num(ref_scales, nan=0.0), wl.block_table,
+                                wl.seq_lens, wl.query_start_loc, wl.num_computed_tokens, wl.scale, "bf16")
+    assert_close(out_f64(out), ref, "bf16", f"int8 prefill {Hq}/{Hkv} neg={neg}")
+
+
+def test_int8_prefill_bad_block_id_confined_to_its_request():
+    # an id outside the pool in a chunk's table (in the first 128 tiles of
+    # one request, past them in another) is reported and turns only those
+    # requests' rows into NaN
+    _gpu()
+    import paged_kv_cache_61_amd as pkv
+    reqs = [(9000, 70), (500, 100), (20, 1), (300, 50)]
+    wl = workloads.build(workloads.small_spec("int8 prefill bad id", 58, "bf16", 16, 4, 128, reqs))
+    good, *_ = _run(wl, "bf16")
+    bt = wl.block_table.copy()
+    bt[0, 4 * 130 + 1] = wl.num_blocks + 3
+    bt[1, 5] = -2
+    out, *_ = _run(wl, "bf16", block_table=bt, expect_error=pkv.DEVERR_BLOCK_ID)
+    o, gd = out_f64(out), out_f64(good)
+    assert np.isnan(o[0:170]).all()
+    assert np.array_equal(o[170:], gd[170:])
 
 
 def test_int8_write_zero_rows_and_padding():
