@@ -262,9 +262,12 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  *   values are the dequantised rows; q and out are in dtype (bf16 or fp32).
  *   With bf16 q and head_dim 128, prefill chunks run on the matrix-core
  *   prefill kernel, which dequantises each streamed tile in LDS (code *
- *   scale in float32, rounded to bf16) before both products; every other
- *   row runs on the row kernel, which applies the scales in float32, with
- *   split-KV partitions for rows past 512 tokens.
+ *   scale in float32, rounded to bf16) before both products.  Every other
+ *   row (decode rows, split-KV partitions of rows past 512 tokens, and
+ *   prefill rows of other dtypes or head sizes) runs on a row kernel: with
+ *   bf16 q all G query heads of a kv head share 16x16 matrix-core tiles over
+ *   the exact integer codes, the scales entering in float32 (p * v_scale is
+ *   rounded to bf16); with fp32 q a VALU kernel works in float32.
  *   phase_events as for paged_attention_profiled, or NULL.
  * Other arguments, the workspace and the error conventions are those of
  * paged_kv_write / paged_attention.

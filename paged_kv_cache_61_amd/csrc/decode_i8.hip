@@ -11,12 +11,12 @@
 // (FlashAttention)") with k, v the dequantised rows; work items, split-KV
 // partitions and the merge are those of the bf16 / fp32 row kernel.
 //
-// Per wave and 16-token block:
+// Two kernels: bf16 q runs on the matrix cores (row_attn_i8_mfma_kernel,
+// below); fp32 q on the VALU kernel, per wave and 16-token block:
 //  * q.k: 4 lanes per token, each over a quarter of head_dim.  A code c is
 //    read as the unsigned byte u = c + 128 (one xor per 4 codes), converted
 //    with v_cvt_f32_ubyte, and sum_d q_d c_d = sum_d q_d u_d - 128 sum_d q_d
-//    (the q sums are taken once per item).  For bf16 q the u values, exact in
-//    bf16, are paired for v_dot2_f32_bf16.  The dot is multiplied by the
+//    (the q sums are taken once per item).  The dot is multiplied by the
 //    token's K scale; the quad adds finish it on all 4 lanes.
 //  * online softmax in the log2 domain, the row max moving per block.
 //  * p.v: lanes own 4 consecutive head_dim elements of D/4-lane groups; the
@@ -77,37 +77,14 @@ PKV_DEV void ubytes(uint32_t w, float (&f)[4]) {
   f[3] = (float)(w >> 24);
 }
 
-// Two small integers as float32 -> their bf16 pair (exact: < 2^8).
-PKV_DEV uint32_t pair_bf16(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302);
-}
-
-template <bool QBF16>
-struct QSlice;
-// bf16 q: the lane's D/4 elements as bf16 pairs
-template <>
-struct QSlice<true> {
-  template <int N>
-  struct Regs {
-    uint32_t w[N / 2];
-  };
-};
-template <>
-struct QSlice<false> {
-  template <int N>
-  struct Regs {
-    float w[N];
-  };
-};
-
-template <bool QBF16, int D, int GM>
+// fp32 q (bf16 q: row_attn_i8_mfma_kernel).
+template <int D, int GM>
 __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const float* __restrict__ kv_scales) {
   constexpr int QPL = D / 4;          // q elements per lane (4 lanes per token)
   constexpr int KLD = QPL / 16;       // 16-byte code loads per lane per block (K)
   constexpr int VL = D / 4;           // lanes per token row in the p.v layout (4 codes each)
   constexpr int TPV = kWave / VL;     // tokens per V load
   constexpr int VLD = kBlock / TPV;   // V loads per lane per block
-  using QR = typename QSlice<QBF16>::template Regs<QPL>;
   __shared__ float pw_lds[4][GM][kBlock];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -131,38 +108,23 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
     const ItemI8 cur = fetch_item_i8(a, it, per_pair, n_head, gmax);
     const size_t out_row = ((size_t)cur.t * a.num_q_heads + cur.h0) * D;
     if (cur.part == kNanRow) {
-      for (int idx = lane; idx < cur.nh * D; idx += kWave) {
-        if (QBF16)
-          ((uint16_t*)a.out)[out_row + idx] = 0x7fc0;
-        else
-          ((float*)a.out)[out_row + idx] = __builtin_nanf("");
-      }
+      for (int idx = lane; idx < cur.nh * D; idx += kWave) ((float*)a.out)[out_row + idx] = __builtin_nanf("");
       continue;
     }
     const int g = cur.g, nh = cur.nh, vis = cur.vis;
 
     // q slice: elements cq*QPL .. +QPL-1 of each head; and its sum.
-    QR qr[GM];
+    float qr[GM][QPL];
     float qsum[GM];
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
       qsum[hh] = 0.f;
-      if constexpr (QBF16) {
-        const uint32_t* src = (const uint32_t*)((const uint16_t*)a.q + out_row + hh * D + cq * QPL);
+      const float* src = (const float*)a.q + out_row + hh * D + cq * QPL;
 #pragma unroll
-        for (int j = 0; j < QPL / 2; ++j) {
-          const uint32_t x = hh < nh ? src[j] : 0u;
-          qr[hh].w[j] = x;
-          qsum[hh] += bf16_lo(x) + bf16_hi(x);
-        }
-      } else {
-        const float* src = (const float*)a.q + out_row + hh * D + cq * QPL;
-#pragma unroll
-        for (int j = 0; j < QPL; ++j) {
-          const float x = hh < nh ? src[j] : 0.f;
-          qr[hh].w[j] = x;
-          qsum[hh] += x;
-        }
+      for (int j = 0; j < QPL; ++j) {
+        const float x = hh < nh ? src[j] : 0.f;
+        qr[hh][j] = x;
+        qsum[hh] += x;
       }
     }
 
@@ -208,15 +170,9 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
           float f[4];
           ubytes(s.k[j][c] ^ 0x80808080u, f);
 #pragma unroll
-          for (int hh = 0; hh < GM; ++hh) {
-            if constexpr (QBF16) {
-              x[hh] = dot2_bf16(qr[hh].w[8 * j + 2 * c], pair_bf16(f[0], f[1]), x[hh]);
-              x[hh] = dot2_bf16(qr[hh].w[8 * j + 2 * c + 1], pair_bf16(f[2], f[3]), x[hh]);
-            } else {
+          for (int hh = 0; hh < GM; ++hh)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) x[hh] = fmaf(qr[hh].w[16 * j + 4 * c + e], f[e], x[hh]);
-            }
-          }
+            for (int e = 0; e < 4; ++e) x[hh] = fmaf(qr[hh][16 * j + 4 * c + e], f[e], x[hh]);
         }
       }
       float sc[GM], bm[GM];
@@ -305,14 +261,8 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
         const int d0 = 4 * vd;
         if (cur.slot0 < 0) {
           const float inv = wave_bad ? __builtin_nanf("") : 1.f / l;
-          if constexpr (QBF16) {
-            uint16_t* dst = (uint16_t*)a.out + out_row + hh * D + d0;
-            *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16(o[hh][0] * inv) | ((uint32_t)f32_to_bf16(o[hh][1] * inv) << 16),
-                                      (uint32_t)f32_to_bf16(o[hh][2] * inv) | ((uint32_t)f32_to_bf16(o[hh][3] * inv) << 16));
-          } else {
-            *(float4*)((float*)a.out + out_row + hh * D + d0) =
-                make_float4(o[hh][0] * inv, o[hh][1] * inv, o[hh][2] * inv, o[hh][3] * inv);
-          }
+          *(float4*)((float*)a.out + out_row + hh * D + d0) =
+              make_float4(o[hh][0] * inv, o[hh][1] * inv, o[hh][2] * inv, o[hh][3] * inv);
         } else {
           const size_t sidx = (size_t)(cur.slot0 + cur.part) * a.num_q_heads + cur.h0 + hh;
           const float nan_or_0 = wave_bad ? __builtin_nanf("") : 0.f;
@@ -325,40 +275,311 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
   }
 }
 
-template <bool QBF16, int D, int GM>
-int launch_i8_g(const RowParams& p, const float* scales, int64_t bound_waves, int cus, hipStream_t s) {
-  // persistent grid: as many 4-wave workgroups as fit at once, no more than the items need
+// ---------------------------------------------------------------------------
+// bf16 q: the G query heads of a kv head share the block on the matrix cores.
+//
+// One wave per (query row or split-KV partition, kv head), all G <= 16 heads
+// of the group in the 16 columns of 16x16 MFMA tiles (columns past G carry
+// q = 0 and are not stored).  Per 16-token block:
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over head_dim/32 k-steps: A = the
+//                   block's codes as exact bf16 integers (lane l: token l%16),
+//                   B = q (lane l: head l%16), so lane l ends up with head l%16
+//                   and tokens 4*(l/16) + 0..3 of the block;
+//   scores          S * k_scale[token] * scale * log2(e); online softmax per
+//                   head (the block max needs two exchanges, lanes l^16 and
+//                   l^32); the reference max moves only when a block's max
+//                   exceeds it by more than 2^8 (then O and l are rescaled);
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16 over head_dim/16 tiles: A = the
+//                   codes of the same 4 tokens (lane l: head_dim row l%16 of
+//                   each tile), B = p * v_scale[token] rounded to bf16, taken
+//                   from the S^T registers as they are.
+// The dequantisation is exact (codes are small integers), the scales enter in
+// float32; only p * v_scale is rounded to bf16 (relative 2^-9), as in the
+// bf16-cache kernels.  Each lane's head_dim order inside a k-step is the same
+// permutation for q and the codes (the dot product does not depend on it);
+// head_dim tile dt, MFMA row r holds element (D/16)*r + dt, so a lane's output
+// elements are contiguous.  Masked tokens (past the row's position, including
+// unused tail slots whose codes and scales may be garbage or NaN) get p = 0
+// by selection.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Signed byte k of w as float (v_cvt_f32_i32 with a sign-extending byte select).
+template <int K>
+PKV_DEV float sbyte(uint32_t w) {
+  return (float)(((int)w << (24 - 8 * K)) >> 24);
+}
+// Two integer-valued floats (|x| < 2^8) as a bf16 pair: the top halves (exact).
+PKV_DEV uint32_t ipair(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302);
+}
+// x[l] op x[l ^ 16] and x[l] op x[l ^ 32] (v_permlane16_swap / v_permlane32_swap).
+PKV_DEV float xmax16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+PKV_DEV float xmax32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+PKV_DEV float xsum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+PKV_DEV float xsum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+#define PKV_INLINE __attribute__((always_inline))
+
+constexpr float kRefSlackI8 = 8.f;   // see the reference max above (log2 units)
+
+template <int D, int NST>
+__global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel(RowParams a, const float* __restrict__ kv_scales) {
+  constexpr int NS = D / 32;    // k-steps of S^T
+  constexpr int NDT = D / 16;   // head_dim tiles of O^T = code bytes per token per lane
+  constexpr int KLD = D / 64;   // 16-byte code loads per lane per block (K)
+  constexpr int VW = NDT / 4;   // code dwords per token per lane (V)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int per_pair = a.num_kv_heads * a.head_groups;
+  const int64_t total = (int64_t)a.hdr[kHdrRowItems] * per_pair;
+  const int n_head = a.hdr[kHdrRowHead];
+  const uint32_t row_stride = (uint32_t)a.num_kv_heads * D;      // bytes between token rows
+  const uint32_t blk_bytes = kBlock * row_stride;
+  const int8_t* kbase = (const int8_t*)a.cache;
+  const int8_t* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
+  const size_t scale_half = (size_t)a.num_blocks * kBlock * a.num_kv_heads;
+  const float sl2 = a.scale_log2;
+
+  for (int64_t it = (int64_t)blockIdx.x * 4 + w; it < total; it += (int64_t)gridDim.x * 4) {
+    const ItemI8 cur = fetch_item_i8(a, it, per_pair, n_head, 16);
+    const size_t out_row = ((size_t)cur.t * a.num_q_heads + cur.h0) * D;
+    if (cur.part == kNanRow) {
+      for (int idx = lane; idx < cur.nh * D; idx += kWave) ((uint16_t*)a.out)[out_row + idx] = 0x7fc0;
+      continue;
+    }
+    const int g = cur.g, nh = cur.nh, vis = cur.vis;
+    const bool col_ok = r16 < nh;
+
+    // q of head r16 as the B operand: k-step s holds elements
+    // 64*(s/2) + 16*q4 + 8*(s%2) + 0..7 (the codes use the same order)
+    // (columns past the group read head 0's row, then zero it: no address
+    // outside q is formed)
+    u32x4 qb[NS];
+    const uint32_t qmask = col_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x4* src = (const u32x4*)((const uint16_t*)a.q + out_row + (col_ok ? r16 : 0) * D + 64 * (s >> 1) +
+                                        16 * q4 + 8 * (s & 1));
+      qb[s] = *src & qmask;
+    }
+
+    f32x4_t oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, lsum = 0.f;
+    bool bad = false;
+
+    struct Stage {
+      u32x4 k[KLD];
+      uint32_t v[4][VW];
+      float sk, sv;
+    };
+    // K: token r16, bytes 64j + 16*q4 .. +15 (j < KLD); V: tokens 4*q4 + i,
+    // bytes NDT*r16 .. +NDT-1; scales of token r16.
+    const uint32_t koff = r16 * row_stride + g * D + 16 * q4;
+    const uint32_t voff = 4 * q4 * row_stride + g * D + NDT * r16;
+    auto load = [&](Stage& st, int phys) PKV_INLINE {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)phys * blk_bytes, blk_bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)phys * blk_bytes, blk_bytes);
+#pragma unroll
+      for (int j = 0; j < KLD; ++j) st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * j, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (VW == 2) {
+          const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, 0);
+          st.v[i][0] = x.x;
+          st.v[i][1] = x.y;
+        } else {
+          st.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, i * row_stride, 0);
+        }
+      }
+      const size_t srow = ((size_t)phys * kBlock + r16) * a.num_kv_heads + g;
+      st.sk = kv_scales[srow];
+      st.sv = kv_scales[scale_half + srow];
+    };
+
+    auto compute = [&](const Stage& st, int jblk) PKV_INLINE {
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint32_t c0 = st.k[s >> 1][2 * (s & 1)], c1 = st.k[s >> 1][2 * (s & 1) + 1];
+        const u32x4 ka = {ipair(sbyte<0>(c0), sbyte<1>(c0)), ipair(sbyte<2>(c0), sbyte<3>(c0)),
+                          ipair(sbyte<0>(c1), sbyte<1>(c1)), ipair(sbyte<2>(c1), sbyte<3>(c1))};
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                       __builtin_bit_cast(bf16x8_t, qb[s]), sacc, 0, 0, 0);
+      }
+      // scales of tokens 4*q4 + i from the lanes that loaded them (lane = token)
+      const int tok0 = jblk * kBlock + 4 * q4;
+      float sc[4], vsc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int src = 4 * (4 * q4 + i);
+        const float ks = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(st.sk)));
+        vsc[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(st.sv)));
+        sc[i] = tok0 + i < vis ? sacc[i] * (ks * sl2) : -INFINITY;
+      }
+      float bmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      bmax = xmax32(xmax16(bmax));
+      if (__any(bmax > m_ref + kRefSlackI8)) {
+        const float mn = fmaxf(m_ref, bmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);   // 0 on the first block
+        m_ref = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      }
+      float pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[i] - m_ref);   // 0 for masked tokens
+        lsum += p;
+        pw[i] = tok0 + i < vis ? p * vsc[i] : 0.f;
+      }
+      const u32x2 pb = {__builtin_bit_cast(uint32_t, __builtin_convertvector(
+                            (float __attribute__((ext_vector_type(2)))){pw[0], pw[1]}, bf16x2_t)),
+                        __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                            (float __attribute__((ext_vector_type(2)))){pw[2], pw[3]}, bf16x2_t))};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int wd = dt >> 2;
+        float c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t x = st.v[i][wd];
+          c[i] = (dt & 3) == 0 ? sbyte<0>(x) : (dt & 3) == 1 ? sbyte<1>(x) : (dt & 3) == 2 ? sbyte<2>(x) : sbyte<3>(x);
+        }
+        const u32x2 va = {ipair(c[0], c[1]), ipair(c[2], c[3])};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, va),
+                                                             __builtin_bit_cast(s16x4_t, pb), oacc[dt], 0, 0, 0);
+      }
+    };
+
+    // blocks jb .. je-1, ids 64 at a time, NST - 1 blocks in flight ahead
+    const int n = cur.je - cur.jb;
+    const int32_t* bt = a.block_table + (size_t)cur.r * a.max_blocks_per_req;
+    for (int k0 = 0; k0 < n; k0 += kWave) {
+      int id = cur.jb + k0 + lane < cur.je ? bt[cur.jb + k0 + lane] : 0;
+      if (id < 0 || id >= a.num_blocks) {
+        id = 0;
+        bad = true;
+      }
+      const int nb = min(kWave, n - k0);
+      const int jfirst = cur.jb + k0;
+      Stage st[NST];
+#pragma unroll
+      for (int j = 0; j < NST - 1; ++j)
+        if (j < nb) load(st[j], __builtin_amdgcn_readlane(id, j));
+      for (int k = 0; k < nb; k += NST) {
+#pragma unroll
+        for (int j = 0; j < NST; ++j) {
+          if (k + j < nb) {
+            if (k + j + NST - 1 < nb) load(st[(j + NST - 1) % NST], __builtin_amdgcn_readlane(id, k + j + NST - 1));
+            compute(st[j], jfirst + k + j);
+          }
+        }
+      }
+    }
+
+    // finish: l over the head's four lanes; lane (r16, q4) holds O elements
+    // NDT*(4*q4 + i) + dt of head r16
+    const bool wave_bad = __any(bad);
+    if (wave_bad && lane == 0) atomicOr(a.err, PKV_DEVERR_BLOCK_ID);
+    const float l = xsum32(xsum16(lsum));
+    if (col_ok) {
+      if (cur.slot0 < 0) {
+        const float inv = wave_bad ? __builtin_nanf("") : 1.f / l;
+        uint16_t* dst = (uint16_t*)a.out + out_row + r16 * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t pk[NDT / 2];
+#pragma unroll
+          for (int e = 0; e < NDT / 2; ++e)
+            pk[e] = (uint32_t)f32_to_bf16(oacc[2 * e][i] * inv) | ((uint32_t)f32_to_bf16(oacc[2 * e + 1][i] * inv) << 16);
+          if constexpr (NDT == 8)
+            *(u32x4*)(dst + NDT * (4 * q4 + i)) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+          else
+            *(u32x2*)(dst + NDT * (4 * q4 + i)) = u32x2{pk[0], pk[1]};
+        }
+      } else {
+        const size_t sidx = (size_t)(cur.slot0 + cur.part) * a.num_q_heads + cur.h0 + r16;
+        const float nan_or_0 = wave_bad ? __builtin_nanf("") : 0.f;
+        float* dst = a.part_o + sidx * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < NDT / 4; ++e)
+            *(float4*)(dst + NDT * (4 * q4 + i) + 4 * e) =
+                make_float4(oacc[4 * e][i] + nan_or_0, oacc[4 * e + 1][i] + nan_or_0, oacc[4 * e + 2][i] + nan_or_0,
+                            oacc[4 * e + 3][i] + nan_or_0);
+        if (q4 == 0) a.part_ml[sidx] = make_float2(m_ref, l);
+      }
+    }
+  }
+}
+
+constexpr int kI8Stages = 3;   // register ring of blocks per wave
+
+template <int D>
+int launch_i8_mfma(const RowParams& p, const float* scales, int64_t bound_waves, int cus, hipStream_t s) {
   static int occ = 0;
-  if (occ <= 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, row_attn_i8_kernel<QBF16, D, GM>, 256, 0) !=
+  if (occ <= 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, row_attn_i8_mfma_kernel<D, kI8Stages>, 256, 0) !=
                        hipSuccess ||
                    occ <= 0))
     occ = 2;
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((bound_waves + 3) / 4, (int64_t)cus * occ));
-  hipLaunchKernelGGL((row_attn_i8_kernel<QBF16, D, GM>), dim3((unsigned)grid), dim3(256), 0, s, p, scales);
+  hipLaunchKernelGGL((row_attn_i8_mfma_kernel<D, kI8Stages>), dim3((unsigned)grid), dim3(256), 0, s, p, scales);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <bool QBF16, int D>
+template <int D, int GM>
+int launch_i8_g(const RowParams& p, const float* scales, int64_t bound_waves, int cus, hipStream_t s) {
+  // persistent grid: as many 4-wave workgroups as fit at once, no more than the items need
+  static int occ = 0;
+  if (occ <= 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, row_attn_i8_kernel<D, GM>, 256, 0) !=
+                       hipSuccess ||
+                   occ <= 0))
+    occ = 2;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((bound_waves + 3) / 4, (int64_t)cus * occ));
+  hipLaunchKernelGGL((row_attn_i8_kernel<D, GM>), dim3((unsigned)grid), dim3(256), 0, s, p, scales);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <int D>
 int launch_i8_d(const RowParams& p, const float* scales, int64_t bound_waves, int cus, hipStream_t s) {
-  const int gm = p.head_groups > 1 ? (QBF16 ? 4 : 2) : p.group;
-  if (gm <= 1) return launch_i8_g<QBF16, D, 1>(p, scales, bound_waves, cus, s);
-  if (gm <= 2) return launch_i8_g<QBF16, D, 2>(p, scales, bound_waves, cus, s);
-  if constexpr (QBF16) return launch_i8_g<QBF16, D, 4>(p, scales, bound_waves, cus, s);
+  // fp32 q: wider groups arrive split into head groups of 2
+  const int gm = p.head_groups > 1 ? 2 : p.group;
+  if (gm <= 1) return launch_i8_g<D, 1>(p, scales, bound_waves, cus, s);
+  if (gm <= 2) return launch_i8_g<D, 2>(p, scales, bound_waves, cus, s);
   return 1;
 }
 
 }  // namespace
 
-int max_group_regs_i8(int32_t dtype) { return dtype == PKV_BF16 ? 4 : 2; }
+int max_group_regs_i8(int32_t dtype) { return dtype == PKV_BF16 ? 16 : 2; }
 
 int launch_rows_i8(const RowParams& p, const float* kv_scales, int32_t dtype, int32_t head_dim,
                    int64_t bound_waves, int cus, hipStream_t stream) {
   if (bound_waves <= 0) return 0;
-  const bool bf16 = dtype == PKV_BF16;
-  if (head_dim == 64) return bf16 ? launch_i8_d<true, 64>(p, kv_scales, bound_waves, cus, stream)
-                                  : launch_i8_d<false, 64>(p, kv_scales, bound_waves, cus, stream);
-  return bf16 ? launch_i8_d<true, 128>(p, kv_scales, bound_waves, cus, stream)
-              : launch_i8_d<false, 128>(p, kv_scales, bound_waves, cus, stream);
+  if (dtype == PKV_BF16)  // every group width in one wave (head_groups == 1)
+    return head_dim == 64 ? launch_i8_mfma<64>(p, kv_scales, bound_waves, cus, stream)
+                          : launch_i8_mfma<128>(p, kv_scales, bound_waves, cus, stream);
+  if (head_dim == 64) return launch_i8_d<64>(p, kv_scales, bound_waves, cus, stream);
+  return launch_i8_d<128>(p, kv_scales, bound_waves, cus, stream);
 }
 
 }  // namespace pkv

@@ -61,7 +61,9 @@ def _run(wl, dtype_q, block_table=None, expect_error=0):
 
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 8, 8), ("bf16", 128, 32, 8), ("bf16", 64, 16, 2),
-                                            ("f32", 64, 8, 2), ("f32", 128, 4, 4), ("bf16", 128, 64, 8)])
+                                            ("f32", 64, 8, 2), ("f32", 128, 4, 4), ("bf16", 128, 64, 8),
+                                            ("bf16", 128, 16, 1), ("bf16", 64, 32, 2), ("bf16", 128, 6, 2),
+                                            ("f32", 128, 16, 2)])
 def test_int8_write_and_attention(dtype, D, Hq, Hkv):
     _gpu()
     reqs = [(0, 1), (37, 1), (600, 1), (1500, 1), (15, 9), (40, 33), (0, 70), (511, 1), (512, 1), (2100, 2)]
