@@ -533,6 +533,221 @@ __global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
   }
 }
 
+// bf16 q and cache on the matrix cores: one wave per (row or partition, kv
+// head) with all G <= 16 query heads of the group in the 16 columns of 16x16
+// MFMA tiles (columns past G carry q = 0 and are not stored), so a block is
+// read once and its dot products cost a few MFMAs whatever G is.  Per block:
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over head_dim/32 k-steps, the
+//                   A operand straight from the loaded rows (lane l: token
+//                   l%16, elements 32s + 8*(l/16) .. +7 of k-step s), B = q of
+//                   head l%16 (same elements), so lane l ends up with head
+//                   l%16 and tokens 4*(l/16) + 0..3;
+//   online softmax  per head in the log2 domain, the block max over two
+//                   lane exchanges (l^16, l^32), the reference max moving only
+//                   when a block's max exceeds it by more than 2^8; p rounded
+//                   to bf16 for the product and added to l as rounded;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16 over head_dim/16 tiles: A = V of
+//                   the same 4 tokens (lane l: element (D/16)*(l%16) + dt of
+//                   tile dt, two half-word permutes per tile), B = P^T from the
+//                   S^T registers as they are.
+// Masked tokens (past the row's position) get p = 0 by selection and their V
+// rows are zeroed before the product, so NaN in unused slots never reaches
+// the output.  Items are visited in the serpentine order of row_attn_kernel,
+// with the next item's descriptor and block ids fetched while one streams.
+template <int D>
+__global__ __launch_bounds__(256, 2) void row_attn_mfma_kernel(RowParams a) {
+  constexpr int NS = D / 32;    // k-steps of S^T = 16-byte K loads per lane per block
+  constexpr int NDT = D / 16;   // head_dim tiles of O^T = V elements per token per lane
+  constexpr int ROWB = D * 2;
+  constexpr int NST = 2;        // register ring of blocks
+  typedef typename std::conditional<NDT == 8, u32x4, u32x2>::type VRow;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int per_pair = a.num_kv_heads * a.head_groups;
+  const int64_t total = (int64_t)a.hdr[kHdrRowItems] * per_pair;
+  const int n_head = a.hdr[kHdrRowHead];
+  const uint32_t row_stride = (uint32_t)a.num_kv_heads * ROWB;
+  const uint32_t blk_bytes = kBlock * row_stride;
+  const char* kbase = (const char*)a.cache;
+  const char* vbase = kbase + (size_t)a.num_blocks * blk_bytes;
+  const float sl2 = a.scale_log2;
+
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + w;
+  auto item_of = [&](int64_t k) { return k * nw + ((k & 1) ? nw - 1 - gw : gw); };
+  int64_t round = 0;
+  const int64_t it = item_of(0);
+  if (it >= total) return;
+  int64_t nx = item_of(1);
+  RowItem cur = fetch_item<16>(a, it, per_pair, n_head);
+  int btv = fetch_ids(a, cur, 0, lane);
+
+  while (true) {
+    const bool has_next = nx < total;
+    const int64_t nx2 = item_of(round + 2);
+    RowItem nxt = cur;
+    int btv_next = 0;
+    if (has_next) {  // prefetch: consumed only after this item
+      nxt = fetch_item<16>(a, nx, per_pair, n_head);
+      btv_next = fetch_ids(a, nxt, 0, lane);
+    }
+    const size_t out_row = ((size_t)cur.t * a.num_q_heads + cur.h0) * D;
+    if (cur.part == kNanRow) {
+      for (int idx = lane; idx < cur.nh * D; idx += kWave) ((uint16_t*)a.out)[out_row + idx] = 0x7fc0;
+    } else {
+      const int g = cur.g, nh = cur.nh, vis = cur.vis;
+      const bool col_ok = r16 < nh;
+      // q of head r16 (columns past the group read head 0's row, then zero it)
+      u32x4 qb[NS];
+      const uint32_t qmask = col_ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        qb[s] = *(const u32x4*)((const uint16_t*)a.q + out_row + (col_ok ? r16 : 0) * D + 32 * s + 8 * q4) & qmask;
+
+      f32x4_t oacc[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      float m_ref = -INFINITY, lsum = 0.f;
+      bool bad = false;
+
+      struct Stage {
+        u32x4 k[NS];
+        VRow v[4];
+      };
+      const uint32_t koff = r16 * row_stride + g * ROWB + 16 * q4;
+      const uint32_t voff = 4 * q4 * row_stride + g * ROWB + 2 * NDT * r16;
+      auto load = [&](Stage& st, int phys) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)phys * blk_bytes, blk_bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)phys * blk_bytes, blk_bytes);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * s, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (NDT == 8)
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, i * row_stride, 0);
+          else
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, 0);
+        }
+      };
+
+      auto compute = [&](const Stage& st, int jblk) __attribute__((always_inline)) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, st.k[s]),
+                                                         __builtin_bit_cast(bf16x8_t, qb[s]), sacc, 0, 0, 0);
+        const int tok0 = jblk * kBlock + 4 * q4;
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = tok0 + i < vis ? sacc[i] * sl2 : -INFINITY;
+        float bmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        bmax = xmax32(xmax16(bmax));
+        if (__any(bmax > m_ref + kRefSlack)) {
+          const float mn = fmaxf(m_ref, bmax);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);   // 0 on the first block
+          m_ref = mn;
+          lsum *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        }
+        uint32_t pb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[i] - m_ref));   // 0 for masked tokens
+          lsum += __uint_as_float(pb[i] << 16);
+        }
+        const u32x2 pt = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+        uint32_t vw[4][NDT / 2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < NDT / 2; ++e) vw[i][e] = st.v[i][e];
+        if (jblk * kBlock + kBlock > vis) {   // the row's last block: zero V past the position
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tok0 + i >= vis)
+#pragma unroll
+              for (int e = 0; e < NDT / 2; ++e) vw[i][e] = 0u;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+          const u32x2 va = {__builtin_amdgcn_perm(vw[1][dt >> 1], vw[0][dt >> 1], sel),
+                            __builtin_amdgcn_perm(vw[3][dt >> 1], vw[2][dt >> 1], sel)};
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, va),
+                                                               __builtin_bit_cast(s16x4_t, pt), oacc[dt], 0, 0, 0);
+        }
+      };
+
+      // Blocks jb .. je-1, 64 ids at a time, NST - 1 blocks in flight ahead.
+      const int n = cur.je - cur.jb;
+      for (int k0 = 0; k0 < n; k0 += kWave) {
+        if (k0 > 0) btv = fetch_ids(a, cur, k0, lane);
+        if (btv < 0 || btv >= a.num_blocks) {
+          btv = 0;
+          bad = true;
+        }
+        const int nb = min(kWave, n - k0);
+        const int jfirst = cur.jb + k0;
+        Stage st[NST];
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j)
+          if (j < nb) load(st[j], __builtin_amdgcn_readlane(btv, j));
+        for (int k = 0; k < nb; k += NST) {
+#pragma unroll
+          for (int j = 0; j < NST; ++j) {
+            if (k + j < nb) {
+              if (k + j + NST - 1 < nb) load(st[(j + NST - 1) % NST], __builtin_amdgcn_readlane(btv, k + j + NST - 1));
+              compute(st[j], jfirst + k + j);
+            }
+          }
+        }
+      }
+
+      // Finish: l over the head's four lanes; lane (r16, q4) holds O
+      // elements NDT*(4*q4 + i) + dt of head r16.
+      const bool wave_bad = __any(bad);
+      if (wave_bad && lane == 0) atomicOr(a.err, PKV_DEVERR_BLOCK_ID);
+      const float l = xsum32(xsum16(lsum));
+      if (col_ok) {
+        if (cur.slot0 < 0) {
+          const float inv = wave_bad ? __builtin_nanf("") : 1.f / l;
+          uint16_t* dst = (uint16_t*)a.out + out_row + r16 * D;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t pk[NDT / 2];
+#pragma unroll
+            for (int e = 0; e < NDT / 2; ++e)
+              pk[e] = (uint32_t)f32_to_bf16(oacc[2 * e][i] * inv) | ((uint32_t)f32_to_bf16(oacc[2 * e + 1][i] * inv) << 16);
+            if constexpr (NDT == 8)
+              *(u32x4*)(dst + NDT * (4 * q4 + i)) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            else
+              *(u32x2*)(dst + NDT * (4 * q4 + i)) = u32x2{pk[0], pk[1]};
+          }
+        } else {
+          const size_t sidx = (size_t)(cur.slot0 + cur.part) * a.num_q_heads + cur.h0 + r16;
+          const float nan_or_0 = wave_bad ? __builtin_nanf("") : 0.f;
+          float* dst = a.part_o + sidx * D;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < NDT / 4; ++e)
+              *(float4*)(dst + NDT * (4 * q4 + i) + 4 * e) =
+                  make_float4(oacc[4 * e][i] + nan_or_0, oacc[4 * e + 1][i] + nan_or_0,
+                              oacc[4 * e + 2][i] + nan_or_0, oacc[4 * e + 3][i] + nan_or_0);
+          if (q4 == 0) a.part_ml[sidx] = make_float2(m_ref, l);
+        }
+      }
+    }
+    if (!has_next) break;
+    ++round;
+    nx = nx2;
+    cur = nxt;
+    btv = btv_next;
+  }
+}
+
 // Merge of split-KV partitions: one wave per (row, query head).  With
 // M = max_p m_p and f_p = exp2(m_p - M) (log2 domain), the row's output is
 // sum_p f_p o_p / sum_p f_p l_p, o_p being partition p's un-normalised
@@ -634,12 +849,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void r
 
 // Persistent grid: as many 4-wave workgroups as fit on the device at once,
 // but no more than the work items need.
-template <typename K>
-int64_t persistent_grid(K kernel, int64_t bound_wgs, int cus) {
+// (One cached occupancy per kernel: the template argument is the kernel.)
+template <auto K>
+int64_t persistent_grid(int64_t bound_wgs, int cus) {
   static std::atomic<int> occ_cache{0};
   int occ = occ_cache.load(std::memory_order_relaxed);
   if (occ <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, K, 256, 0) != hipSuccess || occ <= 0)
       occ = 2;
     occ_cache.store(occ, std::memory_order_relaxed);
   }
@@ -649,7 +865,7 @@ int64_t persistent_grid(K kernel, int64_t bound_wgs, int cus) {
 template <bool BF16, int D, int GM>
 int launch_rows_g(const RowParams& p, int64_t bound_waves, int cus, hipStream_t s) {
   auto k = row_attn_kernel<BF16, D, GM>;
-  const int64_t grid = persistent_grid(k, (bound_waves + 3) / 4, cus);
+  const int64_t grid = persistent_grid<row_attn_kernel<BF16, D, GM>>((bound_waves + 3) / 4, cus);
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
@@ -667,10 +883,25 @@ int launch_rows_d(const RowParams& p, int64_t bound_waves, int cus, hipStream_t 
 
 }  // namespace
 
+// bf16 groups wider than kMaxGroupRegs run on row_attn_mfma_kernel, one wave
+// for the whole group (as several waves of 4 heads, each reading the blocks,
+// they measured 7% slower at G = 8); narrower groups and fp32 run on
+// row_attn_kernel, which is as fast or slightly faster there.
+bool rows_on_mfma(int32_t dtype, int32_t group) { return dtype == PKV_BF16 && group > kMaxGroupRegs; }
+
+int max_group_regs(int32_t dtype, int32_t group) { return rows_on_mfma(dtype, group) ? 16 : kMaxGroupRegs; }
+
 int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bound_waves, int cus,
                 hipStream_t stream) {
   if (bound_waves <= 0) return 0;
   const bool bf16 = dtype == PKV_BF16;
+  if (rows_on_mfma(dtype, p.group)) {  // the whole group in one wave (head_groups == 1)
+    auto k = head_dim == 64 ? row_attn_mfma_kernel<64> : row_attn_mfma_kernel<128>;
+    const int64_t grid = head_dim == 64 ? persistent_grid<row_attn_mfma_kernel<64>>((bound_waves + 3) / 4, cus)
+                                        : persistent_grid<row_attn_mfma_kernel<128>>((bound_waves + 3) / 4, cus);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+  }
   if (head_dim == 64) return bf16 ? launch_rows_d<true, 64>(p, bound_waves, cus, stream)
                                   : launch_rows_d<false, 64>(p, bound_waves, cus, stream);
   return bf16 ? launch_rows_d<true, 128>(p, bound_waves, cus, stream)

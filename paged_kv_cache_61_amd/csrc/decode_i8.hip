@@ -301,9 +301,6 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
 // elements are contiguous.  Masked tokens (past the row's position, including
 // unused tail slots whose codes and scales may be garbage or NaN) get p = 0
 // by selection.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Signed byte k of w as float (v_cvt_f32_i32 with a sign-extending byte select).
 template <int K>
@@ -313,23 +310,6 @@ PKV_DEV float sbyte(uint32_t w) {
 // Two integer-valued floats (|x| < 2^8) as a bf16 pair: the top halves (exact).
 PKV_DEV uint32_t ipair(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302);
-}
-// x[l] op x[l ^ 16] and x[l] op x[l ^ 32] (v_permlane16_swap / v_permlane32_swap).
-PKV_DEV float xmax16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-PKV_DEV float xmax32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-PKV_DEV float xsum16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-PKV_DEV float xsum32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 #define PKV_INLINE __attribute__((always_inline))

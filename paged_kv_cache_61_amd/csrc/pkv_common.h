@@ -119,6 +119,29 @@ PKV_DEV float wave_max(float x) {
   return x;
 }
 
+// max / sum of x[l] and x[l ^ 16], and of x[l] and x[l ^ 32], for every lane l
+// (v_permlane16_swap / v_permlane32_swap: VALU, no LDS round trip).
+PKV_DEV float xmax16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+PKV_DEV float xmax32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+PKV_DEV float xsum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+PKV_DEV float xsum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 // Buffer resource over [p, p + bytes); loads past the end return 0.
 constexpr int kRsrcWord3 = 0x00020000;
 PKV_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {

@@ -60,7 +60,6 @@ namespace pkv {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPfRows = 256;   // MFMA rows per workgroup (8 waves x 32)

@@ -52,6 +52,8 @@ SMALL = [
     ("bf16", 128, 32, 8), ("bf16", 128, 12, 4), ("bf16", 64, 16, 1), ("f32", 64, 6, 2),
     ("bf16", 64, 4, 4), ("bf16", 64, 8, 4), ("bf16", 128, 8, 4), ("f32", 64, 4, 4),
     ("f32", 64, 4, 2), ("f32", 128, 8, 4), ("f32", 128, 8, 2), ("f32", 128, 16, 2),
+    # bf16 groups wider than 4 (one wave per group on the matrix cores)
+    ("bf16", 128, 16, 2), ("bf16", 128, 16, 1), ("bf16", 64, 16, 2), ("bf16", 128, 12, 2), ("bf16", 64, 10, 2),
 ]
 
 
