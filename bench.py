@@ -155,6 +155,16 @@ def copy_probe(args):
                       "frac_of_8TBs": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
+def row_kernel_name(wl, kv_int8):
+    """The library kernel that runs the decode rows of this workload."""
+    if kv_int8:
+        return ("row_attn_i8_mfma_kernel (INT8 cache, bf16 q: decode rows + split-KV partitions)"
+                if wl.dtype == "bf16" else "row_attn_i8_kernel (INT8 cache, fp32 q: decode rows + split-KV partitions)")
+    if wl.dtype == "bf16" and wl.num_q_heads // wl.num_kv_heads > 4:
+        return "row_attn_mfma_kernel (decode rows + split-KV partitions, all query heads of a kv head on MFMA)"
+    return "row_attn_kernel (decode rows + split-KV partitions)"
+
+
 def measured_traffic(workload):
     """HBM bytes per row-kernel launch from the committed PMC summary, if it was
     taken on this workload and on the current decode kernel source; else None."""
@@ -327,8 +337,7 @@ def main():
             "kv_cache": "int8 codes + float32 scale per (token, kv head)" if args.kv_int8 else wl.dtype,
         },
         "roofline": {
-            "kernel": ("row_attn_i8_kernel (INT8 cache: decode rows + split-KV partitions)" if args.kv_int8
-                       else "row_attn_kernel (decode rows + split-KV partitions)"),
+            "kernel": row_kernel_name(wl, args.kv_int8),
             "bound": "hbm",
             "achieved": round(rows_gbs, 2),
             "peak": HBM_PEAK_GBS,
