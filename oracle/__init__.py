@@ -105,6 +105,73 @@ def kv_write_int8(codes: np.ndarray, scales: np.ndarray, k: np.ndarray, v: np.nd
     return codes, scales
 
 
+# FP8 KV cache: the same online quantisation per (token, K or V, kv head) row
+# as INT8 (lpnh.cn/news/2436702, section 4.2, "KV Cache 量化"), with codes in
+# the OCP 8-bit floating-point format E4M3 (1 sign, 4 exponent bits with bias
+# 7, 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; no
+# infinities; S.1111.111 is NaN, so the largest finite magnitude is
+# 1.75 * 2^8 = 448).  Reading: scale = max|x| / 448 and code = the E4M3 value
+# nearest to x / scale (float32 quotient, magnitude clipped at 448), ties to
+# the even code; an all-zero row has scale 0 and codes 0.
+
+def fp8_e4m3_magnitudes() -> np.ndarray:
+    """Values of the finite non-negative codes 0x00 .. 0x7e, in code order
+    (increasing), from the format's definition."""
+    out = []
+    for code in range(0x7f):
+        e, m = code >> 3, code & 7
+        out.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(out, np.float64)
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 codes -> float64 values (NaN for 0x7f / 0xff)."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    mags = np.append(fp8_e4m3_magnitudes(), np.nan)
+    v = mags[c & 0x7F]
+    return np.where(c & 0x80, -v, v)
+
+
+def fp8_e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """float32 values -> uint8 codes: the nearest finite E4M3 value to y (|y|
+    clipped at 448), ties to the even code; the sign bit is y's sign bit."""
+    yf = np.asarray(y, np.float32)
+    a = np.minimum(np.abs(yf).astype(np.float64), 448.0)
+    mags = fp8_e4m3_magnitudes()
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, len(mags) - 1)
+    lo = np.clip(hi - 1, 0, len(mags) - 1)
+    dlo, dhi = a - mags[lo], mags[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | np.where(np.signbit(yf), np.uint8(0x80), np.uint8(0))
+
+
+def quantize_fp8(x: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """``x [..., D]`` storage values -> (uint8 E4M3 codes ``[..., D]``, float32 scales ``[...]``)."""
+    xf = to_f64(x, dtype).astype(np.float32)          # exact: bf16 and f32 values are float32
+    amax = np.abs(xf).max(axis=-1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    codes = fp8_e4m3_encode((xf / safe[..., None]).astype(np.float32))
+    codes[scale == 0] = 0
+    return codes, scale
+
+
+def dequantize_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    return fp8_e4m3_decode(codes) * scales.astype(np.float64)[..., None]
+
+
+def kv_write_fp8(codes: np.ndarray, scales: np.ndarray, k: np.ndarray, v: np.ndarray,
+                 slot_mapping: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """FP8 cache write: ``codes [2, NB, 16, Hkv, D]`` uint8 and ``scales
+    [2, NB, 16, Hkv]`` float32, as ``kv_write_int8``."""
+    kc, ks = quantize_fp8(k, dtype)
+    vc, vs = quantize_fp8(v, dtype)
+    codes = kv_write(codes, kc, vc, slot_mapping)
+    scales = kv_write(scales[..., None], ks[..., None], vs[..., None], slot_mapping)[..., 0]
+    return codes, scales
+
+
 # ---------------------------------------------------------------------------
 # paged_kv_write: place each new token's K and V at its slot.
 
@@ -262,6 +329,16 @@ def attention_int8(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, block_t
     """``attention`` over an INT8 cache: the keys and values are the
     dequantised ``code * scale`` (q in ``dtype``)."""
     return attention(to_f64(q, dtype), dequantize_int8(codes, scales), block_table, seq_lens,
+                     query_start_loc, num_computed_tokens, scale, "f64", requests=requests)
+
+
+def attention_fp8(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, block_table: np.ndarray,
+                  seq_lens: np.ndarray, query_start_loc: np.ndarray,
+                  num_computed_tokens: np.ndarray, scale: float, dtype: str,
+                  requests: Optional[Iterable[int]] = None) -> np.ndarray:
+    """``attention`` over an FP8 cache: the keys and values are the
+    dequantised ``decode(code) * scale`` (q in ``dtype``)."""
+    return attention(to_f64(q, dtype), dequantize_fp8(codes, scales), block_table, seq_lens,
                      query_start_loc, num_computed_tokens, scale, "f64", requests=requests)
 
 

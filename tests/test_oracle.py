@@ -548,3 +548,102 @@ def test_int8_attention_equals_plain_on_representable_values():
     got = oracle.attention_int8(case["q"], codes, scales, bt, case["L"], case["qsl"], case["nct"], 0.2, "f32")
     assert np.allclose(got, ref, atol=1e-12, rtol=0)
     assert np.all(scales[:, bt[0, 0]][:, 0] == np.float32(1 / 16))   # max 127/16 over 127
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache: hand-worked decodes and codes from the format's
+# definition, an independent round-to-nearest-even on the float32 bits, the
+# error bound of the rounding, and attention over exactly representable values
+# equals the unquantised oracle.
+
+def test_golden_fp8_e4m3():
+    g = json.load(open(os.path.join(GOLDEN, "fp8_e4m3.json")))
+    for code, val in g["decode"]:
+        got = float(oracle.fp8_e4m3_decode(np.array([int(code, 16)], np.uint8))[0])
+        if val == "nan":
+            assert np.isnan(got)
+        else:
+            assert got == val and np.signbit(got) == np.signbit(val), (code, got, val)
+    x = np.array([r["x"] for r in g["rows"]], np.float32)
+    codes, scales = oracle.quantize_fp8(x, "f32")
+    assert codes.tolist() == [[int(c, 16) for c in r["codes"]] for r in g["rows"]]
+    assert scales.tolist() == [r["scale"] for r in g["rows"]]
+
+
+def _e4m3_rne_bits(y):
+    """Round-to-nearest-even of float32 y (|y| <= 448) to E4M3 by integer
+    arithmetic on the float32 bits: a second construction of the encoding."""
+    out = []
+    for v in np.asarray(y, np.float32).ravel():
+        b = int(np.float32(v).view(np.uint32))
+        sign = (b >> 24) & 0x80
+        a = abs(float(v))
+        if a < 2.0 ** -6:
+            q = a * 512.0                       # subnormal steps of 2^-9
+            n = int(np.floor(q))
+            frac = q - n
+            n += 1 if (frac > 0.5 or (frac == 0.5 and n % 2 == 1)) else 0
+            code = n
+        else:
+            ab = b & 0x7FFFFFFF
+            e = (ab >> 23) - 127 + 7
+            mant = ab & 0x7FFFFF
+            r, rem = mant >> 20, mant & 0xFFFFF
+            r += 1 if (rem > 0x80000 or (rem == 0x80000 and r & 1)) else 0
+            code = (e << 3) + r
+        out.append(sign | code)
+    return np.array(out, np.uint8).reshape(np.shape(y))
+
+
+def test_fp8_encode_matches_bitwise_rne():
+    rng = np.random.default_rng(11)
+    mags = oracle.fp8_e4m3_magnitudes()
+    ties = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)          # every midpoint (exact in float32)
+    rand = (rng.standard_normal(4000) * rng.choice([1e-3, 0.05, 1, 30, 200], 4000)).astype(np.float32)
+    rand = np.clip(rand, -448, 448).astype(np.float32)
+    y = np.concatenate([ties, -ties, mags.astype(np.float32), rand, np.array([0.0, -0.0, 448.0], np.float32)])
+    assert np.array_equal(oracle.fp8_e4m3_encode(y), _e4m3_rne_bits(y))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fp8_rounding_error_bound(dtype):
+    rng = np.random.default_rng(12)
+    x = _draw(rng, (50, 4, 128), dtype)
+    codes, scales = oracle.quantize_fp8(x, dtype)
+    xf = oracle.to_f64(x, dtype)
+    y = np.abs(xf) / np.where(scales > 0, scales, 1)[..., None]
+    # half a step: 2^-4 relative for normals (3 mantissa bits), 2^-10 absolute below 2^-6
+    step = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 1e-300))) - 3), 2.0 ** -9)
+    err = np.abs(oracle.dequantize_fp8(codes, scales) - xf)
+    assert np.all(err <= scales[..., None] * (step / 2 * (1 + 1e-5) + 1e-6) + 1e-30)
+    amax_idx = np.abs(xf).argmax(axis=-1)
+    assert np.all(np.take_along_axis(codes, amax_idx[..., None], -1) & 0x7F == 0x7E)
+    assert not np.any((codes & 0x7F) == 0x7F)
+
+
+def test_fp8_attention_equals_plain_on_representable_values():
+    # values (E4M3 value) * 2^-4 with every row's max exactly 448 * 2^-4:
+    # quantisation is then exact and FP8 attention must equal the plain one
+    rng = np.random.default_rng(13)
+    Hq, Hkv, D = 8, 2, 64
+    reqs = [(30, 1), (0, 20), (60, 5)]
+    mags = oracle.fp8_e4m3_magnitudes()
+    def rep(shape):
+        v = mags[rng.integers(0, 126, shape)] * rng.choice([-1.0, 1.0], shape)
+        v[..., 0] = 448.0
+        return (v / 16).astype(np.float32)
+    Ks = [rep((c + ql, Hkv, D)) for c, ql in reqs]
+    Vs = [rep((c + ql, Hkv, D)) for c, ql in reqs]
+    case = _ragged_case(13, "f32", Hq, Hkv, D, reqs)
+    pool, bt = _scatter_requests(rng, Ks, Vs, [c for c, _ in reqs], Hkv, D, "f32")
+    case = dict(case, Ks=Ks, Vs=Vs, pool=pool, bt=bt)
+    NB = pool.shape[1]
+    codes = np.zeros((2, NB, 16, Hkv, D), np.uint8)
+    scales = np.zeros((2, NB, 16, Hkv), np.float32)
+    for r, (K, V) in enumerate(zip(Ks, Vs)):
+        slots = np.array([bt[r, t // 16] * 16 + t % 16 for t in range(len(K))], np.int64)
+        codes, scales = oracle.kv_write_fp8(codes, scales, K, V, slots, "f32")
+    ref = _run(case, 0.2, "f32")
+    got = oracle.attention_fp8(case["q"], codes, scales, bt, case["L"], case["qsl"], case["nct"], 0.2, "f32")
+    assert np.allclose(got, ref, atol=1e-12, rtol=0)
+    assert np.all(scales[:, bt[0, 0]][:, 0] == np.float32(1 / 16))
