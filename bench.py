@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-int8", action="store_true",
                     help="INT8 KV cache (paged_kv_write_int8 + paged_attention_int8)")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="FP8 (E4M3) KV cache (paged_kv_write_fp8 + paged_attention_fp8)")
     ap.add_argument("--rope", action="store_true",
                     help="write the step's tokens with paged_kv_write_rope (RoPE on K, and on q in place)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
@@ -155,11 +157,13 @@ def copy_probe(args):
                       "frac_of_8TBs": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
-def row_kernel_name(wl, kv_int8):
-    """The library kernel that runs the decode rows of this workload."""
-    if kv_int8:
-        return ("row_attn_i8_mfma_kernel (INT8 cache, bf16 q: decode rows + split-KV partitions)"
-                if wl.dtype == "bf16" else "row_attn_i8_kernel (INT8 cache, fp32 q: decode rows + split-KV partitions)")
+def row_kernel_name(wl, kv8):
+    """The library kernel that runs the decode rows of this workload (kv8:
+    None, "int8" or "fp8")."""
+    if kv8:
+        f = kv8.upper()
+        return (f"row_attn_i8_mfma_kernel ({f} cache, bf16 q: decode rows + split-KV partitions)"
+                if wl.dtype == "bf16" else f"row_attn_i8_kernel ({f} cache, fp32 q: decode rows + split-KV partitions)")
     if wl.dtype == "bf16" and wl.num_q_heads // wl.num_kv_heads > 4:
         return "row_attn_mfma_kernel (decode rows + split-KV partitions, all query heads of a kv head on MFMA)"
     return "row_attn_kernel (decode rows + split-KV partitions)"
@@ -189,6 +193,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.kv_int8 and args.kv_fp8:
+        raise SystemExit("--kv-int8 and --kv-fp8 are separate modes")
+    kv8 = "int8" if args.kv_int8 else "fp8" if args.kv_fp8 else None
 
     import numpy as np
     import torch
@@ -235,30 +242,32 @@ def main():
             e.record()
     torch.cuda.synchronize()
 
-    if args.kv_int8:
+    if kv8:
         if args.rope:
-            raise SystemExit("--kv-int8 and --rope are separate modes")
+            raise SystemExit("--kv-int8 / --kv-fp8 and --rope are separate modes")
+        write8 = pkv.paged_kv_write_int8 if kv8 == "int8" else pkv.paged_kv_write_fp8
+        attend8 = pkv.paged_attention_int8 if kv8 == "int8" else pkv.paged_attention_fp8
         # quantise every slot of the pool once (unused slots hold NaN: their
         # codes and scales are never read)
         nb = pool.shape[1]
-        codes = torch.empty(pool.shape, dtype=torch.int8, device=dev)
+        codes = torch.empty(pool.shape, dtype=torch.int8 if kv8 == "int8" else torch.uint8, device=dev)
         kv_scales = torch.empty(pool.shape[:4], dtype=torch.float32, device=dev)
-        pkv.paged_kv_write_int8(pool[0].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
-                                pool[1].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
-                                torch.arange(nb * 16, dtype=torch.int64, device=dev), codes, kv_scales)
+        write8(pool[0].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
+               pool[1].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
+               torch.arange(nb * 16, dtype=torch.int64, device=dev), codes, kv_scales)
         del pool
         torch.cuda.synchronize()
 
     def step(evs=None):
         if evs is not None:
             evs[2 * nph].record()
-        if args.kv_int8:
-            pkv.paged_kv_write_int8(k_new, v_new, slot_mapping, codes, kv_scales)
+        if kv8:
+            write8(k_new, v_new, slot_mapping, codes, kv_scales)
             if evs is not None:
                 evs[2 * nph + 1].record()
-            pkv.paged_attention_int8(q, codes, kv_scales, bt, sl, qsl, nct, wl.scale,
-                                     max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, out=out,
-                                     workspace=ws, phase_events=None if evs is None else evs[:2 * nph])
+            attend8(q, codes, kv_scales, bt, sl, qsl, nct, wl.scale,
+                    max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, out=out,
+                    workspace=ws, phase_events=None if evs is None else evs[:2 * nph])
             return
         if args.rope:
             pkv.paged_kv_write_rope(k_new, v_new, positions, cos_sin, slot_mapping, pool, q=q)
@@ -308,7 +317,7 @@ def main():
     write_bytes = acct["write_rope_bytes"] if args.rope else acct["write_bytes"]
     step_bytes = acct["step_bytes"] - acct["write_bytes"] + write_bytes
     dec_bytes = acct["decode_bytes"]
-    if args.kv_int8:   # k/v read in their dtype, written as codes + scales
+    if kv8:   # k/v read in their dtype, written as codes + scales
         T_, s_ = wl.num_tokens, 2 if wl.dtype == "bf16" else 4
         write_bytes = 2 * T_ * wl.num_kv_heads * (wl.head_dim * s_ + wl.head_dim + 4) + 8 * T_
         dec_bytes = acct["decode_bytes_int8"]
@@ -334,22 +343,22 @@ def main():
             "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
             "head_dim": wl.head_dim, "block_size": 16, "num_blocks": wl.num_blocks,
             "decode_kv_tokens": acct["decode_kv_tokens"], "max_seq_len": wl.max_seq_len,
-            "kv_cache": "int8 codes + float32 scale per (token, kv head)" if args.kv_int8 else wl.dtype,
+            "kv_cache": (f"{kv8} codes + float32 scale per (token, kv head)" if kv8 else wl.dtype),
         },
         "roofline": {
-            "kernel": row_kernel_name(wl, args.kv_int8),
+            "kernel": row_kernel_name(wl, kv8),
             "bound": "hbm",
             "achieved": round(rows_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if args.kv_int8 else measured_traffic(args.workload),
+            "traffic": None if kv8 else measured_traffic(args.workload),
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": round(phase_ms["rows"], 5),
         },
         "phases_ms": {k: round(v, 5) for k, v in phase_ms.items()},
         "write": {"kernel": ("kv_write_rope_kernel (RoPE on K and q)" if args.rope else
-                             "kv_write_i8_kernel (quantising)" if args.kv_int8 else "kv_write_kernel"),
+                             f"kv_write_i8_kernel ({kv8} quantising)" if kv8 else "kv_write_kernel"),
                   "ms": round(write_ms, 5), "bytes": write_bytes,
                   "GB/s": round(write_bytes / (write_ms * 1e-3) / 1e9, 1) if write_ms > 0 else None},
         "step_algorithmic_bytes": step_bytes,

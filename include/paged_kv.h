@@ -285,6 +285,38 @@ int paged_attention_int8(void* out, const void* q, const void* kv_cache_layer, c
                          void* const* phase_events);
 
 /*
+ * FP8 KV cache: the INT8 cache's layout and per-(token, K or V, kv head)
+ * scales (online KV-cache quantisation, lpnh.cn/news/2436702, section 4.2),
+ * with codes in the OCP 8-bit floating-point format E4M3 (1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, no
+ * infinities; 0x7f / 0xff are NaN and never written):
+ *   kv_cache_layer  uint8 [2][num_blocks][16][num_kv_heads][head_dim] codes,
+ *   kv_scales       float32 [2][num_blocks][16][num_kv_heads] scales,
+ * value = E4M3(code) * scale, with scale = max|x| / 448 and code = the E4M3
+ * value nearest to x / scale (IEEE float32 quotient, magnitude clipped at
+ * 448), ties to the even code, sign bit from the quotient; an all-zero row
+ * has scale 0 and codes 0.
+ *
+ * paged_kv_write_fp8 — quantise and store the step's new K/V, as
+ *   paged_kv_write_int8.
+ * paged_attention_fp8 — paged_attention over such a cache, with the kernels
+ *   of paged_attention_int8: the codes become bf16 (exact) or float32 before
+ *   the products and the scales enter as for INT8.
+ * Arguments, workspace and error conventions are those of the INT8 calls.
+ */
+int paged_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
+                       float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream);
+int paged_attention_fp8(void* out, const void* q, const void* kv_cache_layer, const float* kv_scales,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                        float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                        int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                        int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* phase_events);
+
+/*
  * paged_kv_copy_blocks — copy whole cache blocks (K and V, every kv head):
  * the copy half of copy-on-write prefix sharing (lpnh.cn/news/2436702,
  * section 2.2: sequences share prefix blocks and a block is copied only

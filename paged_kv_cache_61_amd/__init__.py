@@ -14,6 +14,8 @@ Functions keep the C names:
 * ``paged_kv_write_rope(k, v, positions, cos_sin_cache, slot_mapping, kv_cache_layer, ...)``
 * ``paged_kv_write_int8(k, v, slot_mapping, kv_cache_i8, kv_scales)`` and
   ``paged_attention_int8(q, kv_cache_i8, kv_scales, block_table, ...)`` (INT8 cache)
+* ``paged_kv_write_fp8`` / ``paged_attention_fp8`` (FP8 E4M3 cache: uint8 or
+  torch.float8_e4m3fn codes, same arguments)
 * ``paged_kv_copy_blocks(kv_cache_layer, copies)``
 * ``BlockManager`` — the host block manager / step scheduler (``pkv_bm_*``)
 """
@@ -30,7 +32,8 @@ __all__ = [
     "pkv_read_device_error", "pkv_validate_metadata_host", "lib_path", "load_library",
     "DEVERR_SEQ_LEN", "DEVERR_LIMITS", "DEVERR_QSL", "DEVERR_BLOCK_ID", "DEVERR_SLOT",
     "DEVERR_CAPACITY", "DEVERR_POSITION", "BLOCK_SIZE", "paged_kv_copy_blocks", "paged_kv_write_rope",
-    "paged_kv_write_int8", "paged_attention_int8", "BlockManager", "Step",
+    "paged_kv_write_int8", "paged_attention_int8", "paged_kv_write_fp8", "paged_attention_fp8",
+    "BlockManager", "Step",
 ]
 
 BLOCK_SIZE = 16
@@ -100,6 +103,10 @@ def load_library() -> ctypes.CDLL:
     lib.paged_attention_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i64, i32, i32, i32, i32,
                                          i32, i32, i32, i32, vp, sz, vp, vp]
     lib.paged_attention_int8.restype = ctypes.c_int
+    lib.paged_kv_write_fp8.argtypes = lib.paged_kv_write_int8.argtypes
+    lib.paged_kv_write_fp8.restype = ctypes.c_int
+    lib.paged_attention_fp8.argtypes = lib.paged_attention_int8.argtypes
+    lib.paged_attention_fp8.restype = ctypes.c_int
     lib.paged_kv_copy_blocks.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     pbm = ctypes.c_void_p
@@ -129,7 +136,7 @@ EXPORTED_SYMBOLS = ("paged_kv_write", "paged_attention", "paged_attention_profil
                     "paged_attention_workspace_size",
                     "pkv_read_device_error", "pkv_validate_metadata_host", "pkv_status_string",
                     "pkv_last_error_detail", "paged_kv_copy_blocks", "paged_kv_write_rope",
-                    "paged_kv_write_int8", "paged_attention_int8",
+                    "paged_kv_write_int8", "paged_attention_int8", "paged_kv_write_fp8", "paged_attention_fp8",
                     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_request",
                     "pkv_bm_add_request_with_prefix", "pkv_bm_fork", "pkv_bm_append_tokens",
                     "pkv_bm_finish", "pkv_bm_num_free_blocks", "pkv_bm_request_state",
@@ -306,11 +313,17 @@ def paged_kv_write_rope(k: torch.Tensor, v: torch.Tensor, positions: torch.Tenso
         raise PagedKVError(st, "paged_kv_write_rope")
 
 
-def _check_i8_cache(kv_cache: torch.Tensor, kv_scales: torch.Tensor):
-    _check_dev("kv_cache_layer", kv_cache, torch.int8)
+_CODE_DTYPES = {"int8": (torch.int8,), "fp8": (torch.uint8, torch.float8_e4m3fn)}
+
+
+def _check_i8_cache(kv_cache: torch.Tensor, kv_scales: torch.Tensor, fmt: str = "int8"):
+    if kv_cache.dtype not in _CODE_DTYPES[fmt]:
+        raise TypeError(f"kv_cache_layer must have dtype {' or '.join(map(str, _CODE_DTYPES[fmt]))}, "
+                        f"got {kv_cache.dtype}")
+    _check_dev("kv_cache_layer", kv_cache)
     _check_dev("kv_scales", kv_scales, torch.float32)
     if kv_cache.dim() != 5 or kv_cache.shape[0] != 2 or kv_cache.shape[2] != BLOCK_SIZE:
-        raise ValueError("kv_cache_layer must be int8 [2, num_blocks, 16, num_kv_heads, head_dim]")
+        raise ValueError("kv_cache_layer must be [2, num_blocks, 16, num_kv_heads, head_dim] codes")
     if tuple(kv_scales.shape) != tuple(kv_cache.shape[:4]):
         raise ValueError("kv_scales must be float32 [2, num_blocks, 16, num_kv_heads]")
 
@@ -319,7 +332,18 @@ def paged_kv_write_int8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Te
                         kv_cache_layer: torch.Tensor, kv_scales: torch.Tensor,
                         device_error: Optional[torch.Tensor] = None, stream=None) -> None:
     """Quantise ``k, v [T, Hkv, D]`` (bf16 / fp32) into the INT8 cache at ``slot_mapping``."""
-    _check_i8_cache(kv_cache_layer, kv_scales)
+    _kv_write_8bit("int8", k, v, slot_mapping, kv_cache_layer, kv_scales, device_error, stream)
+
+
+def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                       kv_cache_layer: torch.Tensor, kv_scales: torch.Tensor,
+                       device_error: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Quantise ``k, v [T, Hkv, D]`` (bf16 / fp32) into the FP8 (E4M3) cache at ``slot_mapping``."""
+    _kv_write_8bit("fp8", k, v, slot_mapping, kv_cache_layer, kv_scales, device_error, stream)
+
+
+def _kv_write_8bit(fmt, k, v, slot_mapping, kv_cache_layer, kv_scales, device_error, stream):
+    _check_i8_cache(kv_cache_layer, kv_scales, fmt)
     _check_dev("k", k)
     _check_dev("v", v, k.dtype)
     _check_dev("slot_mapping", slot_mapping, torch.int64)
@@ -329,10 +353,11 @@ def paged_kv_write_int8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Te
     T = k.shape[0]
     if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d) or slot_mapping.shape != (T,):
         raise ValueError("k, v must be [T, num_kv_heads, head_dim] and slot_mapping [T]")
-    st = _lib.paged_kv_write_int8(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(kv_cache_layer), _ptr(kv_scales),
-                                  T, nb, hkv, d, _dtype_code(k.dtype), _ptr(device_error), _stream_ptr(stream))
+    fn = getattr(_lib, f"paged_kv_write_{fmt}")
+    st = fn(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(kv_cache_layer), _ptr(kv_scales),
+            T, nb, hkv, d, _dtype_code(k.dtype), _ptr(device_error), _stream_ptr(stream))
     if st != 0:
-        raise PagedKVError(st, "paged_kv_write_int8")
+        raise PagedKVError(st, f"paged_kv_write_{fmt}")
 
 
 def paged_attention_int8(q: torch.Tensor, kv_cache_layer: torch.Tensor, kv_scales: torch.Tensor,
@@ -343,7 +368,29 @@ def paged_attention_int8(q: torch.Tensor, kv_cache_layer: torch.Tensor, kv_scale
                          phase_events=None) -> torch.Tensor:
     """``paged_attention`` over an INT8 cache (``kv_cache_layer`` int8 codes,
     ``kv_scales`` float32 per (token, kv head)); ``q`` / ``out`` bf16 or fp32."""
-    _check_i8_cache(kv_cache_layer, kv_scales)
+    return _attention_8bit("int8", q, kv_cache_layer, kv_scales, block_table, seq_lens, query_start_loc,
+                           num_computed_tokens, scale, max_query_len, max_seq_len, out, workspace, stream,
+                           phase_events)
+
+
+def paged_attention_fp8(q: torch.Tensor, kv_cache_layer: torch.Tensor, kv_scales: torch.Tensor,
+                        block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                        num_computed_tokens: torch.Tensor, scale: float, *, max_query_len: int,
+                        max_seq_len: int, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None,
+                        phase_events=None) -> torch.Tensor:
+    """``paged_attention`` over an FP8 cache (``kv_cache_layer`` E4M3 codes as
+    uint8 or float8_e4m3fn, ``kv_scales`` float32 per (token, kv head));
+    ``q`` / ``out`` bf16 or fp32."""
+    return _attention_8bit("fp8", q, kv_cache_layer, kv_scales, block_table, seq_lens, query_start_loc,
+                           num_computed_tokens, scale, max_query_len, max_seq_len, out, workspace, stream,
+                           phase_events)
+
+
+def _attention_8bit(fmt, q, kv_cache_layer, kv_scales, block_table, seq_lens, query_start_loc,
+                    num_computed_tokens, scale, max_query_len, max_seq_len, out, workspace, stream,
+                    phase_events):
+    _check_i8_cache(kv_cache_layer, kv_scales, fmt)
     _check_dev("q", q)
     for n, x in (("block_table", block_table), ("seq_lens", seq_lens),
                  ("query_start_loc", query_start_loc), ("num_computed_tokens", num_computed_tokens)):
@@ -370,13 +417,14 @@ def paged_attention_int8(q: torch.Tensor, kv_cache_layer: torch.Tensor, kv_scale
             raise ValueError(f"phase_events needs {2 * NUM_PHASES} entries")
         handles = (ctypes.c_void_p * (2 * NUM_PHASES))(
             *[None if e is None else int(e.cuda_event) for e in phase_events])
-    st = _lib.paged_attention_int8(_ptr(out), _ptr(q), _ptr(kv_cache_layer), _ptr(kv_scales), _ptr(block_table),
-                                   _ptr(seq_lens), _ptr(query_start_loc), _ptr(num_computed_tokens),
-                                   float(scale), R, T, hq, hkv, d, nb, max(block_table.shape[1], 1),
-                                   max_query_len, max_seq_len, _dtype_code(q.dtype), _ptr(workspace),
-                                   workspace.numel(), _stream_ptr(stream), handles)
+    fn = getattr(_lib, f"paged_attention_{fmt}")
+    st = fn(_ptr(out), _ptr(q), _ptr(kv_cache_layer), _ptr(kv_scales), _ptr(block_table),
+            _ptr(seq_lens), _ptr(query_start_loc), _ptr(num_computed_tokens),
+            float(scale), R, T, hq, hkv, d, nb, max(block_table.shape[1], 1),
+            max_query_len, max_seq_len, _dtype_code(q.dtype), _ptr(workspace),
+            workspace.numel(), _stream_ptr(stream), handles)
     if st != 0:
-        raise PagedKVError(st, "paged_attention_int8")
+        raise PagedKVError(st, f"paged_attention_{fmt}")
     return out
 
 

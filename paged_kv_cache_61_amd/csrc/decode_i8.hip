@@ -1,11 +1,12 @@
 // Row attention (decode rows, split-KV partitions, and the rows of prefill
-// chunks) over an INT8 KV cache.
+// chunks) over an 8-bit KV cache: INT8 codes, or FP8 codes in the OCP E4M3
+// format (template argument FP8).
 //
-// The cache holds each token's K and V rows, per kv head, as int8 codes with
-// one float32 scale: value = code * scale (online quantisation of the KV
-// cache, lpnh.cn/news/2436702 section 4.2; the rows are quantised as they are
-// written, by paged_kv_write_int8).  Codes [2][num_blocks][16][Hkv][D] int8,
-// scales [2][num_blocks][16][Hkv] float32.  What is computed is the same
+// The cache holds each token's K and V rows, per kv head, as 8-bit codes with
+// one float32 scale: value = code * scale, or E4M3(code) * scale (online
+// quantisation of the KV cache, lpnh.cn/news/2436702 section 4.2; the rows
+// are quantised as they are written, by paged_kv_write_int8 / _fp8).  Codes
+// [2][num_blocks][16][Hkv][D] bytes, scales [2][num_blocks][16][Hkv] float32.  What is computed is the same
 // softmax(q k^T * scale) v over the request's tokens 0 .. position
 // ("AI Infra入门干货总结", sections "Paged Attention" and "Attention
 // (FlashAttention)") with k, v the dequantised rows; work items, split-KV
@@ -16,7 +17,8 @@
 //  * q.k: 4 lanes per token, each over a quarter of head_dim.  A code c is
 //    read as the unsigned byte u = c + 128 (one xor per 4 codes), converted
 //    with v_cvt_f32_ubyte, and sum_d q_d c_d = sum_d q_d u_d - 128 sum_d q_d
-//    (the q sums are taken once per item).  The dot is multiplied by the
+//    (the q sums are taken once per item); E4M3 codes are converted exactly
+//    with v_cvt_pk_f32_fp8 and need no offset.  The dot is multiplied by the
 //    token's K scale; the quad adds finish it on all 4 lanes.
 //  * online softmax in the log2 domain, the row max moving per block.
 //  * p.v: lanes own 4 consecutive head_dim elements of D/4-lane groups; the
@@ -78,7 +80,7 @@ PKV_DEV void ubytes(uint32_t w, float (&f)[4]) {
 }
 
 // fp32 q (bf16 q: row_attn_i8_mfma_kernel).
-template <int D, int GM>
+template <int D, int GM, bool FP8>
 __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const float* __restrict__ kv_scales) {
   constexpr int QPL = D / 4;          // q elements per lane (4 lanes per token)
   constexpr int KLD = QPL / 16;       // 16-byte code loads per lane per block (K)
@@ -168,7 +170,10 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           float f[4];
-          ubytes(s.k[j][c] ^ 0x80808080u, f);
+          if constexpr (FP8)
+            fp8x4(s.k[j][c], f);
+          else
+            ubytes(s.k[j][c] ^ 0x80808080u, f);
 #pragma unroll
           for (int hh = 0; hh < GM; ++hh)
 #pragma unroll
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
       float sc[GM], bm[GM];
 #pragma unroll
       for (int hh = 0; hh < GM; ++hh) {
-        float v = fmaf(-128.f, qsum[hh], x[hh]);
+        float v = FP8 ? x[hh] : fmaf(-128.f, qsum[hh], x[hh]);
         v += dpp_mov<kDppQuadSwap1>(v);
         v += dpp_mov<kDppQuadSwap2>(v);
         sc[hh] = live ? v * (s.sk * a.scale_log2) : -INFINITY;
@@ -208,7 +213,10 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
 #pragma unroll
       for (int j = 0; j < VLD; ++j) {
         float f[4];
-        ubytes(s.v[j] ^ 0x80808080u, f);
+        if constexpr (FP8)
+          fp8x4(s.v[j], f);
+        else
+          ubytes(s.v[j] ^ 0x80808080u, f);
 #pragma unroll
         for (int hh = 0; hh < GM; ++hh) {
           const float pw = my_p[hh * kBlock + j * TPV + vsub];
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int off = VL; off < kWave; off <<= 1) o[hh][e] += __shfl_xor(o[hh][e], off);
-        o[hh][e] = fmaf(-128.f, bsum, o[hh][e]);
+        if constexpr (!FP8) o[hh][e] = fmaf(-128.f, bsum, o[hh][e]);
       }
       if (hh < nh && vsub == 0) {
         const int d0 = 4 * vd;
@@ -293,9 +301,11 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
 //                   codes of the same 4 tokens (lane l: head_dim row l%16 of
 //                   each tile), B = p * v_scale[token] rounded to bf16, taken
 //                   from the S^T registers as they are.
-// The dequantisation is exact (codes are small integers), the scales enter in
-// float32; only p * v_scale is rounded to bf16 (relative 2^-9), as in the
-// bf16-cache kernels.  Each lane's head_dim order inside a k-step is the same
+// The conversion to bf16 is exact (INT8 codes are small integers; every E4M3
+// value is a bf16 value, converted two at a time by
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1, the V bytes of two tokens first
+// paired by v_perm), the scales enter in float32; only p * v_scale is rounded
+// to bf16 (relative 2^-9), as in the bf16-cache kernels.  Each lane's head_dim order inside a k-step is the same
 // permutation for q and the codes (the dot product does not depend on it);
 // head_dim tile dt, MFMA row r holds element (D/16)*r + dt, so a lane's output
 // elements are contiguous.  Masked tokens (past the row's position, including
@@ -307,6 +317,13 @@ template <int K>
 PKV_DEV float sbyte(uint32_t w) {
   return (float)(((int)w << (24 - 8 * K)) >> 24);
 }
+// The two E4M3 codes in the low (HI = false) or high 16 bits of w as a bf16
+// pair (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value is a bf16
+// value, so the conversion is exact).
+template <bool HI>
+PKV_DEV uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 // Two integer-valued floats (|x| < 2^8) as a bf16 pair: the top halves (exact).
 PKV_DEV uint32_t ipair(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302);
@@ -316,7 +333,7 @@ PKV_DEV uint32_t ipair(float lo, float hi) {
 
 constexpr float kRefSlackI8 = 8.f;   // see the reference max above (log2 units)
 
-template <int D, int NST>
+template <int D, int NST, bool FP8>
 __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel(RowParams a, const float* __restrict__ kv_scales) {
   constexpr int NS = D / 32;    // k-steps of S^T
   constexpr int NDT = D / 16;   // head_dim tiles of O^T = code bytes per token per lane
@@ -398,8 +415,12 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const uint32_t c0 = st.k[s >> 1][2 * (s & 1)], c1 = st.k[s >> 1][2 * (s & 1) + 1];
-        const u32x4 ka = {ipair(sbyte<0>(c0), sbyte<1>(c0)), ipair(sbyte<2>(c0), sbyte<3>(c0)),
-                          ipair(sbyte<0>(c1), sbyte<1>(c1)), ipair(sbyte<2>(c1), sbyte<3>(c1))};
+        u32x4 ka;
+        if constexpr (FP8)
+          ka = u32x4{fp8x2_bf16<false>(c0), fp8x2_bf16<true>(c0), fp8x2_bf16<false>(c1), fp8x2_bf16<true>(c1)};
+        else
+          ka = u32x4{ipair(sbyte<0>(c0), sbyte<1>(c0)), ipair(sbyte<2>(c0), sbyte<3>(c0)),
+                     ipair(sbyte<0>(c1), sbyte<1>(c1)), ipair(sbyte<2>(c1), sbyte<3>(c1))};
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
                                                        __builtin_bit_cast(bf16x8_t, qb[s]), sacc, 0, 0, 0);
       }
@@ -437,13 +458,21 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int wd = dt >> 2;
-        float c[4];
+        u32x2 va;
+        if constexpr (FP8) {
+          // byte dt of tokens 0, 1 (and 2, 3) into one 16-bit half, then converted
+          const uint32_t sel = (uint32_t)(dt & 3) | ((uint32_t)(4 + (dt & 3)) << 8) | 0x0c0c0000u;
+          va = u32x2{fp8x2_bf16<false>(__builtin_amdgcn_perm(st.v[1][wd], st.v[0][wd], sel)),
+                     fp8x2_bf16<false>(__builtin_amdgcn_perm(st.v[3][wd], st.v[2][wd], sel))};
+        } else {
+          float c[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t x = st.v[i][wd];
-          c[i] = (dt & 3) == 0 ? sbyte<0>(x) : (dt & 3) == 1 ? sbyte<1>(x) : (dt & 3) == 2 ? sbyte<2>(x) : sbyte<3>(x);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t x = st.v[i][wd];
+            c[i] = (dt & 3) == 0 ? sbyte<0>(x) : (dt & 3) == 1 ? sbyte<1>(x) : (dt & 3) == 2 ? sbyte<2>(x) : sbyte<3>(x);
+          }
+          va = u32x2{ipair(c[0], c[1]), ipair(c[2], c[3])};
         }
-        const u32x2 va = {ipair(c[0], c[1]), ipair(c[2], c[3])};
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, va),
                                                              __builtin_bit_cast(s16x4_t, pb), oacc[dt], 0, 0, 0);
       }
@@ -514,37 +543,37 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
 
 constexpr int kI8Stages = 3;   // register ring of blocks per wave
 
-template <int D>
+template <int D, bool FP8>
 int launch_i8_mfma(const RowParams& p, const float* scales, int64_t bound_waves, int cus, hipStream_t s) {
   static int occ = 0;
-  if (occ <= 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, row_attn_i8_mfma_kernel<D, kI8Stages>, 256, 0) !=
+  if (occ <= 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, row_attn_i8_mfma_kernel<D, kI8Stages, FP8>, 256, 0) !=
                        hipSuccess ||
                    occ <= 0))
     occ = 2;
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((bound_waves + 3) / 4, (int64_t)cus * occ));
-  hipLaunchKernelGGL((row_attn_i8_mfma_kernel<D, kI8Stages>), dim3((unsigned)grid), dim3(256), 0, s, p, scales);
+  hipLaunchKernelGGL((row_attn_i8_mfma_kernel<D, kI8Stages, FP8>), dim3((unsigned)grid), dim3(256), 0, s, p, scales);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <int D, int GM>
+template <int D, int GM, bool FP8>
 int launch_i8_g(const RowParams& p, const float* scales, int64_t bound_waves, int cus, hipStream_t s) {
   // persistent grid: as many 4-wave workgroups as fit at once, no more than the items need
   static int occ = 0;
-  if (occ <= 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, row_attn_i8_kernel<D, GM>, 256, 0) !=
+  if (occ <= 0 && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, row_attn_i8_kernel<D, GM, FP8>, 256, 0) !=
                        hipSuccess ||
                    occ <= 0))
     occ = 2;
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((bound_waves + 3) / 4, (int64_t)cus * occ));
-  hipLaunchKernelGGL((row_attn_i8_kernel<D, GM>), dim3((unsigned)grid), dim3(256), 0, s, p, scales);
+  hipLaunchKernelGGL((row_attn_i8_kernel<D, GM, FP8>), dim3((unsigned)grid), dim3(256), 0, s, p, scales);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <int D>
+template <int D, bool FP8>
 int launch_i8_d(const RowParams& p, const float* scales, int64_t bound_waves, int cus, hipStream_t s) {
   // fp32 q: wider groups arrive split into head groups of 2
   const int gm = p.head_groups > 1 ? 2 : p.group;
-  if (gm <= 1) return launch_i8_g<D, 1>(p, scales, bound_waves, cus, s);
-  if (gm <= 2) return launch_i8_g<D, 2>(p, scales, bound_waves, cus, s);
+  if (gm <= 1) return launch_i8_g<D, 1, FP8>(p, scales, bound_waves, cus, s);
+  if (gm <= 2) return launch_i8_g<D, 2, FP8>(p, scales, bound_waves, cus, s);
   return 1;
 }
 
@@ -552,14 +581,21 @@ int launch_i8_d(const RowParams& p, const float* scales, int64_t bound_waves, in
 
 int max_group_regs_i8(int32_t dtype) { return dtype == PKV_BF16 ? 16 : 2; }
 
-int launch_rows_i8(const RowParams& p, const float* kv_scales, int32_t dtype, int32_t head_dim,
+template <bool FP8>
+int launch_rows_fmt(const RowParams& p, const float* kv_scales, int32_t dtype, int32_t head_dim,
+                    int64_t bound_waves, int cus, hipStream_t stream) {
+  if (dtype == PKV_BF16)  // every group width in one wave (head_groups == 1)
+    return head_dim == 64 ? launch_i8_mfma<64, FP8>(p, kv_scales, bound_waves, cus, stream)
+                          : launch_i8_mfma<128, FP8>(p, kv_scales, bound_waves, cus, stream);
+  if (head_dim == 64) return launch_i8_d<64, FP8>(p, kv_scales, bound_waves, cus, stream);
+  return launch_i8_d<128, FP8>(p, kv_scales, bound_waves, cus, stream);
+}
+
+int launch_rows_i8(const RowParams& p, const float* kv_scales, int32_t dtype, int32_t head_dim, bool fp8,
                    int64_t bound_waves, int cus, hipStream_t stream) {
   if (bound_waves <= 0) return 0;
-  if (dtype == PKV_BF16)  // every group width in one wave (head_groups == 1)
-    return head_dim == 64 ? launch_i8_mfma<64>(p, kv_scales, bound_waves, cus, stream)
-                          : launch_i8_mfma<128>(p, kv_scales, bound_waves, cus, stream);
-  if (head_dim == 64) return launch_i8_d<64>(p, kv_scales, bound_waves, cus, stream);
-  return launch_i8_d<128>(p, kv_scales, bound_waves, cus, stream);
+  return fp8 ? launch_rows_fmt<true>(p, kv_scales, dtype, head_dim, bound_waves, cus, stream)
+             : launch_rows_fmt<false>(p, kv_scales, dtype, head_dim, bound_waves, cus, stream);
 }
 
 }  // namespace pkv

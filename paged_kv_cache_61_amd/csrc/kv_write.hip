@@ -145,15 +145,44 @@ int launch_kv_write_rope(const RopeParams& p, bool bf16, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-// paged_kv_write_int8: quantise each new token's K and V rows, per kv head,
-// to int8 codes with one float32 scale, and store both at the token's slot
-// (online KV-cache quantisation, lpnh.cn/news/2436702 section 4.2).  Per
-// (token, K or V, head) row of head_dim values: scale = max|x| / 127,
-// code = round-half-even(x / scale) clamped to [-127, 127]; an all-zero row
-// gets scale 0 and codes 0.  Both divisions are IEEE float32 so the codes
-// are reproducible.  One wave per row: each lane holds head_dim / 64 values,
-// the row max is a wave reduction, lane 0 stores the scale.
-template <bool BF16, int D>
+// E4M3 code of a float32 y (OCP 8-bit floating point: bias 7, 3 mantissa
+// bits, subnormals m/8 * 2^-6, no infinities, largest finite 448): the
+// nearest E4M3 value to y, magnitude clipped at 448, ties to the even code,
+// sign bit from y.  Below 2^-6 the steps are 2^-9, so the code is
+// round-half-even(|y| * 2^9) (an exact product); above, the float32
+// mantissa is rounded to 3 bits half to even, and a carry moves into the
+// exponent field by the addition.  448 has code 0x7e and nothing rounds past
+// it after the clip, so the NaN code 0x7f never appears.
+PKV_DEV uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t e = (b >> 23) - 127u + 7u;
+    const uint32_t mant = b & 0x7fffffu;
+    uint32_t r = mant >> 20;
+    const uint32_t rem = mant & 0xfffffu;
+    r += (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
+    code = (e << 3) + r;
+  }
+  return sign | code;
+}
+
+// paged_kv_write_int8 / paged_kv_write_fp8: quantise each new token's K and
+// V rows, per kv head, to 8-bit codes with one float32 scale, and store both
+// at the token's slot (online KV-cache quantisation, lpnh.cn/news/2436702
+// section 4.2).  Per (token, K or V, head) row of head_dim values:
+//   INT8: scale = max|x| / 127, code = round-half-even(x / scale) clamped to
+//         [-127, 127];
+//   FP8:  scale = max|x| / 448, code = e4m3_code(x / scale);
+// an all-zero row gets scale 0 and codes 0.  Both divisions are IEEE float32
+// so the codes are reproducible.  One wave per row: each lane holds
+// head_dim / 64 values, the row max is a wave reduction, lane 0 stores the
+// scale.
+template <bool BF16, int D, bool FP8>
 __global__ __launch_bounds__(256) void kv_write_i8_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                           const int64_t* __restrict__ slot_mapping,
                                                           int8_t* __restrict__ cache, float* __restrict__ scales,
@@ -187,10 +216,15 @@ __global__ __launch_bounds__(256) void kv_write_i8_kernel(const void* __restrict
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
     amax = wave_max(amax);
-    const float scale = amax / 127.f;
+    const float scale = amax / (FP8 ? 448.f : 127.f);
     int8_t c[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) c[e] = scale > 0.f ? (int8_t)fminf(fmaxf(rintf(x[e] / scale), -127.f), 127.f) : 0;
+    for (int e = 0; e < E; ++e) {
+      if constexpr (FP8)
+        c[e] = scale > 0.f ? (int8_t)e4m3_code(x[e] / scale) : 0;
+      else
+        c[e] = scale > 0.f ? (int8_t)fminf(fmaxf(rintf(x[e] / scale), -127.f), 127.f) : 0;
+    }
     int8_t* dst = cache + ((size_t)kv * num_slots + slot) * num_kv_heads * D + (size_t)h * D + lane * E;
     if constexpr (E == 2)
       *(uint16_t*)dst = (uint16_t)((uint8_t)c[0] | ((uint16_t)(uint8_t)c[1] << 8));
@@ -202,7 +236,7 @@ __global__ __launch_bounds__(256) void kv_write_i8_kernel(const void* __restrict
 
 int launch_kv_write_i8(const void* k, const void* v, const int64_t* slot_mapping, void* cache, float* scales,
                        int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, bool bf16,
-                       int32_t* device_error, hipStream_t stream) {
+                       bool fp8, int32_t* device_error, hipStream_t stream) {
   if (num_tokens == 0) return 0;
   const int64_t rows = num_tokens * 2 * num_kv_heads;
   int64_t grid = (rows + 3) / 4;
@@ -211,10 +245,17 @@ int launch_kv_write_i8(const void* k, const void* v, const int64_t* slot_mapping
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, k, v, slot_mapping, (int8_t*)cache,
                        scales, num_tokens, num_blocks, num_kv_heads, device_error);
   };
-  if (head_dim == 64)
-    bf16 ? go(kv_write_i8_kernel<true, 64>) : go(kv_write_i8_kernel<false, 64>);
-  else
-    bf16 ? go(kv_write_i8_kernel<true, 128>) : go(kv_write_i8_kernel<false, 128>);
+  if (fp8) {
+    if (head_dim == 64)
+      bf16 ? go(kv_write_i8_kernel<true, 64, true>) : go(kv_write_i8_kernel<false, 64, true>);
+    else
+      bf16 ? go(kv_write_i8_kernel<true, 128, true>) : go(kv_write_i8_kernel<false, 128, true>);
+  } else {
+    if (head_dim == 64)
+      bf16 ? go(kv_write_i8_kernel<true, 64, false>) : go(kv_write_i8_kernel<false, 64, false>);
+    else
+      bf16 ? go(kv_write_i8_kernel<true, 128, false>) : go(kv_write_i8_kernel<false, 128, false>);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -184,8 +184,8 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                           int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
                           int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                          void* const* phase_events, const float* kv_scales = nullptr) {
-  const bool i8 = kv_scales != nullptr;   // int8 cache + per-(token, head) scales
+                          void* const* phase_events, const float* kv_scales = nullptr, bool fp8 = false) {
+  const bool i8 = kv_scales != nullptr;   // 8-bit cache (INT8, or E4M3 when fp8) + per-(token, head) scales
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
   if (num_reqs < 0 || num_tokens < 0)
@@ -261,6 +261,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.q = q;
     fp.cache = kv_cache_layer;
     fp.kv_scales = kv_scales;
+    fp.kv_fp8 = fp8 ? 1 : 0;
     fp.block_table = block_table;
     fp.qsl = query_start_loc;
     fp.nct = num_computed_tokens;
@@ -306,7 +307,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   {
     const int64_t bound_waves = ws.cap_row_items * num_kv_heads * rp.head_groups;
     mark(PKV_PHASE_ROWS, 0);
-    if (i8 ? pkv::launch_rows_i8(rp, kv_scales, dtype, head_dim, bound_waves, cus, s)
+    if (i8 ? pkv::launch_rows_i8(rp, kv_scales, dtype, head_dim, fp8, bound_waves, cus, s)
            : pkv::launch_rows(rp, dtype, head_dim, bound_waves, cus, s))
       return fail(PKV_ERR_LAUNCH, "row launch failed");
     mark(PKV_PHASE_ROWS, 1);
@@ -371,9 +372,24 @@ int paged_attention_int8(void* out, const void* q, const void* kv_cache_layer, c
                         workspace, workspace_bytes, stream, phase_events, kv_scales);
 }
 
-int paged_kv_write_int8(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
-                        float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream) {
+int paged_attention_fp8(void* out, const void* q, const void* kv_cache_layer, const float* kv_scales,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                        float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                        int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                        int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* phase_events) {
+  if (!kv_scales) return fail(PKV_ERR_NULL, "kv_scales is NULL");
+  return attention_impl(out, q, kv_cache_layer, block_table, seq_lens, query_start_loc,
+                        num_computed_tokens, scale, num_reqs, num_tokens, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, max_blocks_per_req, max_query_len, max_seq_len, dtype,
+                        workspace, workspace_bytes, stream, phase_events, kv_scales, true);
+}
+
+static int kv_write_8bit(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
+                         float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream, bool fp8) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
   if (num_tokens < 0) return fail(PKV_ERR_DIMS, "num_tokens %lld < 0", num_tokens);
@@ -387,9 +403,24 @@ int paged_kv_write_int8(const void* k, const void* v, const int64_t* slot_mappin
       !aligned(slot_mapping, 8))
     return fail(PKV_ERR_ALIGN, "k, v, cache must be 16-byte aligned, scales 4-byte, slot_mapping 8-byte");
   if (pkv::launch_kv_write_i8(k, v, slot_mapping, kv_cache_layer, kv_scales, num_tokens, num_blocks, num_kv_heads,
-                              head_dim, dtype == PKV_BF16, device_error, (hipStream_t)stream))
-    return fail(PKV_ERR_LAUNCH, "kv_write_int8 launch: %lld", (long long)hipGetLastError());
+                              head_dim, dtype == PKV_BF16, fp8, device_error, (hipStream_t)stream))
+    return fail(PKV_ERR_LAUNCH, fp8 ? "kv_write_fp8 launch: %lld" : "kv_write_int8 launch: %lld",
+                (long long)hipGetLastError());
   return ok();
+}
+
+int paged_kv_write_int8(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
+                        float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream) {
+  return kv_write_8bit(k, v, slot_mapping, kv_cache_layer, kv_scales, num_tokens, num_blocks, num_kv_heads,
+                       head_dim, dtype, device_error, stream, false);
+}
+
+int paged_kv_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
+                       float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream) {
+  return kv_write_8bit(k, v, slot_mapping, kv_cache_layer, kv_scales, num_tokens, num_blocks, num_kv_heads,
+                       head_dim, dtype, device_error, stream, true);
 }
 
 int32_t pkv_read_device_error(const void* workspace, void* stream) {

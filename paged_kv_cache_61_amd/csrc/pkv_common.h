@@ -138,6 +138,17 @@ PKV_DEV float xsum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The 4 OCP E4M3 codes of w (byte order) as float (v_cvt_pk_f32_fp8: every
+// E4M3 value is a float32 value, so the conversion is exact).
+PKV_DEV void fp8x4(uint32_t w, float (&f)[4]) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  f[0] = lo.x;
+  f[1] = lo.y;
+  f[2] = hi.x;
+  f[3] = hi.y;
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

@@ -69,7 +69,8 @@ struct PrefillParams {
   const int4* items;
   int32_t* hdr;
   int32_t* err;
-  const float* kv_scales;  // int8 cache: [2][num_blocks][16][num_kv_heads] scales; else nullptr
+  const float* kv_scales;  // 8-bit cache: [2][num_blocks][16][num_kv_heads] scales; else nullptr
+  int32_t kv_fp8;          // 8-bit cache codes: 0 INT8, 1 OCP E4M3
   float scale_log2;
   int32_t num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_req;
 };
@@ -95,10 +96,11 @@ int launch_kv_write_rope(const RopeParams& p, bool bf16, hipStream_t stream);
 
 int launch_kv_write_i8(const void* k, const void* v, const int64_t* slot_mapping, void* cache, float* scales,
                        int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, bool bf16,
-                       int32_t* device_error, hipStream_t stream);
-// Row kernel over an int8 cache (decode_i8.hip); query heads per wave:
+                       bool fp8, int32_t* device_error, hipStream_t stream);
+// Row kernels over an 8-bit (INT8 or FP8 E4M3) cache (decode_i8.hip); query
+// heads per wave:
 int max_group_regs_i8(int32_t dtype);
-int launch_rows_i8(const RowParams& p, const float* kv_scales, int32_t dtype, int32_t head_dim,
+int launch_rows_i8(const RowParams& p, const float* kv_scales, int32_t dtype, int32_t head_dim, bool fp8,
                    int64_t bound_waves, int cus, hipStream_t stream);
 
 int launch_kv_copy_blocks(void* cache, const int32_t* copies, int32_t num_copies, int32_t num_blocks,

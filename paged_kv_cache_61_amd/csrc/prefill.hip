@@ -71,10 +71,11 @@ constexpr int kHalfTile = kPfKeys * kRowB;  // K or V part of a tile: 16 KiB
 constexpr int kStage = 2 * kHalfTile;       // one ring slot: K then V
 constexpr int kStages = 4;                  // ring slots: tiles t-1 (PV), t (QK), t+1 and t+2 (in flight)
 constexpr int kKSteps = kD / 16;            // Q.K k-steps
-// INT8 cache: the copies bring codes (128-byte rows) and per-row scales into
-// a 4-slot ring, three tiles ahead; every period the waves dequantise K(t+1)
-// and V(t) (code * scale, rounded to bf16) into two K and two V tiles laid
-// out like the bf16 ring's halves, which the MFMA phases read.
+// 8-bit cache (INT8 or FP8 E4M3 codes): the copies bring codes (128-byte
+// rows) and per-row scales into a 4-slot ring, three tiles ahead; every
+// period the waves dequantise K(t+1) and V(t) (value * scale in float32,
+// rounded to bf16) into two K and two V tiles laid out like the bf16 ring's
+// halves, which the MFMA phases read.
 constexpr int kRowB8 = kD;                        // bytes of one int8 key row
 constexpr int kHalf8 = kPfKeys * kRowB8;          // codes of K or V of a tile: 8 KiB
 constexpr int kScl = kPfKeys * 4;                 // scales of K or V of a tile
@@ -212,7 +213,7 @@ PKV_DEV u32x4 buffer_desc(const void* base, uint32_t bytes) {
 
 // The metadata arrays are passed on their own as restrict pointers so their
 // wave-uniform reads become scalar loads, which never wait on the tile stream.
-template <bool I8>
+template <bool I8, bool FP8>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     PrefillParams a, const int4* __restrict__ items, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ nct, const int32_t* __restrict__ block_table) {
@@ -398,9 +399,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     uint32_t o[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const int x = (int)cw[d];
-      o[2 * d] = pack_bf16((float)((x << 24) >> 24) * sc, (float)((x << 16) >> 24) * sc);
-      o[2 * d + 1] = pack_bf16((float)((x << 8) >> 24) * sc, (float)(x >> 24) * sc);
+      if constexpr (FP8) {
+        float f[4];
+        fp8x4(cw[d], f);
+        o[2 * d] = pack_bf16(f[0] * sc, f[1] * sc);
+        o[2 * d + 1] = pack_bf16(f[2] * sc, f[3] * sc);
+      } else {
+        const int x = (int)cw[d];
+        o[2 * d] = pack_bf16((float)((x << 24) >> 24) * sc, (float)((x << 16) >> 24) * sc);
+        o[2 * d + 1] = pack_bf16((float)((x << 8) >> 24) * sc, (float)(x >> 24) * sc);
+      }
     }
     char* dst = lds + kConv + (2 * kv + (tile & 1)) * kHalfTile;
     *(u32x4*)(dst + cv_w0) = u32x4{o[0], o[1], o[2], o[3]};
@@ -675,12 +683,8 @@ int prefill_tile_rows(int32_t group) { return kPfRows / (group > 0 ? group : 1);
 
 int launch_prefill(const PrefillParams& p, int32_t head_dim, int64_t grid, hipStream_t stream) {
   if (head_dim != kD || grid <= 0) return 1;
-  if (p.kv_scales)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.qsl,
-                       p.nct, p.block_table);
-  else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items,
-                       p.qsl, p.nct, p.block_table);
+  auto k = !p.kv_scales ? prefill_kernel<false, false> : p.kv_fp8 ? prefill_kernel<true, true> : prefill_kernel<true, false>;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.qsl, p.nct, p.block_table);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
