@@ -91,10 +91,6 @@ PKV_DEV float chunk_dot<false>(const u32x4& q, const u32x4& k, float acc) {
   return acc;
 }
 
-PKV_DEV void unpack_v(uint32_t x, float& v0, float& v1) {
-  v0 = bf16_lo(x);
-  v1 = bf16_hi(x);
-}
 PKV_DEV void unpack_v(u32x2 x, float& v0, float& v1) {
   v0 = __uint_as_float(x.x);
   v1 = __uint_as_float(x.y);
