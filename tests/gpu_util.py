@@ -103,3 +103,61 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -
     assert stats["nan"] == 0 and not np.isnan(err).any(), f"{what}: NaN in output"
     assert stats["max_abs"] <= tol, f"{what}: max abs err {stats['max_abs']} > {tol}"
     return stats
+
+
+def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
+    """An 8-bit cache (``fmt`` "int8" or "fp8") at a benchmark workload's full
+    size, in the benchmark's launch configuration: the whole pool quantised on
+    the device, the step's tokens written, one attention call.  Checked on a
+    sample: the codes and scales of every block the sampled rows read, bit for
+    bit against the oracle's quantisation of the same (written) pool, and the
+    sampled rows against the oracle's attention over those dequantised blocks."""
+    import paged_kv_cache_61_amd as pkv
+    write8 = pkv.paged_kv_write_int8 if fmt == "int8" else pkv.paged_kv_write_fp8
+    attend8 = pkv.paged_attention_int8 if fmt == "int8" else pkv.paged_attention_fp8
+    quant = oracle.quantize_int8 if fmt == "int8" else oracle.quantize_fp8
+    deq = oracle.dequantize_int8 if fmt == "int8" else oracle.dequantize_fp8
+    wl = workloads.build(workloads.CONFIGS[n])
+    print(f"[case] {fmt} config {n}: {wl.spec.name}", flush=True)
+    s = upload(wl)
+    NB, Hkv, D = wl.num_blocks, wl.num_kv_heads, wl.head_dim
+    codes = torch.empty(tuple(s.pool.shape), dtype=torch.int8 if fmt == "int8" else torch.uint8, device="cuda")
+    scales = torch.empty(tuple(s.pool.shape[:4]), dtype=torch.float32, device="cuda")
+    write8(s.pool[0].reshape(NB * 16, Hkv, D).contiguous(), s.pool[1].reshape(NB * 16, Hkv, D).contiguous(),
+           torch.arange(NB * 16, dtype=torch.int64, device="cuda"), codes, scales)
+    del s.pool
+    write8(s.k_new, s.v_new, s.slot_mapping, codes, scales)
+    attend8(s.q, codes, scales, s.block_table, s.seq_lens, s.qsl, s.nct, wl.scale,
+            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, out=s.out, workspace=s.workspace)
+    torch.cuda.synchronize()
+    assert device_error(s) == 0
+    # sampled rows and the blocks they read
+    rng = np.random.default_rng(seed)
+    qsl, ql = wl.query_start_loc, np.diff(wl.query_start_loc)
+    rows = []
+    for r in np.nonzero(ql > 1)[0][:4]:  # prefill chunks: first, last and random rows
+        rows += [int(qsl[r]), int(qsl[r + 1]) - 1] + rng.integers(qsl[r], qsl[r + 1], 10).tolist()
+    dec = np.nonzero(ql == 1)[0]
+    rows += [int(qsl[r]) for r in rng.choice(dec, min(48, len(dec)), replace=False)]
+    rows = sorted(set(rows))
+    reqs = sorted({int(np.searchsorted(qsl, t, side="right") - 1) for t in rows})
+    blocks = sorted({int(b) for r in reqs for b in wl.block_table[r, :(int(wl.seq_lens[r]) + 15) // 16]})
+    ref_pool = oracle_pool(wl)[:, blocks]                         # [2, nsub, 16, Hkv, D]
+    with np.errstate(invalid="ignore"):
+        live = ~np.isnan(oracle.to_f64(ref_pool, wl.dtype)).any(axis=-1)   # unused slots are NaN
+    rc, rs = quant(np.where(live[..., None], ref_pool, 0).astype(ref_pool.dtype), wl.dtype)
+    idx = torch.tensor(blocks, dtype=torch.int64, device="cuda")
+    gc = codes.index_select(1, idx).cpu().numpy()
+    gs = scales.index_select(1, idx).cpu().numpy()
+    assert np.array_equal(gc[live], rc[live]), "codes differ"
+    assert gs[live].tobytes() == rs[live].tobytes(), "scales differ"
+    # attention over the dequantised blocks (block ids remapped to the subset)
+    remap = {b: i for i, b in enumerate(blocks)}
+    bt = np.zeros_like(wl.block_table)
+    for r in reqs:
+        nb_r = (int(wl.seq_lens[r]) + 15) // 16
+        bt[r, :nb_r] = [remap[int(b)] for b in wl.block_table[r, :nb_r]]
+    pool_deq = np.where(live[..., None], deq(rc, rs), 0.0)
+    ref = oracle.attention_rows(oracle.to_f64(wl.q, wl.dtype), pool_deq, bt, wl.seq_lens, qsl,
+                                wl.num_computed_tokens, wl.scale, "f64", tokens=rows)
+    assert_close(out_f64(s.out)[rows], ref, wl.dtype, f"{fmt} config {n} sampled")

@@ -174,3 +174,11 @@ def test_fp8_write_zero_rows_negative_zero_and_padding():
     assert np.array_equal(d_codes.cpu().numpy(), rc) and d_scales.cpu().numpy().tobytes() == rs.tobytes()
     assert rs[0, 1, 1].tolist() == [0.0, 0.0]
     assert (rc[0, 2, 8, 0, :5] == 0x80).all()
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_fp8_config_full_sampled(n):
+    # the benchmark's decode and mixed-step workloads at full size, sampled
+    _gpu()
+    from gpu_util import eightbit_full_sampled
+    eightbit_full_sampled("fp8", n, 70 + n)

@@ -136,3 +136,11 @@ def test_int8_write_zero_rows_and_padding():
     rc, rs = oracle.kv_write_int8(codes, scales, k, v, slots, "f32")
     assert np.array_equal(d_codes.cpu().numpy(), rc) and d_scales.cpu().numpy().tobytes() == rs.tobytes()
     assert rs[0, 1, 1].tolist() == [0.0, 0.0]
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_int8_config_full_sampled(n):
+    # the benchmark's decode and mixed-step workloads at full size, sampled
+    _gpu()
+    from gpu_util import eightbit_full_sampled
+    eightbit_full_sampled("int8", n, 70 + n)
