@@ -111,3 +111,43 @@ def test_attention_after_write_rope_matches_oracle():
     ref = oracle.attention(q_rot, ref_pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
                            wl.num_computed_tokens, wl.scale, dtype)
     assert_close(out_f64(out), ref, dtype, "attention after fused RoPE write")
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_write_rope_config_full_sampled(n):
+    # the benchmark's decode and mixed-step workloads at full size, written
+    # with the fused RoPE as `bench.py --rope` does (rotary_dim = head_dim,
+    # neox pairs, positions num_computed_tokens + i): every rotated K and q
+    # row against the oracle's rotation, then sampled attention rows
+    _gpu()
+    import paged_kv_cache_61_amd as pkv
+    from gpu_util import device_error, run_attention, upload
+    wl = workloads.build(workloads.CONFIGS[n])
+    print(f"[case] rope config {n}: {wl.spec.name}", flush=True)
+    dtype, D = wl.dtype, wl.head_dim
+    pos = np.concatenate([np.arange(int(wl.num_computed_tokens[r]), int(wl.seq_lens[r]))
+                          for r in range(wl.num_reqs)]).astype(np.int64)
+    cache = _cache(wl.max_seq_len + 1, D)
+    s = upload(wl)
+    pkv.paged_kv_write_rope(s.k_new, s.v_new, torch.from_numpy(pos).cuda(), torch.from_numpy(cache).cuda(),
+                            s.slot_mapping, s.pool, q=s.q)
+    run_attention(s)
+    torch.cuda.synchronize()
+    assert device_error(s) == 0
+    k_rot = oracle.rope(wl.k_new, pos, cache, D, True, dtype)
+    q_rot = oracle.rope(wl.q, pos, cache, D, True, dtype)
+    assert_close(_f64(from_dev(s.q), dtype), q_rot, dtype, "q rotated in place")
+    sb, so = wl.slot_mapping // 16, wl.slot_mapping % 16
+    got_k = from_dev(s.pool[0][torch.from_numpy(sb).cuda(), torch.from_numpy(so).cuda()])
+    assert_close(_f64(got_k, dtype), k_rot, dtype, "K rotated into the cache")
+    assert from_dev(s.pool[1][torch.from_numpy(sb).cuda(), torch.from_numpy(so).cuda()]).tobytes() == \
+        np.ascontiguousarray(wl.v_new).tobytes()
+    rng = np.random.default_rng(80 + n)
+    rows = sorted(set(rng.integers(0, wl.num_tokens, 96).tolist()))
+    qsl = wl.query_start_loc
+    for r in np.nonzero(np.diff(qsl) > 1)[0][:4]:
+        rows = sorted(set(rows + [int(qsl[r]), int(qsl[r + 1]) - 1]))
+    ref_pool = oracle.kv_write(wl.pool, oracle.round_to_storage(k_rot, dtype), wl.v_new, wl.slot_mapping)
+    ref = oracle.attention_rows(oracle.round_to_storage(q_rot, dtype), ref_pool, wl.block_table, wl.seq_lens, qsl,
+                                wl.num_computed_tokens, wl.scale, dtype, tokens=rows)
+    assert_close(out_f64(s.out)[rows], ref, dtype, f"attention after the fused RoPE write, config {n}")
