@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain device-to-device copy of known size instead (HBM calibration)")
     ap.add_argument("--copy-gib", type=float, default=4.0)
+    ap.add_argument("--block-manager", action="store_true",
+                    help="time the host block manager building the mixed step's metadata instead (CPU only)")
     return ap.parse_args()
 
 
@@ -157,6 +159,66 @@ def copy_probe(args):
                       "frac_of_8TBs": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
+def block_manager_probe(args):
+    """Host cost of the C++ block manager (pkv_bm_*) for the mixed continuous-
+    batching step's shape: 2048 running decodes with contexts U[256, 2048]
+    plus 3 new 2048-token prompts (one sharing a 256-token prefix), token
+    budget 8192.  Times one pkv_bm_schedule + pkv_bm_commit pair per step (the
+    C calls only, outputs preallocated), after the appends of the step's
+    generated tokens."""
+    import ctypes
+    import time
+    import numpy as np
+    import paged_kv_cache_61_amd as pkv
+    lib = pkv._lib
+    NB, MB, S, BUDGET, MAXLEN = 200000, 512, 2051 + 8, 8192, 8192
+    bm = pkv.BlockManager(NB, MB)
+    rng = np.random.default_rng(4)
+    for r, L in enumerate(rng.integers(256, 2049, 2048)):
+        bm.add_request(r, int(L))
+    while True:   # prefill every prompt (chunked) so the 2048 requests are decoding
+        st = bm.schedule(S, BUDGET, MAXLEN)
+        bm.commit()
+        if st.max_query_len <= 1:
+            break
+    buf = dict(req_ids=np.zeros(S, np.int64), qsl=np.zeros(S + 1, np.int32), sl=np.zeros(S, np.int32),
+               nct=np.zeros(S, np.int32), bt=np.zeros((S, MB), np.int32), sm=np.zeros(BUDGET, np.int64),
+               cp=np.zeros((S, 2), np.int32))
+    p = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+    step = pkv._PkvStep(S, BUDGET, MAXLEN, p(buf["req_ids"]), p(buf["qsl"]), p(buf["sl"]), p(buf["nct"]),
+                        p(buf["bt"]), p(buf["sm"]), p(buf["cp"]), 0, 0, 0, 0, 0)
+    times, kinds = [], []
+    nxt = 2048
+    for it in range(args.warmup + args.steps):
+        for r in range(2048):
+            bm.append_tokens(r, 1)
+        if it % 8 == 0:   # new prompts arrive: three 2048-token requests, one with a shared prefix
+            bm.add_request(nxt, 2048)
+            bm.add_request(nxt + 1, 2048, prefix_from=0, prefix_tokens=256)
+            bm.add_request(nxt + 2, 2048)
+            new = [nxt, nxt + 1, nxt + 2]
+            nxt += 3
+        t0 = time.perf_counter()
+        rc = lib.pkv_bm_schedule(bm._h, ctypes.byref(step))
+        rc |= lib.pkv_bm_commit(bm._h)
+        dt = time.perf_counter() - t0
+        if rc != 0:
+            raise SystemExit(f"block manager call failed: {rc}")
+        if it % 8 == 7:
+            for r in new:
+                bm.finish(r)
+        if it >= args.warmup:
+            times.append(dt)
+            kinds.append(step.max_query_len > 1)
+    t = np.array(times) * 1e6
+    mixed = t[np.array(kinds)] if any(kinds) else t
+    print(json.dumps({"probe": "host block manager: pkv_bm_schedule + pkv_bm_commit per step",
+                      "requests": int(step.num_reqs), "step_tokens": int(step.num_tokens),
+                      "us_per_step_median": round(float(np.median(t)), 1),
+                      "us_per_mixed_step_median": round(float(np.median(mixed)), 1),
+                      "us_per_step_max": round(float(t.max()), 1), "steps": len(t)}), flush=True)
+
+
 def row_kernel_name(wl, kv8):
     """The library kernel that runs the decode rows of this workload (kv8:
     None, "int8" or "fp8")."""
@@ -187,6 +249,9 @@ def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args)
+        return
+    if args.block_manager:
+        block_manager_probe(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
