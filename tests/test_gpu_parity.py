@@ -190,10 +190,15 @@ def test_single_token_context_returns_v(dtype):
 # ---------------------------------------------------------------------------
 # bad metadata is reported, never faults, and poisons only its own rows
 
-def test_bad_metadata_sets_error_and_nan_rows():
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("f32", 4, 2, 64), ("bf16", 8, 2, 128), ("bf16", 16, 2, 128),
+                                            ("bf16", 32, 2, 64)])
+def test_bad_metadata_sets_error_and_nan_rows(dtype, Hq, Hkv, D):
+    # every row kernel (VALU groups of <= 4 heads, the MFMA kernel for wider
+    # bf16 groups) turns bad metadata into NaN rows of that request only,
+    # split-KV partitions included
     import paged_kv_cache_61_amd as pkv
-    reqs = [(40, 1), (10, 3), (100, 1)]
-    wl = workloads.build(workloads.small_spec("bad", 25, "f32", 4, 2, 64, reqs))
+    reqs = [(40, 1), (10, 3), (100, 1), (1200, 1)]
+    wl = workloads.build(workloads.small_spec("bad", 25, dtype, Hq, Hkv, D, reqs))
     s = upload(wl)
     run_write(s)
     good = out_f64(run_attention(s))
@@ -207,7 +212,7 @@ def test_bad_metadata_sets_error_and_nan_rows():
     err = device_error(s2)
     assert err & pkv.DEVERR_SEQ_LEN
     assert np.isnan(out[1:4]).all()
-    assert np.array_equal(out[[0, 4]], good[[0, 4]])
+    assert np.array_equal(out[[0, 4, 5]], good[[0, 4, 5]])
     # request 2: a block id outside the pool
     s3 = upload(wl)
     run_write(s3)
@@ -217,7 +222,17 @@ def test_bad_metadata_sets_error_and_nan_rows():
     out = out_f64(run_attention(s3))
     assert device_error(s3) & pkv.DEVERR_BLOCK_ID
     assert np.isnan(out[4]).all()
-    assert np.array_equal(out[:4], good[:4])
+    assert np.array_equal(out[[0, 1, 2, 3, 5]], good[[0, 1, 2, 3, 5]])
+    # request 3 (three 512-token partitions): a bad id in the middle one
+    s4 = upload(wl)
+    run_write(s4)
+    bt = s4.block_table.clone()
+    bt[3, 40] = -7
+    s4.block_table = bt
+    out = out_f64(run_attention(s4))
+    assert device_error(s4) & pkv.DEVERR_BLOCK_ID
+    assert np.isnan(out[5]).all()
+    assert np.array_equal(out[:5], good[:5])
 
 
 def test_write_skips_padding_and_bad_slots():
