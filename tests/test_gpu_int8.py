@@ -105,16 +105,17 @@ def test_int8_prefill_bad_block_id_confined_to_its_request():
     # requests' rows into NaN
     _gpu()
     import paged_kv_cache_61_amd as pkv
-    reqs = [(9000, 70), (500, 100), (20, 1), (300, 50)]
+    reqs = [(9000, 70), (500, 100), (20, 1), (300, 50), (2000, 1)]
     wl = workloads.build(workloads.small_spec("int8 prefill bad id", 58, "bf16", 16, 4, 128, reqs))
     good, *_ = _run(wl, "bf16")
     bt = wl.block_table.copy()
     bt[0, 4 * 130 + 1] = wl.num_blocks + 3
     bt[1, 5] = -2
+    bt[4, 70] = wl.num_blocks + 9     # a decode row: the third of its four 512-token partitions
     out, *_ = _run(wl, "bf16", block_table=bt, expect_error=pkv.DEVERR_BLOCK_ID)
     o, gd = out_f64(out), out_f64(good)
-    assert np.isnan(o[0:170]).all()
-    assert np.array_equal(o[170:], gd[170:])
+    assert np.isnan(o[0:170]).all() and np.isnan(o[221]).all()
+    assert np.array_equal(o[170:221], gd[170:221])
 
 
 def test_int8_write_zero_rows_and_padding():
