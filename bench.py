@@ -269,7 +269,7 @@ def main():
     import workloads
 
     t_gen = time.perf_counter()
-    wl = workloads.build(workloads.CONFIGS[args.workload])
+    wl = workloads.build(workloads.BENCH_WORKLOADS[args.workload])
     gen_s = time.perf_counter() - t_gen
     acct = accounting(wl)
 

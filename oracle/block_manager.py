@@ -24,7 +24,7 @@ What it models, and where each rule comes from:
   budget, the model's maximum length, and the free blocks (same page, same
   section, "4个硬性约束").
 
-Readings where the pages are silent (each is stated in the design doc):
+Readings where the pages are silent:
 
 * Requests are served first come, first served; a request that cannot get a
   block this step is skipped (it waits; no preemption), and later requests may

@@ -117,8 +117,8 @@ def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
     attend8 = pkv.paged_attention_int8 if fmt == "int8" else pkv.paged_attention_fp8
     quant = oracle.quantize_int8 if fmt == "int8" else oracle.quantize_fp8
     deq = oracle.dequantize_int8 if fmt == "int8" else oracle.dequantize_fp8
-    wl = workloads.build(workloads.CONFIGS[n])
-    print(f"[case] {fmt} config {n}: {wl.spec.name}", flush=True)
+    wl = workloads.build(workloads.BENCH_WORKLOADS[n])
+    print(f"[case] {fmt} workload {n}: {wl.spec.name}", flush=True)
     s = upload(wl)
     NB, Hkv, D = wl.num_blocks, wl.num_kv_heads, wl.head_dim
     codes = torch.empty(tuple(s.pool.shape), dtype=torch.int8 if fmt == "int8" else torch.uint8, device="cuda")
@@ -160,4 +160,4 @@ def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
     pool_deq = np.where(live[..., None], deq(rc, rs), 0.0)
     ref = oracle.attention_rows(oracle.to_f64(wl.q, wl.dtype), pool_deq, bt, wl.seq_lens, qsl,
                                 wl.num_computed_tokens, wl.scale, "f64", tokens=rows)
-    assert_close(out_f64(s.out)[rows], ref, wl.dtype, f"{fmt} config {n} sampled")
+    assert_close(out_f64(s.out)[rows], ref, wl.dtype, f"{fmt} workload {n} sampled")

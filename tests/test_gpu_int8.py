@@ -140,7 +140,7 @@ def test_int8_write_zero_rows_and_padding():
 
 
 @pytest.mark.parametrize("n", [2, 4])
-def test_int8_config_full_sampled(n):
+def test_int8_workload_full_sampled(n):
     # the benchmark's decode and mixed-step workloads at full size, sampled
     _gpu()
     from gpu_util import eightbit_full_sampled

@@ -77,14 +77,14 @@ def test_edge_lengths():
 # the benchmark workloads
 
 @pytest.mark.parametrize("n", [1, 2, 3, 5])
-def test_config_full(n):
-    wl = workloads.build(workloads.CONFIGS[n])
-    _full_step(wl, f"config {n}: {wl.spec.name}")
+def test_workload_full(n):
+    wl = workloads.build(workloads.BENCH_WORKLOADS[n])
+    _full_step(wl, f"workload {n}: {wl.spec.name}")
 
 
-def test_config4_mixed_step_sampled():
-    wl = workloads.build(workloads.CONFIGS[4])
-    what = "config 4 mixed step"
+def test_workload4_mixed_step_sampled():
+    wl = workloads.build(workloads.BENCH_WORKLOADS[4])
+    what = "workload 4 mixed step"
     print(f"[case] {what}", flush=True)
     s = upload(wl)
     run_write(s)

@@ -114,7 +114,7 @@ def test_attention_after_write_rope_matches_oracle():
 
 
 @pytest.mark.parametrize("n", [2, 4])
-def test_write_rope_config_full_sampled(n):
+def test_write_rope_workload_full_sampled(n):
     # the benchmark's decode and mixed-step workloads at full size, written
     # with the fused RoPE as `bench.py --rope` does (rotary_dim = head_dim,
     # neox pairs, positions num_computed_tokens + i): every rotated K and q
@@ -122,8 +122,8 @@ def test_write_rope_config_full_sampled(n):
     _gpu()
     import paged_kv_cache_61_amd as pkv
     from gpu_util import device_error, run_attention, upload
-    wl = workloads.build(workloads.CONFIGS[n])
-    print(f"[case] rope config {n}: {wl.spec.name}", flush=True)
+    wl = workloads.build(workloads.BENCH_WORKLOADS[n])
+    print(f"[case] rope workload {n}: {wl.spec.name}", flush=True)
     dtype, D = wl.dtype, wl.head_dim
     pos = np.concatenate([np.arange(int(wl.num_computed_tokens[r]), int(wl.seq_lens[r]))
                           for r in range(wl.num_reqs)]).astype(np.int64)
@@ -150,4 +150,4 @@ def test_write_rope_config_full_sampled(n):
     ref_pool = oracle.kv_write(wl.pool, oracle.round_to_storage(k_rot, dtype), wl.v_new, wl.slot_mapping)
     ref = oracle.attention_rows(oracle.round_to_storage(q_rot, dtype), ref_pool, wl.block_table, wl.seq_lens, qsl,
                                 wl.num_computed_tokens, wl.scale, dtype, tokens=rows)
-    assert_close(out_f64(s.out)[rows], ref, dtype, f"attention after the fused RoPE write, config {n}")
+    assert_close(out_f64(s.out)[rows], ref, dtype, f"attention after the fused RoPE write, workload {n}")

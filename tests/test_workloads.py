@@ -37,9 +37,9 @@ def _check_structure(wl):
     assert wl.k_new.shape == wl.v_new.shape == (T, wl.num_kv_heads, wl.head_dim)
 
 
-def test_tiny_config_structure_and_determinism():
-    a = workloads.build(workloads.CONFIGS[1])
-    b = workloads.build(workloads.CONFIGS[1])
+def test_tiny_workload_structure_and_determinism():
+    a = workloads.build(workloads.BENCH_WORKLOADS[1])
+    b = workloads.build(workloads.BENCH_WORKLOADS[1])
     assert a.dtype == "f32" and a.num_reqs == 4 and a.num_blocks == 65
     assert ((a.seq_lens >= 1) & (a.seq_lens <= 64)).all()
     _check_structure(a)
@@ -52,8 +52,8 @@ def test_small_specs_structure(reqs):
     _check_structure(workloads.build(workloads.small_spec("s", 3, "bf16", 4, 2, 8, reqs)))
 
 
-def test_config_request_shapes():
-    for n, spec in workloads.CONFIGS.items():
+def test_workload_request_shapes():
+    for n, spec in workloads.BENCH_WORKLOADS.items():
         reqs = spec.requests(np.random.default_rng([spec.seed, 0]))
         ql = np.array([q for _, q in reqs])
         L = np.array([c + q for c, q in reqs])

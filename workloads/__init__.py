@@ -243,7 +243,7 @@ def _long_decode(g):
     return _decode(np.full(8, 32768))
 
 
-CONFIGS = {
+BENCH_WORKLOADS = {
     1: Spec("tiny paged decode fp32 (4 seqs, L~U[1,64], 8q/2kv, D=64, pool 64)",
             1, "f32", 8, 2, 64, _tiny_decode, pool_blocks=64),
     2: Spec("Llama-7B-shaped decode bf16 (64 seqs, L~U[512,4096], 32q/32kv, D=128)",
