@@ -189,8 +189,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
                     base.slots > a.cap_slots;
   // Bucket offsets, longest bucket first: thread t owns the 4 buckets at
   // descending positions 4t .. 4t+3 of the prefill list; thread 0 also does
-  // the 32 tail buckets.
-  {
+  // the 32 tail buckets.  (Skipped, like pass 2, when nothing is sorted:
+  // base is the same in every thread.)
+  const bool sorted_work = base.prefill > 0 || base.tail > 0;
+  if (sorted_work) {
     constexpr int kPer = kPfBuckets / kPlanThreads;
     int n[kPer], local = 0;
 #pragma unroll
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
 
   // Pass 2: scatter the sorted items (order inside a bucket is irrelevant:
   // an item's result does not depend on which worker computes it).
-  if (!over) {
+  if (!over && sorted_work) {
     int slot_base = 0;  // the split rows' partial slots, recomputed as in pass 1
     for (int r0 = 0; r0 < a.num_reqs; r0 += kPlanThreads) {
       const int r = r0 + threadIdx.x;
