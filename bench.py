@@ -316,7 +316,7 @@ def main():
         # codes and scales are never read)
         nb = pool.shape[1]
         codes = torch.empty(pool.shape, dtype=torch.int8 if kv8 == "int8" else torch.uint8, device=dev)
-        kv_scales = torch.empty(pool.shape[:4], dtype=torch.float32, device=dev)
+        kv_scales = torch.empty((2, nb, wl.num_kv_heads, 16), dtype=torch.float32, device=dev)
         write8(pool[0].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
                pool[1].reshape(nb * 16, wl.num_kv_heads, wl.head_dim).contiguous(),
                torch.arange(nb * 16, dtype=torch.int64, device=dev), codes, kv_scales)

@@ -248,7 +248,9 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  * dequantisation as it is read: lpnh.cn/news/2436702, section 4.2, "KV
  * Cache 量化").  The cache of one layer is
  *   kv_cache_layer  int8 [2][num_blocks][16][num_kv_heads][head_dim] codes,
- *   kv_scales       float32 [2][num_blocks][16][num_kv_heads] scales,
+ *   kv_scales       float32 [2][num_blocks][num_kv_heads][16] scales (a kv
+ *                   head's 16 scales of a block are contiguous; the scale of
+ *                   slot (block b, offset o), head h is [kv][b][h][o]),
  * value = code * scale.  Each (token, K or V, kv head) row of head_dim
  * values is quantised on its own: scale = max|x| / 127, code =
  * round-half-even(x / scale) clamped to [-127, 127], both divisions IEEE
@@ -291,7 +293,7 @@ int paged_attention_int8(void* out, const void* q, const void* kv_cache_layer, c
  * exponent bits with bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, no
  * infinities; 0x7f / 0xff are NaN and never written):
  *   kv_cache_layer  uint8 [2][num_blocks][16][num_kv_heads][head_dim] codes,
- *   kv_scales       float32 [2][num_blocks][16][num_kv_heads] scales,
+ *   kv_scales       float32 [2][num_blocks][num_kv_heads][16] scales (as INT8),
  * value = E4M3(code) * scale, with scale = max|x| / 448 and code = the E4M3
  * value nearest to x / scale (IEEE float32 quotient, magnitude clipped at
  * 448), ties to the even code, sign bit from the quotient; an all-zero row

@@ -324,8 +324,8 @@ def _check_i8_cache(kv_cache: torch.Tensor, kv_scales: torch.Tensor, fmt: str = 
     _check_dev("kv_scales", kv_scales, torch.float32)
     if kv_cache.dim() != 5 or kv_cache.shape[0] != 2 or kv_cache.shape[2] != BLOCK_SIZE:
         raise ValueError("kv_cache_layer must be [2, num_blocks, 16, num_kv_heads, head_dim] codes")
-    if tuple(kv_scales.shape) != tuple(kv_cache.shape[:4]):
-        raise ValueError("kv_scales must be float32 [2, num_blocks, 16, num_kv_heads]")
+    if tuple(kv_scales.shape) != (2, kv_cache.shape[1], kv_cache.shape[3], BLOCK_SIZE):
+        raise ValueError("kv_scales must be float32 [2, num_blocks, num_kv_heads, 16]")
 
 
 def paged_kv_write_int8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,

@@ -6,7 +6,8 @@
 // one float32 scale: value = code * scale, or E4M3(code) * scale (online
 // quantisation of the KV cache, lpnh.cn/news/2436702 section 4.2; the rows
 // are quantised as they are written, by paged_kv_write_int8 / _fp8).  Codes
-// [2][num_blocks][16][Hkv][D] bytes, scales [2][num_blocks][16][Hkv] float32.  What is computed is the same
+// [2][num_blocks][16][Hkv][D] bytes, scales [2][num_blocks][Hkv][16] float32
+// (a kv head's 16 scales of a block are contiguous).  What is computed is the same
 // softmax(q k^T * scale) v over the request's tokens 0 .. position
 // ("AI Infra入门干货总结", sections "Paged Attention" and "Attention
 // (FlashAttention)") with k, v the dequantised rows; work items, split-KV
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
       for (int j = 0; j < KLD; ++j) s.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 16 * j, 0, 0);
 #pragma unroll
       for (int j = 0; j < VLD; ++j) s.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, j * TPV * row_stride, 0);
-      const size_t srow = ((size_t)phys * kBlock + tk) * a.num_kv_heads + g;
+      const size_t srow = ((size_t)phys * a.num_kv_heads + g) * kBlock + tk;
       s.sk = kv_scales[srow];
       s.sv = kv_scales[scale_half + srow];
     };
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
           st.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, i * row_stride, 0);
         }
       }
-      const size_t srow = ((size_t)phys * kBlock + r16) * a.num_kv_heads + g;
+      const size_t srow = ((size_t)phys * a.num_kv_heads + g) * kBlock + r16;
       st.sk = kv_scales[srow];
       st.sv = kv_scales[scale_half + srow];
     };

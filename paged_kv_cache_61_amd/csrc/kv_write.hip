@@ -230,7 +230,9 @@ __global__ __launch_bounds__(256) void kv_write_i8_kernel(const void* __restrict
       *(uint16_t*)dst = (uint16_t)((uint8_t)c[0] | ((uint16_t)(uint8_t)c[1] << 8));
     else
       dst[0] = c[0];
-    if (lane == 0) scales[((size_t)kv * num_slots + slot) * num_kv_heads + h] = scale;
+    // scales [2][num_blocks][num_kv_heads][16]: a head's 16 scales of a block are contiguous
+    if (lane == 0)
+      scales[(((size_t)kv * num_blocks + slot / kBlock) * num_kv_heads + h) * kBlock + slot % kBlock] = scale;
   }
 }
 

@@ -240,8 +240,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   const int cblk = w & 3;
   const char* cbase = w < 4 ? kbase : vbase;
   const int ldst_half = I8 ? (w < 4 ? 0 : kHalf8) + cblk * kBlock * kRowB8 : (w < 4 ? 0 : kHalfTile) + cblk * kBlock * kRowB;
-  // (INT8) this wave's block of scales: [2][num_blocks][16][Hkv] fp32
-  const float* sbase = a.kv_scales + (w < 4 ? 0 : (size_t)a.num_blocks * kBlock * Hkv);
 
   // V^T transpose-read geometry (per lane, independent of the tile).
   const int ts = lane & 15;                            // source lane inside a 16-lane group
@@ -257,6 +255,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // the current tile runs.
   const int n_entries = a.hdr[kHdrPrefillItems];
   const int g = blockIdx.x % Hkv;
+  // (8-bit cache) scales [2][num_blocks][Hkv][16] fp32: this wave's K or V
+  // half, and inside a block the 16 contiguous scales of kv head g
+  const float* sbase = a.kv_scales + (w < 4 ? 0 : (size_t)a.num_blocks * kBlock * Hkv) + (size_t)g * kBlock;
 
   // Copy geometry, the same for every tile: instruction j, lane L of this
   // wave's block copy carries token row 4j + L/16 of the block and the chunk
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // (INT8: instruction j < 2 fills LDS rows s = 8j + L/8 of the block, 16
   // codes of token row s ^ bit2(s) each, so rows r and r + 4 sit in opposite
   // bank halves for the dequantisation reads; voff[2] is the scale of token
-  // row L of the block, L < 16, stored in row order.)
+  // row L of the block, L < 16, among kv head g's 16 contiguous scales.)
   uint32_t voff[4];
   if constexpr (I8) {
 #pragma unroll
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       const int tr = sr ^ ((sr >> 2) & 1);     // token row it holds
       voff[j] = tr * (uint32_t)row_bytes + g * kRowB8 + ((lane & 7) << 4);
     }
-    voff[2] = (uint32_t)(lane & 15) * (uint32_t)Hkv * 4u + (uint32_t)g * 4u;
+    voff[2] = (uint32_t)(lane & 15) * 4u;
     voff[3] = 0;
   } else {
 #pragma unroll
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     const u32x4 rs = buffer_desc(cbase + (uint64_t)phys * blk_bytes32, nbytes);
     if constexpr (I8) {
       // codes (2 instructions) and scales (1): three vector-memory operations per tile
-      const uint32_t sbytes = (uint32_t)min(max(nvalid, 0), kBlock) * (uint32_t)Hkv * 4u;
+      const uint32_t sbytes = (uint32_t)min(max(nvalid, 0), kBlock) * 4u;
       const u32x4 rss = buffer_desc(sbase + (size_t)phys * kBlock * Hkv, sbytes);
       const uint32_t slot = (uint32_t)(tile & (kStages8 - 1)) * kStage8;
       static_assert(8 * kRowB8 == 0x400, "dma_pair steps M0 by 1 KiB (8 token rows)");

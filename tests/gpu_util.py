@@ -105,6 +105,17 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -
     return stats
 
 
+def scales_to_dev(scales: np.ndarray) -> torch.Tensor:
+    """Per-row scales in the oracle's cache order [2, NB, 16, Hkv] -> the
+    library's 8-bit scale layout [2, NB, Hkv, 16] on the device."""
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(scales, np.float32).transpose(0, 1, 3, 2))).cuda()
+
+
+def scales_from_dev(t: torch.Tensor) -> np.ndarray:
+    """The inverse of scales_to_dev: [2, NB, Hkv, 16] -> [2, NB, 16, Hkv] (numpy)."""
+    return np.ascontiguousarray(t.cpu().numpy().transpose(0, 1, 3, 2))
+
+
 def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
     """An 8-bit cache (``fmt`` "int8" or "fp8") at a benchmark workload's full
     size, in the benchmark's launch configuration: the whole pool quantised on
@@ -122,7 +133,7 @@ def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
     s = upload(wl)
     NB, Hkv, D = wl.num_blocks, wl.num_kv_heads, wl.head_dim
     codes = torch.empty(tuple(s.pool.shape), dtype=torch.int8 if fmt == "int8" else torch.uint8, device="cuda")
-    scales = torch.empty(tuple(s.pool.shape[:4]), dtype=torch.float32, device="cuda")
+    scales = torch.empty((2, NB, Hkv, 16), dtype=torch.float32, device="cuda")
     write8(s.pool[0].reshape(NB * 16, Hkv, D).contiguous(), s.pool[1].reshape(NB * 16, Hkv, D).contiguous(),
            torch.arange(NB * 16, dtype=torch.int64, device="cuda"), codes, scales)
     del s.pool
@@ -148,7 +159,7 @@ def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
     rc, rs = quant(np.where(live[..., None], ref_pool, 0).astype(ref_pool.dtype), wl.dtype)
     idx = torch.tensor(blocks, dtype=torch.int64, device="cuda")
     gc = codes.index_select(1, idx).cpu().numpy()
-    gs = scales.index_select(1, idx).cpu().numpy()
+    gs = scales_from_dev(scales.index_select(1, idx))
     assert np.array_equal(gc[live], rc[live]), "codes differ"
     assert gs[live].tobytes() == rs[live].tobytes(), "scales differ"
     # attention over the dequantised blocks (block ids remapped to the subset)

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import assert_close, out_f64, to_dev
+from gpu_util import assert_close, out_f64, scales_from_dev, scales_to_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -63,14 +63,14 @@ def _run(wl, dtype_q, block_table=None, expect_error=0):
     import paged_kv_cache_61_amd as pkv
     codes, scales = _quantised_pool(wl)
     d_codes = torch.from_numpy(codes).cuda()
-    d_scales = torch.from_numpy(scales).cuda()
+    d_scales = scales_to_dev(scales)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     pkv.paged_kv_write_fp8(to_dev(wl.k_new, wl.dtype), to_dev(wl.v_new, wl.dtype),
                            torch.from_numpy(wl.slot_mapping).cuda(), d_codes, d_scales, device_error=err)
     out, ws_err = _attend(wl, dtype_q, d_codes, d_scales, block_table)
     assert int(err.item()) == 0 and ws_err == expect_error
     ref_codes, ref_scales = oracle.kv_write_fp8(codes, scales, wl.k_new, wl.v_new, wl.slot_mapping, wl.dtype)
-    return out, d_codes.cpu().numpy(), d_scales.cpu().numpy(), ref_codes, ref_scales
+    return out, d_codes.cpu().numpy(), scales_from_dev(d_scales), ref_codes, ref_scales
 
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 8, 8), ("bf16", 128, 32, 8), ("bf16", 64, 16, 2),
@@ -110,7 +110,7 @@ def test_fp8_every_code_decodes_exactly(dtype, D, ql):
     if ql > 1:   # the chunk's second key: any finite codes
         codes[:, blk, 1] = rng.integers(0, 0x7E, (2, Hkv, D)).astype(np.uint8)
         scales[:, blk, 1] = np.float32(1.0)
-    out, err = _attend(wl, dtype, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    out, err = _attend(wl, dtype, torch.from_numpy(codes).cuda(), scales_to_dev(scales))
     assert err == 0
     want = oracle.fp8_e4m3_decode(v_codes) * 0.25          # [Hkv, D]
     got = out_f64(out)[0].reshape(Hkv, Hq // Hkv, D)
@@ -167,12 +167,12 @@ def test_fp8_write_zero_rows_negative_zero_and_padding():
     slots = np.array([3, 17, -1, 40, 63, 0], np.int64)   # one padding token
     codes = np.full((2, NB, 16, Hkv, D), 7, np.uint8)
     scales = np.full((2, NB, 16, Hkv), 5.0, np.float32)
-    d_codes, d_scales = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    d_codes, d_scales = torch.from_numpy(codes).cuda(), scales_to_dev(scales)
     pkv.paged_kv_write_fp8(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda(),
                            d_codes, d_scales)
     torch.cuda.synchronize()
     rc, rs = oracle.kv_write_fp8(codes, scales, k, v, slots, "f32")
-    assert np.array_equal(d_codes.cpu().numpy(), rc) and d_scales.cpu().numpy().tobytes() == rs.tobytes()
+    assert np.array_equal(d_codes.cpu().numpy(), rc) and scales_from_dev(d_scales).tobytes() == rs.tobytes()
     assert rs[0, 1, 1].tolist() == [0.0, 0.0]
     assert (rc[0, 2, 8, 0, :5] == 0x80).all()
 

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import assert_close, from_dev, out_f64, to_dev
+from gpu_util import assert_close, from_dev, out_f64, scales_from_dev, scales_to_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def _run(wl, dtype_q, block_table=None, expect_error=0):
     bt = wl.block_table if block_table is None else block_table
     codes, scales = _quantised_pool(wl)
     d_codes = torch.from_numpy(codes).cuda()
-    d_scales = torch.from_numpy(scales).cuda()
+    d_scales = scales_to_dev(scales)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     pkv.paged_kv_write_int8(to_dev(wl.k_new, wl.dtype), to_dev(wl.v_new, wl.dtype),
                             torch.from_numpy(wl.slot_mapping).cuda(), d_codes, d_scales, device_error=err)
@@ -57,7 +57,7 @@ def _run(wl, dtype_q, block_table=None, expect_error=0):
     torch.cuda.synchronize()
     assert int(err.item()) == 0 and pkv.pkv_read_device_error(ws) == expect_error
     ref_codes, ref_scales = oracle.kv_write_int8(codes, scales, wl.k_new, wl.v_new, wl.slot_mapping, wl.dtype)
-    return out, d_codes.cpu().numpy(), d_scales.cpu().numpy(), ref_codes, ref_scales
+    return out, d_codes.cpu().numpy(), scales_from_dev(d_scales), ref_codes, ref_scales
 
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 8, 8), ("bf16", 128, 32, 8), ("bf16", 64, 16, 2),
@@ -130,12 +130,12 @@ def test_int8_write_zero_rows_and_padding():
     slots = np.array([3, 17, -1, 40, 63, 0], np.int64)   # one padding token
     codes = np.full((2, NB, 16, Hkv, D), 7, np.int8)
     scales = np.full((2, NB, 16, Hkv), 5.0, np.float32)
-    d_codes, d_scales = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    d_codes, d_scales = torch.from_numpy(codes).cuda(), scales_to_dev(scales)
     pkv.paged_kv_write_int8(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda(),
                             d_codes, d_scales)
     torch.cuda.synchronize()
     rc, rs = oracle.kv_write_int8(codes, scales, k, v, slots, "f32")
-    assert np.array_equal(d_codes.cpu().numpy(), rc) and d_scales.cpu().numpy().tobytes() == rs.tobytes()
+    assert np.array_equal(d_codes.cpu().numpy(), rc) and scales_from_dev(d_scales).tobytes() == rs.tobytes()
     assert rs[0, 1, 1].tolist() == [0.0, 0.0]
 
 
