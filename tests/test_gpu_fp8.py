@@ -69,6 +69,9 @@ def _run(wl, dtype_q, block_table=None, expect_error=0):
                            torch.from_numpy(wl.slot_mapping).cuda(), d_codes, d_scales, device_error=err)
     out, ws_err = _attend(wl, dtype_q, d_codes, d_scales, block_table)
     assert int(err.item()) == 0 and ws_err == expect_error
+    again, _ = _attend(wl, dtype_q, d_codes, d_scales, block_table)     # deterministic: same bits
+    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32),
+                       again.view(torch.int16) if again.dtype == torch.bfloat16 else again.view(torch.int32))
     ref_codes, ref_scales = oracle.kv_write_fp8(codes, scales, wl.k_new, wl.v_new, wl.slot_mapping, wl.dtype)
     return out, d_codes.cpu().numpy(), scales_from_dev(d_scales), ref_codes, ref_scales
 

@@ -54,8 +54,15 @@ def _run(wl, dtype_q, block_table=None, expect_error=0):
                                    i32(wl.seq_lens), i32(wl.query_start_loc), i32(wl.num_computed_tokens),
                                    wl.scale, max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
                                    workspace=ws)
+    again = pkv.paged_attention_int8(to_dev(wl.q, dtype_q), d_codes, d_scales, i32(bt),
+                                     i32(wl.seq_lens), i32(wl.query_start_loc), i32(wl.num_computed_tokens),
+                                     wl.scale, max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                                     workspace=ws)
     torch.cuda.synchronize()
     assert int(err.item()) == 0 and pkv.pkv_read_device_error(ws) == expect_error
+    # deterministic: the same bits (NaN rows included)
+    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32),
+                       again.view(torch.int16) if again.dtype == torch.bfloat16 else again.view(torch.int32))
     ref_codes, ref_scales = oracle.kv_write_int8(codes, scales, wl.k_new, wl.v_new, wl.slot_mapping, wl.dtype)
     return out, d_codes.cpu().numpy(), scales_from_dev(d_scales), ref_codes, ref_scales
 

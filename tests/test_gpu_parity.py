@@ -132,9 +132,11 @@ def test_block_permutation_bit_exact():
     assert a == b
 
 
-def test_determinism_and_batch_invariance():
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (16, 2), (32, 2)])
+def test_determinism_and_batch_invariance(Hq, Hkv):
+    # groups of 4 (VALU row kernel) and 8, 16 (MFMA row kernel)
     reqs = [(700, 1), (30, 1), (2000, 1), (100, 9), (0, 25), (1300, 1)]
-    wl = workloads.build(workloads.small_spec("batch", 22, "bf16", 16, 4, 128, reqs))
+    wl = workloads.build(workloads.small_spec("batch", 22, "bf16", Hq, Hkv, 128, reqs))
     s = upload(wl)
     run_write(s)
     a = _bits(run_attention(s))
