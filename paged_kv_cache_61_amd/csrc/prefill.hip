@@ -83,7 +83,7 @@ constexpr int kStage8 = 2 * kHalf8 + 2 * kScl;    // one int8 ring slot
 constexpr int kStages8 = 4;
 constexpr int kConv = kStages8 * kStage8;         // offset of the bf16 tiles K0, K1, V0, V1
 constexpr int kLdsI8 = kConv + 4 * kHalfTile;
-static_assert(kLdsI8 + 64 <= 160 * 1024, "INT8 prefill LDS");
+static_assert(kLdsI8 + 64 <= 160 * 1024, "8-bit prefill LDS");
 constexpr int kDTiles = kD / 32;            // O^T row tiles
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // wave's block copy carries token row 4j + L/16 of the block and the chunk
   // that lands at LDS position L mod 16 (chunk (L mod 16) ^ swz(row)); the
   // destination is this wave's quarter of a ring slot's K or V half.
-  // (INT8: instruction j < 2 fills LDS rows s = 8j + L/8 of the block, 16
+  // (8-bit cache: instruction j < 2 fills LDS rows s = 8j + L/8 of the block, 16
   // codes of token row s ^ bit2(s) each, so rows r and r + 4 sit in opposite
   // bank halves for the dequantisation reads; voff[2] is the scale of token
   // row L of the block, L < 16, among kv head g's 16 contiguous scales.)
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     if (I8 && ntiles > 2) issue_tile(2);
   };
 
-  // (INT8) Dequantisation role: lane L = 16a + 8b + k of wave w handles
+  // (8-bit cache) Dequantisation role: lane L = 16a + 8b + k of wave w handles
   // tile row r = 8w + 4b + a, codes 16k .. 16k+15 (LDS row r ^ b of the int8
   // slot), and writes them as bf16 chunks 2k and 2k+1 of row r at their
   // swizzled positions; each 16-lane group covers rows of opposite bank
