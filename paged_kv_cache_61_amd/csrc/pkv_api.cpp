@@ -239,11 +239,19 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   pp.split_decode = 1;
   pp.mfma_prefill = prefill_on_mfma(dtype, head_dim) ? 1 : 0;
   pp.prefill_tile_rows = (int32_t)tile_rows;
+  // One 8-wave prefill workgroup per CU; the grid is a multiple of the kv
+  // head count so every workgroup owns one head (slot = blockIdx / heads).
+  const int cus = num_cus();
+  const int64_t pf_per_head =
+      std::max<int64_t>(1, std::min<int64_t>(ws.cap_prefill_items, (int64_t)cus / num_kv_heads));
+  pp.prefill_slots = (int32_t)pf_per_head;
   pp.hdr = hdr;
   pp.row_items = (int4*)(wsb + ws.row_items);
   pp.row_items_tail = (int4*)(wsb + ws.row_items_tail);
   pp.prefill_items = (int4*)(wsb + ws.prefill_items);
   pp.reduce_items = (int4*)(wsb + ws.reduce_items);
+  pp.pf_order = (int32_t*)(wsb + ws.pf_order);
+  pp.pf_slot_start = (int32_t*)(wsb + ws.pf_slot_start);
   pp.cap_row_items = ws.cap_row_items;
   pp.cap_prefill_items = ws.cap_prefill_items;
   pp.cap_reduce = ws.cap_reduce;
@@ -252,7 +260,6 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   if (pkv::launch_plan(pp, s)) return fail(PKV_ERR_LAUNCH, "plan launch failed");
   mark(PKV_PHASE_PLAN, 1);
 
-  const int cus = num_cus();
   const float scale_log2 = scale * 1.4426950408889634f;
   mark(PKV_PHASE_PREFILL, 0);
   if (pp.mfma_prefill && max_query_len > 1) {
@@ -266,6 +273,8 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.qsl = query_start_loc;
     fp.nct = num_computed_tokens;
     fp.items = pp.prefill_items;
+    fp.pf_order = pp.pf_order;
+    fp.pf_slot_start = pp.pf_slot_start;
     fp.hdr = hdr;
     fp.err = hdr + pkv::kHdrError;
     fp.scale_log2 = scale_log2;
@@ -274,11 +283,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.group = group;
     fp.num_blocks = num_blocks;
     fp.max_blocks_per_req = max_blocks_per_req;
-    // One 8-wave workgroup per CU; the grid is a multiple of the kv head
-    // count so every workgroup owns one head.
-    const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(ws.cap_prefill_items,
-                                                                   (int64_t)cus / num_kv_heads));
-    const int64_t grid = per_head * num_kv_heads;
+    const int64_t grid = pf_per_head * num_kv_heads;
     if (pkv::launch_prefill(fp, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "prefill launch failed");
   }
 

@@ -22,9 +22,12 @@ enum HdrWord {
   kHdrReduceItems = 3,
   kHdrSlots = 4,
   kHdrRowHead = 5,      // row items in the first region (the rest are in the tail region)
+  kHdrPrefillStatic = 6,  // 1: prefill items come from per-slot lists (pf_order), 0: from the queues
   kHdrPrefillQueue = 16,  // one prefill work-queue counter per kv head (zeroed by the plan kernel)
 };
 constexpr int kMaxKvHeads = 240;  // kv heads with a prefill queue counter in the header
+constexpr int kPfMaxSlots = 64;   // static prefill assignment: at most this many workgroups per kv head
+constexpr int kPfMaxStatic = 256; // ... and at most this many prefill items
 constexpr size_t kHdrBytes = 1024;
 static_assert((kHdrPrefillQueue + kMaxKvHeads) * 4 <= kHdrBytes, "header too small");
 
@@ -38,7 +41,7 @@ constexpr int kNanRow = -2;
 // (relative to the request), z = rows in the tile, w = unused.
 
 struct WsLayout {
-  size_t row_items, row_items_tail, prefill_items, reduce_items, part_ml, part_o, total;
+  size_t row_items, row_items_tail, prefill_items, reduce_items, pf_order, pf_slot_start, part_ml, part_o, total;
   int64_t cap_row_items, cap_prefill_items, cap_reduce, cap_slots;
 };
 
@@ -62,6 +65,8 @@ inline WsLayout ws_layout(int64_t num_reqs, int64_t num_tokens, int64_t num_q_he
   w.row_items_tail = off; off = align_up(off + sizeof(int32_t) * 4 * w.cap_row_items, 256);
   w.prefill_items = off;  off = align_up(off + sizeof(int32_t) * 4 * w.cap_prefill_items, 256);
   w.reduce_items = off;   off = align_up(off + sizeof(int32_t) * 4 * w.cap_reduce, 256);
+  w.pf_order = off;       off = align_up(off + sizeof(int32_t) * kPfMaxStatic, 256);
+  w.pf_slot_start = off;  off = align_up(off + sizeof(int32_t) * (kPfMaxSlots + 1), 256);
   w.part_ml = off;        off = align_up(off + sizeof(float) * 2 * w.cap_slots * num_q_heads, 256);
   w.part_o = off;         off = align_up(off + sizeof(float) * w.cap_slots * num_q_heads * head_dim, 256);
   w.total = off;

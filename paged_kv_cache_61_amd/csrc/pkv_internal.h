@@ -25,11 +25,14 @@ struct PlanParams {
   int32_t split_decode;      // decode rows may be split into partitions
   int32_t mfma_prefill;      // query_len > 1 requests go to the prefill kernel
   int32_t prefill_tile_rows; // query rows per prefill tile
+  int32_t prefill_slots;     // prefill workgroups per kv head (the prefill grid / num_kv_heads)
   int32_t* hdr;
   int4* row_items;
   int4* row_items_tail;
   int4* prefill_items;
   int4* reduce_items;
+  int32_t* pf_order;         // static prefill assignment: item indices slot by slot
+  int32_t* pf_slot_start;    // [prefill_slots + 1] offsets of each slot's items in pf_order
   int64_t cap_row_items, cap_prefill_items, cap_reduce, cap_slots;
 };
 
@@ -69,7 +72,9 @@ struct PrefillParams {
   const int4* items;
   int32_t* hdr;
   int32_t* err;
-  const float* kv_scales;  // 8-bit cache: [2][num_blocks][16][num_kv_heads] scales; else nullptr
+  const int32_t* pf_order;       // per-slot item lists, used when hdr[kHdrPrefillStatic] is 1
+  const int32_t* pf_slot_start;
+  const float* kv_scales;  // 8-bit cache: [2][num_blocks][num_kv_heads][16] scales; else nullptr
   int32_t kv_fp8;          // 8-bit cache codes: 0 INT8, 1 OCP E4M3
   float scale_log2;
   int32_t num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_req;

@@ -119,8 +119,73 @@ __device__ int pf_bucket(const ReqInfo& q, int row0, int rows) {
   return min((kv_end + 63) / 64, kPfBuckets - 1);
 }
 
+// Wave-wide maximum of an int (all 64 lanes active): rotations inside rows
+// of 16 lanes (DPP), then the v_permlane16/32 swaps; VALU only.
+template <int CTRL>
+PKV_DEV int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
+}
+PKV_DEV int wave_max_i(int x) {
+  x = max(x, dpp_i<0x121>(x));  // row_ror:1
+  x = max(x, dpp_i<0x122>(x));  // row_ror:2
+  x = max(x, dpp_i<0x124>(x));  // row_ror:4
+  x = max(x, dpp_i<0x128>(x));  // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = max((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+
+// Static assignment of the prefill items to the W workgroups of each kv head
+// (every head has the same item list): best fit decreasing on a cost of
+// (10 * tiles + 50) per item (KV tiles to read plus the item's fixed
+// overhead, in tenths of a tile period).  Items arrive longest first; each
+// goes to the fullest slot it still fits in under the capacity
+// ceil(total / W) + 5, or else to the emptiest slot.  Lane s of the calling
+// wave holds slot s's load and item count; the choice is one wave maximum
+// over (load, slot) keys.  Writes slot_of[i] and the item's rank inside its
+// slot, then the slot offsets (exclusive sums of the counts).
+PKV_DEV void assign_best_fit(const int* tiles, int n, int W, int* slot_of, int* rank_of, int* slot_start) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int total = 0;
+  for (int i = lane; i < n; i += kWave) total += 10 * tiles[i] + 50;
+  for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
+  const int cap = (total + W - 1) / W + 5;
+  int load = 0, cnt = 0;
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int tl = i0 + lane < n ? tiles[i0 + lane] : 0;
+    for (int j = 0; j < kWave && i0 + j < n; ++j) {
+      const int c = 10 * __builtin_amdgcn_readlane(tl, j) + 50;
+      const bool live = lane < W;
+      int m = wave_max_i(live && load + c <= cap ? (load << 6) | (63 - lane) : -1);
+      if (m < 0) m = wave_max_i(live ? ((0xffffff - load) << 6) | (63 - lane) : -1);
+      const int win = 63 - (m & 63);
+      const int rank = __builtin_amdgcn_readlane(cnt, win);
+      if (lane == win) {
+        load += c;
+        ++cnt;
+      }
+      if (lane == 0) {
+        slot_of[i0 + j] = win;
+        rank_of[i0 + j] = rank;
+      }
+    }
+  }
+  // exclusive sums of the counts (W <= 64 lanes)
+  __shared__ int cnt_lds[kPfMaxSlots];
+  cnt_lds[lane] = cnt;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int st = 0;
+  for (int j = 0; j < lane; ++j) st += cnt_lds[j];
+  if (lane <= W) slot_start[lane] = lane == W ? n : st;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   __shared__ int err_acc;
+  __shared__ int pf_tiles[kPfMaxStatic], pf_slot_of[kPfMaxStatic], pf_rank[kPfMaxStatic];
+  __shared__ int pf_start[kPfMaxSlots + 1];
   __shared__ int pf_off[kPfBuckets];
   __shared__ int tail_off[kTailBuckets];
   for (int i = threadIdx.x; i < kPfBuckets; i += kPlanThreads) pf_off[i] = 0;
@@ -238,13 +303,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
       } else if (q.kind == 2) {
         for (int row0 = 0; row0 < q.ql; row0 += a.prefill_tile_rows) {
           const int rows = min(a.prefill_tile_rows, q.ql - row0);
-          const int pos = atomicAdd(&pf_off[pf_bucket(q, row0, rows)], 1);
+          const int tiles = pf_bucket(q, row0, rows);
+          const int pos = atomicAdd(&pf_off[tiles], 1);
           a.prefill_items[pos] = make_int4(r, row0, rows, 0);
+          if (pos < kPfMaxStatic) pf_tiles[pos] = tiles;
         }
       }
     }
   }
   __syncthreads();
+  // Static prefill assignment when it is small enough to build here (one
+  // wave); otherwise the prefill kernel takes items from per-head queues.
+  const int npf = base.prefill;
+  const bool pf_static = !over && npf > 0 && npf <= kPfMaxStatic && a.prefill_slots > 0 &&
+                         a.prefill_slots <= kPfMaxSlots;
+  if (pf_static && threadIdx.x < kWave) assign_best_fit(pf_tiles, npf, a.prefill_slots, pf_slot_of, pf_rank, pf_start);
+  __syncthreads();
+  if (pf_static) {
+    for (int i = threadIdx.x; i < npf; i += blockDim.x) a.pf_order[pf_start[pf_slot_of[i]] + pf_rank[i]] = i;
+    for (int i = threadIdx.x; i <= a.prefill_slots; i += blockDim.x) a.pf_slot_start[i] = pf_start[i];
+  }
   for (int i = threadIdx.x; i < kMaxKvHeads; i += blockDim.x) a.hdr[kHdrPrefillQueue + i] = 0;
   if (threadIdx.x == 0) {
     // On overflow nothing past the capacity was written; run no work at all.
@@ -252,6 +330,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     a.hdr[kHdrRowItems] = over ? 0 : base.rows + base.tail;
     a.hdr[kHdrRowHead] = over ? 0 : base.rows;
     a.hdr[kHdrPrefillItems] = over ? 0 : base.prefill;
+    a.hdr[kHdrPrefillStatic] = pf_static ? 1 : 0;
     a.hdr[kHdrReduceItems] = over ? 0 : base.reduce;
     a.hdr[kHdrSlots] = over ? 0 : base.slots;
   }

@@ -288,8 +288,22 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   const uint32_t ldsc = (uint32_t)(uintptr_t)PKV_LDS(lds) + (uint32_t)(2 * kHalf8 + (w < 4 ? 0 : kScl) + cblk * kBlock * 4);
   const uint32_t blk_bytes32 = (uint32_t)blk_bytes;
   int* queue = a.hdr + kHdrPrefillQueue + g;
+  // Items come either from the plan's static assignment (this workgroup's
+  // slot blockIdx.x / Hkv: a list in pf_order, the same for every head) or,
+  // when the plan did not build one, from the head's queue.
+  const bool from_list = a.hdr[kHdrPrefillStatic] != 0;
+  int list_pos = 0, list_base = 0, list_len = 0;
+  if (from_list) {
+    const int slot = blockIdx.x / Hkv;
+    list_base = a.pf_slot_start[slot];
+    list_len = a.pf_slot_start[slot + 1] - list_base;
+  }
+  auto take = [&]() PKV_INLINE -> int {   // the next item index (thread 0 only)
+    if (!from_list) return atomicAdd(queue, 1);
+    return list_pos < list_len ? a.pf_order[list_base + list_pos++] : n_entries;
+  };
   __shared__ int next_item[2];
-  if (tid == 0) next_item[0] = atomicAdd(queue, 1);
+  if (tid == 0) next_item[0] = take();
   __syncthreads();
 
   // State of the item being run, set by begin_item.
@@ -351,7 +365,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // first this runs right after the previous item's tile loop, so these
   // latencies overlap that item's epilogue.
   auto begin_item = [&](int ee) PKV_INLINE {
-    if (tid == 0) nxt = atomicAdd(queue, 1);
+    if (tid == 0) nxt = take();
     const int4 item = items[ee];
     r = item.x;
     row0 = item.y;
