@@ -137,38 +137,56 @@ PKV_DEV int wave_max_i(int x) {
 }
 
 // Static assignment of the prefill items to the W workgroups of each kv head
-// (every head has the same item list): best fit decreasing on a cost of
+// (every head has the same item list): first fit decreasing on a cost of
 // (10 * tiles + 50) per item (KV tiles to read plus the item's fixed
-// overhead, in tenths of a tile period).  Items arrive longest first; each
-// goes to the fullest slot it still fits in under the capacity
-// ceil(total / W) + 5, or else to the emptiest slot.  Lane s of the calling
-// wave holds slot s's load and item count; the choice is one wave maximum
-// over (load, slot) keys.  Writes slot_of[i] and the item's rank inside its
+// overhead of about five tile periods, in tenths of a tile).  Items arrive
+// longest first; each goes to the lowest slot it still fits in under the
+// capacity ceil(total / W) + 5, or else to the emptiest slot, ties to the
+// lowest.  On this list first fit packs as tightly as best fit and needs one
+// ballot per item instead of a wave-wide maximum.  An item costing more than
+// half the capacity fits in no slot that already holds one (those hold items
+// at least as long), so the first such items, up to W, take slots 0, 1, ...
+// directly; the rest are placed one by one.  Lane s of the calling wave holds
+// slot s's load and item count (loads stay below 2^24: at most 256 items of
+// at most 4095 tiles).  Writes slot_of[i] and the item's rank inside its
 // slot, then the slot offsets (exclusive sums of the counts).
-PKV_DEV void assign_best_fit(const int* tiles, int n, int W, int* slot_of, int* rank_of, int* slot_start) {
+PKV_DEV int item_cost(int tiles) { return 10 * tiles + 50; }
+
+PKV_DEV void assign_first_fit(const int* tiles, int n, int W, int* slot_of, int* rank_of, int* slot_start) {
   const int lane = threadIdx.x & (kWave - 1);
-  int total = 0;
-  for (int i = lane; i < n; i += kWave) total += 10 * tiles[i] + 50;
+  int total = 0, big = 0;
+  for (int i = lane; i < n; i += kWave) total += item_cost(tiles[i]);
   for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
   const int cap = (total + W - 1) / W + 5;
-  int load = 0, cnt = 0;
+  for (int i = lane; i < n; i += kWave) big += 2 * item_cost(tiles[i]) > cap ? 1 : 0;
+  for (int off = 32; off > 0; off >>= 1) big += __shfl_xor(big, off);
+  const int p = min(big, W);                        // items placed directly: item i in slot i
+  const bool live = lane < W;
+  int load = lane < p ? item_cost(tiles[lane]) : 0;
+  int cnt = lane < p ? 1 : 0;
   for (int i0 = 0; i0 < n; i0 += kWave) {
     const int tl = i0 + lane < n ? tiles[i0 + lane] : 0;
-    for (int j = 0; j < kWave && i0 + j < n; ++j) {
-      const int c = 10 * __builtin_amdgcn_readlane(tl, j) + 50;
-      const bool live = lane < W;
-      int m = wave_max_i(live && load + c <= cap ? (load << 6) | (63 - lane) : -1);
-      if (m < 0) m = wave_max_i(live ? ((0xffffff - load) << 6) | (63 - lane) : -1);
-      const int win = 63 - (m & 63);
-      const int rank = __builtin_amdgcn_readlane(cnt, win);
-      if (lane == win) {
-        load += c;
-        ++cnt;
+    int slot = i0 + lane < p ? i0 + lane : 0, rank = 0;   // for item i0 + lane
+    for (int j = max(p - i0, 0); j < kWave && i0 + j < n; ++j) {
+      const int c = item_cost(__builtin_amdgcn_readlane(tl, j));
+      const uint64_t fits = __ballot(live && load + c <= cap);
+      int win;
+      if (fits) {
+        win = __builtin_ctzll(fits);
+      } else {   // no slot has room: the emptiest one
+        const int m = wave_max_i(live ? ((0xffffff - load) << 6) | (63 - lane) : -1);
+        win = 63 - (__builtin_amdgcn_readfirstlane(m) & 63);
       }
-      if (lane == 0) {
-        slot_of[i0 + j] = win;
-        rank_of[i0 + j] = rank;
-      }
+      const int r = __builtin_amdgcn_readlane(cnt, win);
+      const bool mine = lane == win;
+      load += mine ? c : 0;
+      cnt += mine ? 1 : 0;
+      slot = lane == j ? win : slot;
+      rank = lane == j ? r : rank;
+    }
+    if (i0 + lane < n) {
+      slot_of[i0 + lane] = slot;
+      rank_of[i0 + lane] = rank;
     }
   }
   // exclusive sums of the counts (W <= 64 lanes)
@@ -179,7 +197,8 @@ PKV_DEV void assign_best_fit(const int* tiles, int n, int W, int* slot_of, int* 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int st = 0;
   for (int j = 0; j < lane; ++j) st += cnt_lds[j];
-  if (lane <= W) slot_start[lane] = lane == W ? n : st;
+  if (lane < W) slot_start[lane] = st;
+  if (lane == 0) slot_start[W] = n;   // W may be 64: no lane W
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
@@ -317,7 +336,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   const int npf = base.prefill;
   const bool pf_static = !over && npf > 0 && npf <= kPfMaxStatic && a.prefill_slots > 0 &&
                          a.prefill_slots <= kPfMaxSlots;
-  if (pf_static && threadIdx.x < kWave) assign_best_fit(pf_tiles, npf, a.prefill_slots, pf_slot_of, pf_rank, pf_start);
+  if (pf_static && threadIdx.x < kWave) assign_first_fit(pf_tiles, npf, a.prefill_slots, pf_slot_of, pf_rank, pf_start);
   __syncthreads();
   if (pf_static) {
     for (int i = threadIdx.x; i < npf; i += blockDim.x) a.pf_order[pf_start[pf_slot_of[i]] + pf_rank[i]] = i;

@@ -300,7 +300,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   }
   auto take = [&]() PKV_INLINE -> int {   // the next item index (thread 0 only)
     if (!from_list) return atomicAdd(queue, 1);
-    return list_pos < list_len ? a.pf_order[list_base + list_pos++] : n_entries;
+    const int e = list_pos < list_len ? a.pf_order[list_base + list_pos++] : n_entries;
+    return (unsigned)e < (unsigned)n_entries ? e : n_entries;
   };
   __shared__ int next_item[2];
   if (tid == 0) next_item[0] = take();

@@ -274,6 +274,21 @@ def test_prefill_group_sizes(Hq, Hkv):
     _full_step(wl, f"prefill G={Hq // Hkv}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,reqs", [
+    # 4 kv heads: 64 workgroups per head on 256 CUs (the widest static
+    # assignment), 67 items of 1 to 47 KV tiles
+    (16, 4, [(0, 2048), (700, 1500), (3000, 600), (0, 5)]),
+    # 8 kv heads, 32 workgroups per head, items of one length only
+    (32, 8, [(0, 64)] * 40 + [(64, 64)] * 8),
+])
+def test_prefill_static_item_assignment(Hq, Hkv, reqs):
+    # the plan kernel hands each prefill workgroup a fixed list of items
+    # (header word 6 set); every item must be run exactly once
+    wl = workloads.build(workloads.small_spec(f"prefill-static-{Hq}-{Hkv}", 47 + Hq, "bf16", Hq, Hkv, 128, reqs))
+    s, _ = _full_step(wl, f"static prefill assignment {Hq}/{Hkv}")
+    assert int(s.workspace[24:28].view(torch.int32).item()) == 1
+
+
 def test_prefill_long_context_reads_table_per_tile():
     # chunks whose keys run past 128 tiles of 64 (8192 keys): the prefill
     # kernel reads those tiles' block ids from the table per tile instead of
