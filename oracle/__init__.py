@@ -225,14 +225,20 @@ def rope(x: np.ndarray, positions: np.ndarray, cos_sin_cache: np.ndarray, rotary
 
 
 def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 -> storage values: float32, or bf16 bit patterns (nearest even,
-    through float32: the two roundings agree except on exact float32 ties,
-    which the product's own fp32 arithmetic cannot avoid either)."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    """float64 -> storage values: float32 (IEEE nearest even), or bf16 bit
+    patterns.  bf16 keeps the top 16 bits of the float32, rounded to nearest
+    with ties to even (a float32 whose low 16 bits are exactly 0x8000 is a
+    tie); the float64 value is first rounded to float32, as the product's own
+    float32 arithmetic does.  A carry out of the mantissa bumps the exponent
+    (so the largest finite float32 rounds to infinity); NaN becomes the quiet
+    NaN 0x7FC0."""
+    with np.errstate(over="ignore", invalid="ignore"):     # beyond float32 -> +-inf
+        f = np.asarray(x, dtype=np.float64).astype(np.float32)
     if dtype == "f32":
         return f
-    u = f.view(np.uint32)
-    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    u = f.view(np.uint32).astype(np.uint64)            # no wrap-around in the addition
+    r = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint16)
+    return np.where(np.isnan(f), np.uint16(0x7FC0), r).astype(np.uint16)
 
 
 def copy_blocks(pool: np.ndarray, copies) -> np.ndarray:

@@ -1,0 +1,68 @@
+"""The Python binding on the CPU: the package imports and the build module
+runs on a tree with no built library, the library then fails loudly on first
+use, and every entry point refuses a cache that is not
+[2, num_blocks, 16, num_kv_heads, head_dim] before anything is enqueued."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _unbuilt_copy(tmp_path):
+    """The package's sources (no lib/) in a fresh directory."""
+    src = os.path.join(ROOT, "paged_kv_cache_61_amd")
+    dst = tmp_path / "paged_kv_cache_61_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("lib", "__pycache__", "*.so"))
+    return tmp_path
+
+
+def test_import_and_build_module_without_library(tmp_path):
+    tree = _unbuilt_copy(tmp_path)
+    code = ("import paged_kv_cache_61_amd as p, paged_kv_cache_61_amd.build as b, os\n"
+            "assert not os.path.exists(p.lib_path())\n"
+            "assert callable(b.build) and b.sources()\n"
+            "try:\n"
+            "    p._lib.pkv_status_string\n"
+            "except ImportError as e:\n"
+            "    assert 'missing' in str(e); print('raised')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=tree, capture_output=True, text=True,
+                       env=dict(os.environ, PYTHONPATH=str(tree)))
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "raised"
+
+
+BAD_SHAPES = [(2, 4, 8, 2, 64), (1, 4, 16, 2, 64), (2, 4, 16, 2), (2, 0, 16, 2, 64), (3, 4, 16, 2, 64)]
+
+
+@pytest.mark.parametrize("shape", BAD_SHAPES)
+def test_every_entry_point_refuses_a_misshaped_cache(shape):
+    import paged_kv_cache_61_amd as pkv
+    cache = torch.zeros(shape, dtype=torch.bfloat16)
+    i32 = torch.zeros(1, dtype=torch.int32)
+    k = torch.zeros(1, 2, 64, dtype=torch.bfloat16)
+    sm = torch.zeros(1, dtype=torch.int64)
+    q = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    calls = [
+        lambda: pkv.paged_kv_write(k, k, sm, cache),
+        lambda: pkv.paged_attention(q, cache, i32.view(1, 1), i32, torch.zeros(2, dtype=torch.int32), i32,
+                                    0.125, max_query_len=1, max_seq_len=1),
+        lambda: pkv.paged_kv_write_rope(k, k, sm, torch.zeros(4, 64), sm, cache),
+        lambda: pkv.paged_kv_copy_blocks(cache, torch.zeros(1, 2, dtype=torch.int32)),
+    ]
+    codes = cache.to(torch.int8)
+    scales = torch.zeros(2, max(shape[1], 1), 2, 16)
+    calls += [
+        lambda: pkv.paged_kv_write_int8(k, k, sm, codes, scales),
+        lambda: pkv.paged_attention_int8(q, codes, scales, i32.view(1, 1), i32,
+                                         torch.zeros(2, dtype=torch.int32), i32, 0.125,
+                                         max_query_len=1, max_seq_len=1),
+        lambda: pkv.paged_kv_write_fp8(k, k, sm, codes.view(torch.uint8), scales),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="kv_cache_layer must be"):
+            call()

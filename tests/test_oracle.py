@@ -86,6 +86,63 @@ def test_generator_bf16_rounding_matches_torch():
     assert (ours == ref).all()
 
 
+def test_round_to_storage_bf16_hand_worked():
+    """float32 bit patterns -> bf16 bits, each worked out by hand from the
+    rule (keep the top 16 bits; round the low 16 to nearest, ties to even)."""
+    cases = [
+        (0x3F800000, 0x3F80),   # 1.0 exactly
+        (0x3F808000, 0x3F80),   # 1 + 2^-8: a tie, kept mantissa even -> down
+        (0x3F818000, 0x3F82),   # 1 + 3*2^-8: a tie, kept mantissa odd -> up
+        (0x3F808001, 0x3F81),   # just above the tie -> up
+        (0x3F807FFF, 0x3F80),   # just below the tie -> down
+        (0xBF818000, 0xBF82),   # sign does not change the magnitude rule
+        (0x3FFFFFFF, 0x4000),   # 1.99999988: mantissa carry bumps the exponent -> 2.0
+        (0x7F7FFFFF, 0x7F80),   # largest finite float32 rounds up to +inf
+        (0x7F7F7FFF, 0x7F7F),   # below the tie stays the largest finite bf16
+        (0x00008000, 0x0000),   # subnormal tie, even -> +0
+        (0x00018000, 0x0002),   # subnormal tie, odd -> up
+        (0x80008000, 0x8000),   # negative subnormal tie -> -0
+        (0x007FFFFF, 0x0080),   # largest subnormal carries into the smallest normal
+        (0x7F800000, 0x7F80),   # +inf
+        (0xFF800000, 0xFF80),   # -inf
+    ]
+    f32 = np.array([c for c, _ in cases], np.uint32).view(np.float32)
+    got = oracle.round_to_storage(f32.astype(np.float64), "bf16")
+    assert got.tolist() == [b for _, b in cases]
+    # NaN stays NaN, whatever its payload (a plain add-and-shift would turn
+    # 0x7F800001 into infinity and wrap 0xFFFFFFFF round to zero)
+    nans = np.array([0x7FC00000, 0x7F800001, 0xFFFFFFFF, 0xFF800001], np.uint32).view(np.float32)
+    got = oracle.round_to_storage(nans.astype(np.float64), "bf16")
+    assert np.isnan(oracle.bf16_bits_to_f64(got)).all()
+
+
+def test_round_to_storage_goes_through_float32():
+    # 1 + 2^-8 + 2^-40 rounds to float32 1 + 2^-8, a bf16 tie, which goes down
+    # to 1.0 (rounding the float64 straight to bf16 would give 1 + 2^-7)
+    x = np.array([1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24])
+    assert oracle.round_to_storage(x[:1], "bf16").tolist() == [0x3F80]
+    f = oracle.round_to_storage(x[1:], "f32")
+    assert f.dtype == np.float32
+    assert f.tolist() == [1.0, 1 + 2.0 ** -22]       # float32 ties to even
+
+
+def test_round_to_storage_matches_torch():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 32, 400000, dtype=np.uint64).astype(np.uint32)
+    bits[:65536] = (np.arange(65536, dtype=np.uint32) << 16) | 0x8000     # every tie
+    f32 = bits.view(np.float32)
+    x = np.concatenate([f32.astype(np.float64), rng.standard_normal(100000) * 1e3,
+                        rng.standard_normal(1000) * 1e39])               # beyond float32: +-inf
+    ours = oracle.round_to_storage(x, "bf16")
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert (ours[~nan] == ref[~nan]).all()
+    assert (ours[nan] == 0x7FC0).all()
+    ref32 = torch.from_numpy(x).to(torch.float32).numpy()
+    f = oracle.round_to_storage(x, "f32")
+    assert (f.view(np.uint32)[~nan] == ref32.view(np.uint32)[~nan]).all()
+
+
 # ---------------------------------------------------------------------------
 # golden fixtures (hand-worked)
 
