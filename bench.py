@@ -8,8 +8,13 @@ Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
 
-Default workload: Llama-7B-shaped single-layer decode, bf16 (64 sequences,
-32 q / 32 kv heads, head_dim 128, contexts uniform in [512, 4096]).
+Default workload: the mixed continuous-batching step, bf16, token budget 8192
+(3 chunked prefills of 2048 tokens on 0 / 1024 / 4096 cached tokens plus 2048
+decode requests with contexts uniform in [256, 2048]; 32 q / 8 kv heads,
+head_dim 128), the one workload that carries both halves of the metric:
+decode KV-read GB/s against HBM and prefill TFLOP/s against bf16 MFMA.
+``--workload 2`` is the Llama-7B-shaped decode (64 sequences, 32/32 heads),
+3 the GQA decode at 256 sequences, 5 the long-context split-KV decode.
 Prints ONE JSON line.  Only one GPU is supported: ``--gpus`` above 1 exits.
 """
 from __future__ import annotations
@@ -42,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", type=int, default=4, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-int8", action="store_true",
                     help="INT8 KV cache (paged_kv_write_int8 + paged_attention_int8)")
@@ -50,6 +55,8 @@ def parse():
                     help="FP8 (E4M3) KV cache (paged_kv_write_fp8 + paged_attention_fp8)")
     ap.add_argument("--rope", action="store_true",
                     help="write the step's tokens with paged_kv_write_rope (RoPE on K, and on q in place)")
+    ap.add_argument("--no-peak-probes", action="store_true",
+                    help="skip the measured-peak probes (a device copy and a bf16 GEMM)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="CPU seconds the oracle baseline may spend on its sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -92,46 +99,105 @@ def accounting(wl):
 
 
 def cpu_baseline(wl, acct, budget_s):
-    """Time the fp64 oracle on a bounded sample of the same workload."""
+    """Time the fp64 oracle, as it stands, on a bounded sample of the same step.
+
+    The sample is cut into independent pieces (a decode request, or a run of
+    64 consecutive rows of a prefill chunk) that run on a pool of host threads,
+    one BLAS thread each, until about ``budget_s`` seconds of wall time are
+    spent.  Decode pieces are scaled to the step by KV tokens read, prefill
+    pieces by algorithmic FLOPs; the step time estimated from both is reported
+    in the unit of the step's ``value`` (algorithmic bytes per second).  The
+    oracle's cache write is not timed: it returns a fresh copy of the whole
+    pool (a property of its plain form, not of the write)."""
+    import concurrent.futures as cf
     import numpy as np
     import oracle
-    order = np.random.default_rng(1234).permutation(wl.num_reqs)
+    from threadpoolctl import threadpool_limits
+    threads = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                         else (os.cpu_count() or 1)))
+    rng = np.random.default_rng(1234)
     ql = wl.query_lens
-    s = 2 if wl.dtype == "bf16" else 4
-    kv_token_bytes = 2 * wl.num_kv_heads * wl.head_dim * s
+    qsl = wl.query_start_loc
+    D, Hq = wl.head_dim, wl.num_q_heads
+    pieces = []                                # (kind, tokens, work)
+    dec = [int(r) for r in rng.permutation(np.nonzero(ql == 1)[0])]
+    pre = [int(r) for r in np.nonzero(ql > 1)[0]]
+    runs = []
+    for r in pre:                             # runs of 64 rows at random places of each chunk
+        c = int(wl.num_computed_tokens[r])
+        for i0 in rng.permutation(np.arange(0, int(ql[r]), 64)):
+            toks = list(range(int(qsl[r]) + int(i0), min(int(qsl[r]) + int(i0) + 64, int(qsl[r + 1]))))
+            flops = sum(4 * D * Hq * (c + t - int(qsl[r]) + 1) for t in toks)
+            runs.append(("prefill", toks, flops))
+    runs = [runs[i] for i in rng.permutation(len(runs))]
+    # interleave so a bounded run samples both kinds in proportion to their cost
+    di = 0
+    for run in runs:
+        pieces.append(run)
+        for _ in range(max(1, len(dec) // max(1, len(runs)))):
+            if di < len(dec):
+                pieces.append(("decode", [int(qsl[dec[di]])], int(wl.seq_lens[dec[di]])))
+                di += 1
+    pieces += [("decode", [int(qsl[r])], int(wl.seq_lens[r])) for r in dec[di:]]
+    # the step's tokens placed in the host pool in place (the oracle's own
+    # write returns a copy of the whole pool, which is not the write's cost)
+    sm = wl.slot_mapping
+    live = sm >= 0
+    pool = wl.pool
+    pool[0, sm[live] // 16, sm[live] % 16] = wl.k_new[live]
+    pool[1, sm[live] // 16, sm[live] % 16] = wl.v_new[live]
+
+    def one(piece):
+        kind, toks, work = piece
+        t = time.perf_counter()
+        oracle.attention_rows(wl.q, pool, wl.block_table, wl.seq_lens, qsl, wl.num_computed_tokens,
+                              wl.scale, wl.dtype, tokens=toks, max_run=64)
+        return kind, work, time.perf_counter() - t
+
+    done = {"decode": [0, 0.0, 0], "prefill": [0, 0.0, 0]}    # work, thread-seconds, pieces
     t0 = time.perf_counter()
-    pool = oracle.kv_write(wl.pool, wl.k_new, wl.v_new, wl.slot_mapping)
-    done_bytes = 0
-    done_flops = 0
-    n = 0
-    rows = 0
-    for r in order:
-        if ql[r] == 0:
-            continue
-        if ql[r] == 1:
-            oracle.attention(wl.q, pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
-                             wl.num_computed_tokens, wl.scale, wl.dtype, requests=[int(r)])
-            done_bytes += int(wl.seq_lens[r]) * kv_token_bytes
-            rows += 1
-        else:  # a prefill chunk: sample 8 of its rows
-            qs = int(wl.query_start_loc[r])
-            pick = np.linspace(qs, qs + int(ql[r]) - 1, 8).astype(int).tolist()
-            oracle.attention_rows(wl.q, pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
-                                  wl.num_computed_tokens, wl.scale, wl.dtype, tokens=pick)
-            c = int(wl.num_computed_tokens[r])
-            done_flops += sum(4 * wl.head_dim * wl.num_q_heads * (c + t - qs + 1) for t in pick)
-            rows += len(pick)
-        n += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    if acct["decode_rows"] > 0:
-        value, unit = done_bytes / dt / 1e9, "GB/s"
-    else:
-        value, unit = done_flops / dt / 1e12, "TFLOP/s"
-    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {wl.num_reqs} requests ({rows} query rows) in seeded random order, "
-                      f"cache write included, {dt:.1f} s single-threaded numpy fp64",
+    with threadpool_limits(1), cf.ThreadPoolExecutor(threads) as ex:
+        it = iter(pieces)
+        live = set()
+        for _ in range(threads):
+            p_ = next(it, None)
+            if p_ is not None:
+                live.add(ex.submit(one, p_))
+        while live:
+            fin, live = cf.wait(live, return_when=cf.FIRST_COMPLETED)
+            for f in fin:
+                kind, work, dt = f.result()
+                done[kind][0] += work
+                done[kind][1] += dt
+                done[kind][2] += 1
+            if time.perf_counter() - t0 < budget_s:
+                for _ in fin:
+                    p_ = next(it, None)
+                    if p_ is not None:
+                        live.add(ex.submit(one, p_))
+    wall = time.perf_counter() - t0
+    busy = done["decode"][1] + done["prefill"][1]
+    # thread-seconds per unit of work, spread over the threads that ran
+    est = 0.0
+    parts = {}
+    if acct["decode_rows"] and done["decode"][0]:
+        per_tok = done["decode"][1] / done["decode"][0]
+        t_dec = per_tok * acct["decode_kv_tokens"] / threads
+        est += t_dec
+        parts["decode_GB/s"] = round(acct["decode_bytes"] / t_dec / 1e9, 4)
+    if acct["prefill_flops"] and done["prefill"][0]:
+        per_flop = done["prefill"][1] / done["prefill"][0]
+        t_pf = per_flop * acct["prefill_flops"] / threads
+        est += t_pf
+        parts["prefill_TFLOP/s"] = round(acct["prefill_flops"] / t_pf / 1e12, 6)
+    step_bytes = acct["decode_bytes"] + acct["prefill_bytes"]
+    return {"value": round(step_bytes / est / 1e9, 4) if est > 0 else None, "unit": "GB/s",
+            "cores": threads, "kind": "oracle", **parts,
+            "estimated_step_s": round(est, 3),
+            "sample": f"{done['decode'][2]} decode requests and {done['prefill'][2]} prefill runs of <= 64 rows "
+                      f"(seeded random order) in {wall:.1f} s on {threads} threads ({busy:.1f} thread-s); "
+                      "numpy fp64 oracle, one BLAS thread per worker; per-KV-token and per-FLOP costs scaled "
+                      "to the whole step (attention only; the cache write is not timed)",
             "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
 
 
@@ -231,18 +297,60 @@ def row_kernel_name(wl, kv8):
     return "row_attn_kernel (decode rows + split-KV partitions)"
 
 
-def measured_traffic(workload):
-    """HBM bytes per row-kernel launch from the committed PMC summary, if it was
-    taken on this workload and on the current decode kernel source; else None."""
+WORKLOAD_TAGS = {2: "decode_llama7b_bs64", 3: "decode_gqa_bs256", 4: "mixed_step_8192",
+                 5: "decode_long_context_g8"}
+
+
+def measured_traffic(workload, role):
+    """HBM bytes per launch of the ``role`` kernel ("rows" or "prefill") from the
+    committed PMC record of this workload, if it was taken on the kernel's
+    current source; else None."""
     import hashlib
-    rec_path = os.path.join(ROOT, "profiles", "decode_llama7b_bs64_traffic.json")
-    src_path = os.path.join(ROOT, "paged_kv_cache_61_amd", "csrc", "decode.hip")
-    if workload != 2 or not os.path.exists(rec_path):
+    tag = WORKLOAD_TAGS.get(workload)
+    if tag is None:
         return None
-    rec = json.load(open(rec_path))
-    if hashlib.sha256(open(src_path, "rb").read()).hexdigest() != rec.get("decode_hip_sha256"):
+    rec_path = os.path.join(ROOT, "profiles", f"{tag}_traffic.json")
+    if not os.path.exists(rec_path):
+        return None
+    rec = json.load(open(rec_path)).get("kernels", {}).get(role)
+    if not rec:
+        return None
+    src_path = os.path.join(ROOT, "paged_kv_cache_61_amd", "csrc", rec["source"])
+    if hashlib.sha256(open(src_path, "rb").read()).hexdigest() != rec.get("source_sha256"):
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def peak_probes():
+    """Measured ceilings on this GPU: a device-to-device copy (torch copy_,
+    2 GiB each way) and a dense bf16 GEMM (torch.matmul, 8192^3, hipBLASLt)."""
+    import torch
+    res = {}
+    n = (2 << 30) // 4
+    src = torch.empty(n, device="cuda", dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    for name, fn, work in (("copy_GB/s", lambda: dst.copy_(src), 2 * n * 4 / 1e9),
+                           ("bf16_gemm_TFLOP/s", lambda: torch.matmul(a, b), 2 * 8192 ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(work / (e0.elapsed_time(e1) / 10 * 1e-3), 1)
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def pct(xs, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(xs), q)), 5)
 
 
 def main():
@@ -344,6 +452,8 @@ def main():
                             max_seq_len=wl.max_seq_len, out=out, workspace=ws,
                             phase_events=None if evs is None else evs[:2 * nph])
 
+    probes = None if args.no_peak_probes else peak_probes()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -352,19 +462,22 @@ def main():
         raise SystemExit(f"device error word {err:#x}")
 
     # Timed region 1: K plain steps (the library calls exactly as a caller
-    # makes them) -> ms_per_step and the whole-step throughput.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # makes them) -> ms_per_step and the whole-step throughput.  An event
+    # between steps gives the spread of single steps.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e in marks:
+        e.record()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record()
+    marks[0].record()
     for i in range(args.steps):
         step()
-    end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
+    total_ms = marks[0].elapsed_time(marks[-1])
     ms_per_step = total_ms / args.steps
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     # Timed region 2: K more steps with hipEvents recorded by the library on
     # its own stream around each internal phase -> per-kernel launch times
     # (the events add a few microseconds per step, so region 1 gives the
@@ -374,9 +487,9 @@ def main():
         step(step_events[i])
     torch.cuda.synchronize()
     names = ["plan", "prefill", "rows", "reduce"]
-    phase_ms = {}
-    for p, nm in enumerate(names):
-        phase_ms[nm] = float(np.mean([evs[2 * p].elapsed_time(evs[2 * p + 1]) for evs in step_events]))
+    phase_all = {nm: [evs[2 * p].elapsed_time(evs[2 * p + 1]) for evs in step_events]
+                 for p, nm in enumerate(names)}
+    phase_ms = {nm: float(np.mean(v)) for nm, v in phase_all.items()}
 
     write_ms = float(np.mean([evs[2 * nph].elapsed_time(evs[2 * nph + 1]) for evs in step_events]))
     write_bytes = acct["write_rope_bytes"] if args.rope else acct["write_bytes"]
@@ -389,6 +502,40 @@ def main():
         step_bytes = dec_bytes + acct["prefill_bytes"] + write_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     rows_gbs = dec_bytes / (phase_ms["rows"] * 1e-3) / 1e9 if phase_ms["rows"] > 0 else 0.0
+    roof_rows = {
+        "kernel": row_kernel_name(wl, kv8),
+        "bound": "hbm",
+        "achieved": round(rows_gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None if kv8 else measured_traffic(args.workload, "rows"),
+        "algorithmic_bytes_per_launch": dec_bytes,
+        "avg_launch_ms": round(phase_ms["rows"], 5),
+        "launch_ms_p10": pct(phase_all["rows"], 10), "launch_ms_p90": pct(phase_all["rows"], 90),
+    }
+    if probes:
+        roof_rows["frac_of_measured_copy"] = round(rows_gbs / probes["copy_GB/s"], 4)
+    roof_pf = None
+    if acct["prefill_flops"] > 0 and phase_ms["prefill"] > 0.02:
+        tf = acct["prefill_flops"] / (phase_ms["prefill"] * 1e-3) / 1e12
+        roof_pf = {
+            "kernel": "prefill_kernel (chunked prefill on bf16 MFMA"
+                      + (f", {kv8} cache dequantised in LDS)" if kv8 else ")"),
+            "bound": "mfma",
+            "achieved": round(tf, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None if kv8 else measured_traffic(args.workload, "prefill"),
+            "algorithmic_flops_per_launch": acct["prefill_flops"],
+            "avg_launch_ms": round(phase_ms["prefill"], 5),
+            "launch_ms_p10": pct(phase_all["prefill"], 10), "launch_ms_p90": pct(phase_all["prefill"], 90),
+        }
+        if probes:
+            roof_pf["frac_of_measured_gemm"] = round(tf / probes["bf16_gemm_TFLOP/s"], 4)
+    # the dominant kernel (longest launch) is the line's "roofline"
+    dominant_is_pf = roof_pf is not None and phase_ms["prefill"] > phase_ms["rows"]
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -397,6 +544,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_ms_p10": pct(step_ms, 10), "step_ms_p50": pct(step_ms, 50), "step_ms_p90": pct(step_ms, 90),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -405,22 +553,14 @@ def main():
         "config": {
             "workload": f"{WORKLOAD_NAMES[args.workload]}: {wl.spec.name}",
             "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
+            "decode_rows": acct["decode_rows"], "prefill_rows": int(wl.num_tokens - acct["decode_rows"]),
             "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
             "head_dim": wl.head_dim, "block_size": 16, "num_blocks": wl.num_blocks,
             "decode_kv_tokens": acct["decode_kv_tokens"], "max_seq_len": wl.max_seq_len,
             "kv_cache": (f"{kv8} codes + float32 scale per (token, kv head)" if kv8 else wl.dtype),
         },
-        "roofline": {
-            "kernel": row_kernel_name(wl, kv8),
-            "bound": "hbm",
-            "achieved": round(rows_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if kv8 else measured_traffic(args.workload),
-            "algorithmic_bytes_per_launch": dec_bytes,
-            "avg_launch_ms": round(phase_ms["rows"], 5),
-        },
+        "roofline": roof_pf if dominant_is_pf else roof_rows,
+        "rooflines": {"decode_rows": roof_rows, **({"prefill": roof_pf} if roof_pf else {})},
         "phases_ms": {k: round(v, 5) for k, v in phase_ms.items()},
         "write": {"kernel": ("kv_write_rope_kernel (RoPE on K and q)" if args.rope else
                              f"kv_write_i8_kernel ({kv8} quantising)" if kv8 else "kv_write_kernel"),
@@ -430,10 +570,19 @@ def main():
         "wall_s_timed": round(wall_s, 4),
         "input_gen_s": round(gen_s, 2),
     }
-    if acct["prefill_flops"] > 0 and phase_ms["prefill"] > 0.02:
-        tf = acct["prefill_flops"] / (phase_ms["prefill"] * 1e-3) / 1e12 if phase_ms["prefill"] > 0 else 0.0
-        result["prefill"] = {"flops": acct["prefill_flops"], "tflops": round(tf, 2),
-                             "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if roof_pf:
+        result["prefill_tflops"] = roof_pf["achieved"]
+        result["prefill_frac_mfma_bf16"] = roof_pf["frac"]
+        # the step against its two rooflines: bytes at 8 TB/s and FLOPs at 2.5 PFLOP/s
+        t_mem = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        t_fl = acct["prefill_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+        result["step_vs_roofline"] = {"bytes_ms_at_peak": round(t_mem, 5), "flops_ms_at_peak": round(t_fl, 5),
+                                      "measured_over_max": round(ms_per_step / max(t_mem, t_fl), 4),
+                                      "measured_over_sum": round(ms_per_step / (t_mem + t_fl), 4)}
+    result["decode_kv_read_GB/s"] = roof_rows["achieved"]
+    result["decode_frac_hbm"] = roof_rows["frac"]
+    if probes:
+        result["measured_peaks"] = probes
     if not args.no_cpu_baseline and world == 1:
         result["cpu_baseline"] = cpu_baseline(wl, acct, args.cpu_budget_s)
     print(json.dumps(result), flush=True)

@@ -36,9 +36,11 @@
  *    enqueued: the calls return before the GPU finishes, never synchronise,
  *    never allocate and never free.  The caller keeps every buffer alive until
  *    the stream reaches that point.
- *  - The calls keep no global mutable state and may be made from several host
- *    threads at once.  Two calls that share a workspace must be ordered on one
- *    stream.
+ *  - The calls may be made from several host threads at once.  The only
+ *    process-wide state is a per-kernel cache of the occupancy the HIP runtime
+ *    reports (filled on first use with the same value by every caller) and the
+ *    per-thread error detail string.  Two calls that share a workspace must be
+ *    ordered on one stream.
  *  - Errors are returned as a pkv_status, never thrown.  Argument errors are
  *    detected on the host before anything is enqueued.  Bad *contents* of
  *    device metadata (inconsistent lengths, out-of-range block ids or slots)

@@ -290,15 +290,32 @@ def request_weights(q_rows: np.ndarray, K: np.ndarray, computed: int, scale: flo
     """Softmax weights ``[ql, Hq, L]`` of one request (float64).
 
     Query row ``i`` is at absolute position ``computed + i`` and sees keys
-    ``t <= computed + i``.  Query head ``h`` reads KV head ``h // (Hq // Hkv)``."""
-    ql = q_rows.shape[0]
+    ``t <= computed + i``.  Query head ``h`` reads KV head ``h // (Hq // Hkv)``,
+    so the scores are formed one KV head at a time: its ``G = Hq // Hkv``
+    query heads, all rows, times that head's keys (one matrix product)."""
+    ql, _, D = q_rows.shape
     L, Hkv, _ = K.shape
-    group = num_q_heads // Hkv
-    kv_of_head = np.arange(num_q_heads) // group
-    Kh = K[:, kv_of_head, :]                                   # [L, Hq, D]
-    scores = np.einsum("ihd,thd->iht", q_rows, Kh) * scale     # [ql, Hq, L]
+    G = num_q_heads // Hkv
+    scores = np.empty((ql, num_q_heads, L))
+    for g in range(Hkv):
+        heads = slice(g * G, (g + 1) * G)
+        qg = q_rows[:, heads, :].reshape(ql * G, D)
+        scores[:, heads, :] = (np.matmul(qg, K[:, g, :].T) * scale).reshape(ql, G, L)
     visible = (np.arange(L)[None, :] <= (computed + np.arange(ql))[:, None])[:, None, :]
     return _softmax_rows(scores, visible)
+
+
+def weighted_values(w: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """``out [ql, Hq, D] = sum_t w[i, h, t] V[t, h // G]`` (float64), one KV
+    head at a time (its G query heads share that head's values)."""
+    ql, Hq, L = w.shape
+    _, Hkv, D = V.shape
+    G = Hq // Hkv
+    out = np.empty((ql, Hq, D))
+    for g in range(Hkv):
+        heads = slice(g * G, (g + 1) * G)
+        out[:, heads, :] = np.matmul(w[:, heads, :].reshape(ql * G, L), V[:, g, :]).reshape(ql, G, D)
+    return out
 
 
 def attention(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
@@ -322,9 +339,7 @@ def attention(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
             continue
         K, V = gather_kv(pool, block_table[r], L, dtype)
         qf = to_f64(q[qs:qe], dtype)
-        w = request_weights(qf, K, c, scale, Hq)               # [ql, Hq, L]
-        Vh = V[:, np.arange(Hq) // (Hq // Hkv), :]             # [L, Hq, D]
-        out[qs:qe] = np.einsum("iht,thd->ihd", w, Vh)
+        out[qs:qe] = weighted_values(request_weights(qf, K, c, scale, Hq), V)
     return out
 
 
@@ -351,22 +366,33 @@ def attention_fp8(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, block_ta
 def attention_rows(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
                    seq_lens: np.ndarray, query_start_loc: np.ndarray,
                    num_computed_tokens: np.ndarray, scale: float, dtype: str,
-                   tokens: Sequence[int]) -> np.ndarray:
-    """``out[t]`` (all heads, float64) for the chosen token rows only."""
+                   tokens: Sequence[int], max_run: int = 256) -> np.ndarray:
+    """``out[t]`` (all heads, float64) for the chosen token rows only.
+
+    Consecutive chosen rows of one request (at most ``max_run`` of them) are
+    computed together: row ``t`` of request ``r`` is at absolute position
+    ``p = computed + (t - query_start)`` and sees keys ``0 .. p``, so a run
+    starting at row ``t0`` is the request's attention with ``computed + (t0 -
+    query_start)`` tokens before it."""
     Hq = q.shape[1]
-    Hkv = pool.shape[3]
-    res = []
-    for t in tokens:
-        r = int(np.searchsorted(query_start_loc, t, side="right") - 1)
-        qs = int(query_start_loc[r])
+    tokens = [int(t) for t in tokens]
+    res = np.empty((len(tokens), Hq, q.shape[2]))
+    i = 0
+    while i < len(tokens):
+        t0 = tokens[i]
+        r = int(np.searchsorted(query_start_loc, t0, side="right") - 1)
+        qs, qe = int(query_start_loc[r]), int(query_start_loc[r + 1])
         L, c = int(seq_lens[r]), int(num_computed_tokens[r])
-        _check_request(r, L, c, int(query_start_loc[r + 1]) - qs)
-        p = c + (t - qs)                        # absolute position of this query
-        K, V = gather_kv(pool, block_table[r], p + 1, dtype)
-        w = request_weights(to_f64(q[t:t + 1], dtype), K, p, scale, Hq)[0]   # [Hq, p+1]
-        Vh = V[:, np.arange(Hq) // (Hq // Hkv), :]
-        res.append(np.einsum("ht,thd->hd", w, Vh))
-    return np.stack(res) if res else np.zeros((0, Hq, q.shape[2]))
+        _check_request(r, L, c, qe - qs)
+        n = 1
+        while i + n < len(tokens) and n < max_run and tokens[i + n] == t0 + n and t0 + n < qe:
+            n += 1
+        p0 = c + (t0 - qs)                      # absolute position of the run's first query
+        K, V = gather_kv(pool, block_table[r], p0 + n, dtype)
+        w = request_weights(to_f64(q[t0:t0 + n], dtype), K, p0, scale, Hq)   # [n, Hq, p0+n]
+        res[i:i + n] = weighted_values(w, V)
+        i += n
+    return res
 
 
 # ---------------------------------------------------------------------------

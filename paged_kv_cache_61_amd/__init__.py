@@ -50,7 +50,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "lib", "libpagedkv.so")
+    """``lib/libpagedkv.so``, or the library ``PAGED_KV_LIBRARY`` names (the
+    sanitizer build, for CPU-side test runs)."""
+    return os.environ.get("PAGED_KV_LIBRARY") or os.path.join(_HERE, "lib", "libpagedkv.so")
 
 
 class PagedKVError(RuntimeError):

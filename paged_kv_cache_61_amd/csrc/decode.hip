@@ -12,9 +12,10 @@
 // Decode is memory bound (same page, "Prefill vs Decode"): each K/V byte is
 // used G times and then never again, so the kernel is built to stream the
 // cache at full HBM bandwidth:
-//  * a workgroup (4 waves) owns one work item = (row, kv head, partition of
-//    512 tokens); wave w takes blocks w, w+4, ... of the partition and keeps
-//    its own online-softmax state; the 4 states are merged through LDS;
+//  * a work item is (row, kv head, partition of 512 tokens); every wave is an
+//    independent persistent worker that takes items in a fixed interleaved
+//    order and streams all blocks of its item itself (the 4 waves of a
+//    workgroup share nothing but the CU; each has its own small LDS tile);
 //  * a wave reads one whole 16-token block of its kv head per step: K with
 //    16-byte buffer loads in a "4 lanes per token" layout (lane = token * 4 +
 //    quarter), V with one dword per lane per token in a "lanes own head_dim
@@ -845,7 +846,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void r
 
 // Persistent grid: as many 4-wave workgroups as fit on the device at once,
 // but no more than the work items need.
-// (One cached occupancy per kernel: the template argument is the kernel.)
+// (One cached occupancy per kernel: the template argument is the kernel.  The
+// cache is the library's only process-wide state: written once per kernel
+// with the value the runtime reports, which is the same for every caller, so
+// concurrent first calls race benignly.)
 template <auto K>
 int64_t persistent_grid(int64_t bound_wgs, int cus) {
   static std::atomic<int> occ_cache{0};

@@ -93,6 +93,32 @@ def oracle_out(wl: workloads.Workload, pool: np.ndarray, tokens=None) -> np.ndar
     return oracle.attention_rows(*args, tokens=tokens)
 
 
+def host_threads() -> int:
+    """Worker threads for the oracle on the host: every CPU the process may
+    use, at most 16 (the GPU machines give one GPU's job 16 CPUs)."""
+    import os
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def oracle_rows_parallel(q: np.ndarray, pool: np.ndarray, wl: workloads.Workload, tokens, dtype: str,
+                         chunk: int = 128) -> np.ndarray:
+    """``oracle.attention_rows`` for ``tokens`` (sorted), cut into chunks of
+    ``chunk`` rows that run on a pool of threads, each with one BLAS thread
+    (the oracle's matrix products and exponentials release the GIL)."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+    tokens = [int(t) for t in tokens]
+    parts = [tokens[i:i + chunk] for i in range(0, len(tokens), chunk)]
+
+    def one(part):
+        return oracle.attention_rows(q, pool, wl.block_table, wl.seq_lens, wl.query_start_loc,
+                                     wl.num_computed_tokens, wl.scale, dtype, tokens=part, max_run=chunk)
+    with threadpool_limits(1), cf.ThreadPoolExecutor(host_threads()) as ex:
+        res = list(ex.map(one, parts))
+    return np.concatenate(res) if res else np.zeros((0,) + tuple(q.shape[1:]))
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> dict:
     err = np.abs(got - ref)
     tol = TOL[dtype]
@@ -116,20 +142,41 @@ def scales_from_dev(t: torch.Tensor) -> np.ndarray:
     return np.ascontiguousarray(t.cpu().numpy().transpose(0, 1, 3, 2))
 
 
-def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
+def _quantise_blocks_parallel(quant, pool_sub: np.ndarray, dtype: str, step: int = 1024):
+    """The oracle's quantisation of ``pool_sub [2, nb, 16, Hkv, D]``, row by
+    row (every (token, kv head) row is independent), in slices of blocks on a
+    pool of threads."""
+    import concurrent.futures as cf
+    nb = pool_sub.shape[1]
+    codes = np.empty(pool_sub.shape, np.int8 if quant is oracle.quantize_int8 else np.uint8)
+    scales = np.empty(pool_sub.shape[:-1], np.float32)
+
+    def one(lo):
+        c, sc = quant(pool_sub[:, lo:lo + step], dtype)
+        codes[:, lo:lo + step] = c
+        scales[:, lo:lo + step] = sc
+    with cf.ThreadPoolExecutor(host_threads()) as ex:
+        list(ex.map(one, range(0, nb, step)))
+    return codes, scales
+
+
+def eightbit_full(fmt: str, n: int, seed: int, all_rows: bool = False) -> None:
     """An 8-bit cache (``fmt`` "int8" or "fp8") at a benchmark workload's full
     size, in the benchmark's launch configuration: the whole pool quantised on
-    the device, the step's tokens written, one attention call.  Checked on a
-    sample: the codes and scales of every block the sampled rows read, bit for
-    bit against the oracle's quantisation of the same (written) pool, and the
-    sampled rows against the oracle's attention over those dequantised blocks."""
+    the device, the step's tokens written, one attention call.  The codes and
+    scales of every block the checked rows read are compared bit for bit with
+    the oracle's quantisation of the same (written) pool, and the checked rows
+    with the oracle's attention over those dequantised blocks.  Checked rows:
+    every row when ``all_rows``, else the first, last and random rows of each
+    prefill chunk and 48 random decode rows."""
     import paged_kv_cache_61_amd as pkv
     write8 = pkv.paged_kv_write_int8 if fmt == "int8" else pkv.paged_kv_write_fp8
     attend8 = pkv.paged_attention_int8 if fmt == "int8" else pkv.paged_attention_fp8
     quant = oracle.quantize_int8 if fmt == "int8" else oracle.quantize_fp8
     deq = oracle.dequantize_int8 if fmt == "int8" else oracle.dequantize_fp8
     wl = workloads.build(workloads.BENCH_WORKLOADS[n])
-    print(f"[case] {fmt} workload {n}: {wl.spec.name}", flush=True)
+    print(f"[case] {fmt} workload {n}: {wl.spec.name} ({'all rows' if all_rows else 'sampled rows'})",
+          flush=True)
     s = upload(wl)
     NB, Hkv, D = wl.num_blocks, wl.num_kv_heads, wl.head_dim
     codes = torch.empty(tuple(s.pool.shape), dtype=torch.int8 if fmt == "int8" else torch.uint8, device="cuda")
@@ -142,33 +189,41 @@ def eightbit_full_sampled(fmt: str, n: int, seed: int) -> None:
             max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, out=s.out, workspace=s.workspace)
     torch.cuda.synchronize()
     assert device_error(s) == 0
-    # sampled rows and the blocks they read
-    rng = np.random.default_rng(seed)
     qsl, ql = wl.query_start_loc, np.diff(wl.query_start_loc)
-    rows = []
-    for r in np.nonzero(ql > 1)[0][:4]:  # prefill chunks: first, last and random rows
-        rows += [int(qsl[r]), int(qsl[r + 1]) - 1] + rng.integers(qsl[r], qsl[r + 1], 10).tolist()
-    dec = np.nonzero(ql == 1)[0]
-    rows += [int(qsl[r]) for r in rng.choice(dec, min(48, len(dec)), replace=False)]
-    rows = sorted(set(rows))
+    if all_rows:
+        rows = list(range(wl.num_tokens))
+    else:
+        rng = np.random.default_rng(seed)
+        rows = []
+        for r in np.nonzero(ql > 1)[0][:4]:  # prefill chunks: first, last and random rows
+            rows += [int(qsl[r]), int(qsl[r + 1]) - 1] + rng.integers(qsl[r], qsl[r + 1], 10).tolist()
+        dec = np.nonzero(ql == 1)[0]
+        rows += [int(qsl[r]) for r in rng.choice(dec, min(48, len(dec)), replace=False)]
+        rows = sorted(set(rows))
     reqs = sorted({int(np.searchsorted(qsl, t, side="right") - 1) for t in rows})
     blocks = sorted({int(b) for r in reqs for b in wl.block_table[r, :(int(wl.seq_lens[r]) + 15) // 16]})
     ref_pool = oracle_pool(wl)[:, blocks]                         # [2, nsub, 16, Hkv, D]
     with np.errstate(invalid="ignore"):
         live = ~np.isnan(oracle.to_f64(ref_pool, wl.dtype)).any(axis=-1)   # unused slots are NaN
-    rc, rs = quant(np.where(live[..., None], ref_pool, 0).astype(ref_pool.dtype), wl.dtype)
+    rc, rs = _quantise_blocks_parallel(quant, np.where(live[..., None], ref_pool, 0).astype(ref_pool.dtype),
+                                       wl.dtype)
+    del ref_pool
     idx = torch.tensor(blocks, dtype=torch.int64, device="cuda")
     gc = codes.index_select(1, idx).cpu().numpy()
     gs = scales_from_dev(scales.index_select(1, idx))
     assert np.array_equal(gc[live], rc[live]), "codes differ"
     assert gs[live].tobytes() == rs[live].tobytes(), "scales differ"
+    del gc, gs
     # attention over the dequantised blocks (block ids remapped to the subset)
-    remap = {b: i for i, b in enumerate(blocks)}
+    remap = np.full(NB, -1, np.int64)
+    remap[blocks] = np.arange(len(blocks))
     bt = np.zeros_like(wl.block_table)
     for r in reqs:
         nb_r = (int(wl.seq_lens[r]) + 15) // 16
-        bt[r, :nb_r] = [remap[int(b)] for b in wl.block_table[r, :nb_r]]
+        bt[r, :nb_r] = remap[wl.block_table[r, :nb_r]]
     pool_deq = np.where(live[..., None], deq(rc, rs), 0.0)
-    ref = oracle.attention_rows(oracle.to_f64(wl.q, wl.dtype), pool_deq, bt, wl.seq_lens, qsl,
-                                wl.num_computed_tokens, wl.scale, "f64", tokens=rows)
-    assert_close(out_f64(s.out)[rows], ref, wl.dtype, f"{fmt} workload {n} sampled")
+    del rc, rs
+    sub = dataclasses.replace(wl, block_table=bt)
+    ref = oracle_rows_parallel(oracle.to_f64(wl.q, wl.dtype), pool_deq, sub, rows, "f64")
+    assert_close(out_f64(s.out)[rows], ref, wl.dtype,
+                 f"{fmt} workload {n} {'all rows' if all_rows else 'sampled'}")

@@ -30,8 +30,9 @@ def test_import_and_build_module_without_library(tmp_path):
             "    p._lib.pkv_status_string\n"
             "except ImportError as e:\n"
             "    assert 'missing' in str(e); print('raised')\n")
+    env = {k: v for k, v in os.environ.items() if k != "PAGED_KV_LIBRARY"}
     r = subprocess.run([sys.executable, "-c", code], cwd=tree, capture_output=True, text=True,
-                       env=dict(os.environ, PYTHONPATH=str(tree)))
+                       env=dict(env, PYTHONPATH=str(tree)))
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "raised"
 

@@ -146,9 +146,12 @@ def test_int8_write_zero_rows_and_padding():
     assert rs[0, 1, 1].tolist() == [0.0, 0.0]
 
 
-@pytest.mark.parametrize("n", [2, 4])
-def test_int8_workload_full_sampled(n):
-    # the benchmark's decode and mixed-step workloads at full size, sampled
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n,all_rows", [(2, True), (4, False), (5, True)])
+def test_int8_workload_full_size(n, all_rows):
+    # the benchmark's decode, mixed-step and long-context (64 split-KV
+    # partitions per row) workloads at full size: every row of the decode
+    # workloads, sampled rows of the mixed step
     _gpu()
-    from gpu_util import eightbit_full_sampled
-    eightbit_full_sampled("int8", n, 70 + n)
+    from gpu_util import eightbit_full
+    eightbit_full("int8", n, 70 + n, all_rows=all_rows)

@@ -424,6 +424,14 @@ def test_rows_agree_with_full():
     rows = [0, 1, 5, 18, 19, 24]
     np.testing.assert_allclose(oracle.attention_rows(*args, tokens=rows), full[rows],
                                rtol=0, atol=1e-13)
+    # runs of consecutive rows, across request boundaries, with every run length
+    rows = list(range(wl.num_tokens))
+    for run in (1, 2, 3, 5, 256):
+        np.testing.assert_allclose(oracle.attention_rows(*args, tokens=rows, max_run=run), full,
+                                   rtol=0, atol=1e-13)
+    rows = [3, 4, 5, 6, 17, 18, 19, 20, 21, 22, 23, 24]
+    np.testing.assert_allclose(oracle.attention_rows(*args, tokens=rows, max_run=3), full[rows],
+                               rtol=0, atol=1e-13)
 
 
 # ---------------------------------------------------------------------------
