@@ -177,6 +177,35 @@ int paged_attention_profiled(void* out, const void* q, const void* kv_cache_laye
                              void* const* phase_events);
 
 /*
+ * paged_attention_noalloc — paged_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation and results, with the
+ * workspace taken from a static device array of PKV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ * Arguments are those of paged_attention without workspace / workspace_bytes;
+ * the caller still owns q, out, the cache and the metadata.  It calls no
+ * hipMalloc, hipFree or allocating library routine.
+ *   device_error    device int32, or NULL.  When non-NULL, the step's
+ *                   PKV_DEVERR_* bits are OR-ed into it (the scratch is not
+ *                   visible to the caller, so pkv_read_device_error does not
+ *                   apply).
+ * Returns PKV_ERR_WORKSPACE, before anything is enqueued, when
+ * paged_attention_workspace_size for these bounds would exceed the scratch.
+ * Every call on one GPU uses that GPU's one scratch array, which keeps the
+ * last call's contents (each call rebuilds what it reads): calls that may
+ * overlap on one GPU (several streams or threads) race and must be ordered
+ * by the caller.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (128u << 20)
+int paged_attention_noalloc(void* out, const void* q, const void* kv_cache_layer,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                            float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                            int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                            int32_t dtype, int32_t* device_error, void* stream);
+
+/*
  * paged_attention_workspace_size — bytes of workspace paged_attention needs
  * for these bounds (same meaning as its arguments).  Returns 0 for invalid
  * sizes.  Pure host function.

@@ -35,7 +35,7 @@ __all__ = [
     "DEVERR_SEQ_LEN", "DEVERR_LIMITS", "DEVERR_QSL", "DEVERR_BLOCK_ID", "DEVERR_SLOT",
     "DEVERR_CAPACITY", "DEVERR_POSITION", "BLOCK_SIZE", "paged_kv_copy_blocks", "paged_kv_write_rope",
     "paged_kv_write_int8", "paged_attention_int8", "paged_kv_write_fp8", "paged_attention_fp8",
-    "BlockManager", "Step",
+    "BlockManager", "Step", "paged_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 BLOCK_SIZE = 16
@@ -89,6 +89,9 @@ def load_library() -> ctypes.CDLL:
     lib.paged_attention.restype = ctypes.c_int
     lib.paged_attention_profiled.argtypes = lib.paged_attention.argtypes + [vp]
     lib.paged_attention_profiled.restype = ctypes.c_int
+    lib.paged_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i64, i32, i32, i32, i32,
+                                            i32, i32, i32, i32, vp, vp]
+    lib.paged_attention_noalloc.restype = ctypes.c_int
     lib.paged_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.paged_attention_workspace_size.restype = sz
     lib.pkv_read_device_error.argtypes = [vp, vp]
@@ -148,7 +151,7 @@ class _LazyLibrary:
 
 _lib = _LazyLibrary()
 
-EXPORTED_SYMBOLS = ("paged_kv_write", "paged_attention", "paged_attention_profiled",
+EXPORTED_SYMBOLS = ("paged_kv_write", "paged_attention", "paged_attention_profiled", "paged_attention_noalloc",
                     "paged_attention_workspace_size",
                     "pkv_read_device_error", "pkv_validate_metadata_host", "pkv_status_string",
                     "pkv_last_error_detail", "paged_kv_copy_blocks", "paged_kv_write_rope",
@@ -279,6 +282,49 @@ def paged_attention(q: torch.Tensor, kv_cache_layer: torch.Tensor, block_table: 
         st = _lib.paged_attention_profiled(*args, handles)
     if st != 0:
         raise PagedKVError(st, "paged_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def paged_attention_noalloc(q: torch.Tensor, kv_cache_layer: torch.Tensor, block_table: torch.Tensor,
+                            seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                            num_computed_tokens: torch.Tensor, scale: float, *, max_query_len: int,
+                            max_seq_len: int, out: torch.Tensor, device_error: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """``paged_attention`` with its workspace in the library's static device
+    scratch (``NOALLOC_SCRATCH_BYTES`` per GPU): nothing is allocated, so
+    ``out`` must be given.  ``device_error`` (int32, one element, on the
+    device) gets the step's device error bits OR-ed in.  Calls on one GPU share
+    the scratch: calls that may overlap must be ordered by the caller."""
+    _, nb, _, hkv, d = _check_cache_shape(kv_cache_layer)
+    _check_dev("q", q, kv_cache_layer.dtype)
+    _check_dev("kv_cache_layer", kv_cache_layer)
+    _check_dev("out", out, q.dtype)
+    for n, x in (("block_table", block_table), ("seq_lens", seq_lens),
+                 ("query_start_loc", query_start_loc),
+                 ("num_computed_tokens", num_computed_tokens)):
+        _check_dev(n, x, torch.int32)
+    if device_error is not None:
+        _check_dev("device_error", device_error, torch.int32)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [T, num_q_heads, head_dim]")
+    T, hq, dq = q.shape
+    if dq != d:
+        raise ValueError("q head_dim differs from the cache's")
+    R = seq_lens.shape[0]
+    if query_start_loc.shape != (R + 1,) or num_computed_tokens.shape != (R,):
+        raise ValueError("query_start_loc must be [R+1], num_computed_tokens [R]")
+    if block_table.dim() != 2 or block_table.shape[0] != R:
+        raise ValueError("block_table must be [R, max_blocks_per_req]")
+    st = _lib.paged_attention_noalloc(_ptr(out), _ptr(q), _ptr(kv_cache_layer), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(query_start_loc), _ptr(num_computed_tokens),
+                                      float(scale), R, T, hq, hkv, d, nb, max(block_table.shape[1], 1),
+                                      max_query_len, max_seq_len, _dtype_code(q.dtype), _ptr(device_error),
+                                      _stream_ptr(stream))
+    if st != 0:
+        raise PagedKVError(st, "paged_attention_noalloc")
     return out
 
 

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -360,6 +361,82 @@ int paged_attention_profiled(void* out, const void* q, const void* kv_cache_laye
                         num_computed_tokens, scale, num_reqs, num_tokens, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, max_blocks_per_req, max_query_len, max_seq_len, dtype,
                         workspace, workspace_bytes, stream, phase_events);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device memory of paged_attention_noalloc: split-KV partials, work lists and
+// the header with the error word, PKV_NOALLOC_SCRATCH_BYTES per GPU, held
+// from the library's load until the process ends.  In host code the name
+// `scratch` is only the runtime's handle for the array: its device address
+// comes from hipGetSymbolAddress, once per device (each GPU has its own copy).
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t status = hipSuccess;
+};
+ScratchAddr g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (current on this thread).
+void* scratch_on(int dev, hipError_t* status) {
+  ScratchAddr& a = g_scratch_addr[dev];
+  std::call_once(a.once, [&a] {
+    void* p = nullptr;
+    a.status = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    a.ptr = a.status == hipSuccess ? p : nullptr;
+  });
+  *status = a.status;
+  return a.ptr;
+}
+
+// OR the step's device error word into the caller's int32.
+__global__ void export_error_kernel(const int32_t* hdr, int32_t* device_error) {
+  if (threadIdx.x == 0 && hdr[pkv::kHdrError] != 0) *device_error |= hdr[pkv::kHdrError];
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_noalloc(void* out, const void* q, const void* kv_cache_layer,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+                            float scale, int32_t num_reqs, int64_t num_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                            int32_t max_blocks_per_req, int32_t max_query_len, int32_t max_seq_len,
+                            int32_t dtype, int32_t* device_error, void* stream) {
+  // the scratch this step needs, by the bound paged_attention checks its workspace against
+  if (elem_bytes(dtype) == 0) return fail(PKV_ERR_DTYPE, "dtype %lld", dtype);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_DIMS, "num_q_heads %lld / num_kv_heads %lld", num_q_heads, num_kv_heads);
+  const size_t need = workspace_size_tiles(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len,
+                                           max_seq_len,
+                                           tile_rows_for(dtype, head_dim, num_q_heads / num_kv_heads));
+  if (need == 0) return fail(PKV_ERR_DIMS, "num_reqs %lld, num_tokens %lld, limits", num_reqs, num_tokens);
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_ERR_WORKSPACE, "step needs %lld bytes of scratch; the static scratch holds %lld",
+                (long long)need, (long long)PKV_NOALLOC_SCRATCH_BYTES);
+  if (device_error && !aligned(device_error, 4)) return fail(PKV_ERR_ALIGN, "device_error needs 4-byte alignment");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_LAUNCH, "no usable current device (%lld)", dev);
+  hipError_t st = hipSuccess;
+  void* ws = scratch_on(dev, &st);
+  if (ws == nullptr) return fail(PKV_ERR_LAUNCH, "hipGetSymbolAddress of the scratch failed: %lld", (long long)st);
+  const int rc = attention_impl(out, q, kv_cache_layer, block_table, seq_lens, query_start_loc,
+                                num_computed_tokens, scale, num_reqs, num_tokens, num_q_heads, num_kv_heads,
+                                head_dim, num_blocks, max_blocks_per_req, max_query_len, max_seq_len, dtype, ws,
+                                PKV_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+  if (rc != PKV_OK || device_error == nullptr) return rc;
+  hipLaunchKernelGGL(export_error_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const int32_t*)ws,
+                     device_error);
+  if (hipGetLastError() != hipSuccess) return fail(PKV_ERR_LAUNCH, "error export launch failed");
+  return ok();
 }
 
 int paged_attention_int8(void* out, const void* q, const void* kv_cache_layer, const float* kv_scales,

@@ -114,3 +114,16 @@ def test_host_metadata_validator():
     assert pkv.pkv_validate_metadata_host(**args(slot_mapping=sm)) == 6
     assert pkv.pkv_validate_metadata_host(**args(max_seq_len=10)) == 6
     assert pkv.pkv_validate_metadata_host(**args(max_query_len=1)) == 6
+
+
+def test_noalloc_rejects_steps_beyond_its_scratch():
+    import paged_kv_cache_61_amd as pkv
+    lib = pkv._lib
+    args = lambda R, T, Hq, Hkv, D, mql, msl, dtype=1: (16, 16, 16, 16, 16, 16, 16, 1.0, R, T, Hq, Hkv, D, 64, 4,
+                                                        mql, msl, dtype, None, None)
+    need = pkv.paged_attention_workspace_size(64, 64, 64, 128, 1, 1 << 20)
+    assert need > pkv.NOALLOC_SCRATCH_BYTES
+    assert lib.paged_attention_noalloc(*args(64, 64, 64, 8, 128, 1, 1 << 20)) == 4   # returns before any HIP call
+    assert "static scratch" in pkv.last_error_detail()
+    assert lib.paged_attention_noalloc(*args(64, 64, 64, 8, 128, 1, 1 << 20, dtype=9)) == 3
+    assert lib.paged_attention_noalloc(*args(64, 64, 6, 4, 128, 1, 4096)) == 2
