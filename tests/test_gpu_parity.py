@@ -282,7 +282,65 @@ def test_prefill_static_item_assignment(Hq, Hkv, reqs):
     # (header word 6 set); every item must be run exactly once
     wl = workloads.build(workloads.small_spec(f"prefill-static-{Hq}-{Hkv}", 47 + Hq, "bf16", Hq, Hkv, 128, reqs))
     s, _ = _full_step(wl, f"static prefill assignment {Hq}/{Hkv}")
-    assert int(s.workspace[24:28].view(torch.int32).item()) == 1
+    ws = s.workspace.cpu().numpy()
+    hdr = ws[:1024].view(np.int32)
+    assert hdr[6] == 1
+    # the lists themselves: pf_order is a permutation of the items, the slot
+    # starts are monotone and end at the item count, and the per-slot loads
+    # equal those of first fit decreasing on the cost 10 * tiles + 50
+    G = Hq // Hkv
+    tile_rows = 256 // G
+    off = _workspace_offsets(wl.num_reqs, wl.num_tokens, wl.max_seq_len, tile_rows)
+    n = int(hdr[2])
+    items = ws[off["prefill_items"]:off["prefill_items"] + 16 * n].view(np.int32).reshape(n, 4)
+    order = ws[off["pf_order"]:off["pf_order"] + 4 * n].view(np.int32)
+    W = min(torch.cuda.get_device_properties(0).multi_processor_count // Hkv, 64)
+    start = ws[off["pf_slot_start"]:off["pf_slot_start"] + 4 * (W + 1)].view(np.int32)
+    assert sorted(order.tolist()) == list(range(n))
+    assert start[0] == 0 and start[W] == n and np.all(np.diff(start) >= 0)
+    c = wl.num_computed_tokens
+    tiles = np.array([(int(c[r]) + row0 + rows + 63) // 64 for r, row0, rows, _ in items])
+    assert np.all(np.diff(tiles) <= 0), "items are listed longest first"
+    cost = 10 * tiles + 50
+    got = sorted(int(cost[order[start[k]:start[k + 1]]].sum()) for k in range(W))
+    assert got == sorted(_first_fit_decreasing(cost.tolist(), W))
+
+
+def _workspace_offsets(R, T, max_seq_len, tile_rows):
+    """Byte offsets of the work lists in the attention workspace (the layout
+    the library documents: a 1 KiB header, then 256-byte aligned arrays)."""
+    al = lambda x: (x + 255) // 256 * 256
+    dec_rows = min(R, T)
+    parts = (max_seq_len + 511) // 512
+    cap_row = dec_rows * max(parts, 1) + T + 1
+    cap_pf = T // tile_rows + R + 1
+    cap_red = dec_rows + 1
+    o = {}
+    off = 1024
+    o["row_items"] = off; off = al(off + 16 * cap_row)
+    o["row_items_tail"] = off; off = al(off + 16 * cap_row)
+    o["prefill_items"] = off; off = al(off + 16 * cap_pf)
+    o["reduce_items"] = off; off = al(off + 16 * cap_red)
+    o["pf_order"] = off; off = al(off + 4 * 256)
+    o["pf_slot_start"] = off
+    return o
+
+
+def _first_fit_decreasing(costs, W):
+    """Slot loads of first fit decreasing: capacity ceil(total / W) + 5; items
+    over half the capacity take slots 0, 1, ... directly (at most W of
+    them); every other item, longest first, goes to the lowest slot it still
+    fits in, else to the emptiest (lowest on ties)."""
+    cap = (sum(costs) + W - 1) // W + 5
+    load = [0] * W
+    p = min(sum(1 for x in costs if 2 * x > cap), W)
+    for i in range(p):
+        load[i] += costs[i]
+    for x in costs[p:]:
+        fit = [k for k in range(W) if load[k] + x <= cap]
+        k = fit[0] if fit else min(range(W), key=lambda j: (load[j], j))
+        load[k] += x
+    return load
 
 
 def test_prefill_long_context_reads_table_per_tile():
