@@ -55,6 +55,8 @@ def parse():
                     help="FP8 (E4M3) KV cache (paged_kv_write_fp8 + paged_attention_fp8)")
     ap.add_argument("--rope", action="store_true",
                     help="write the step's tokens with paged_kv_write_rope (RoPE on K, and on q in place)")
+    ap.add_argument("--head-dim", type=int, choices=(64, 128), default=None,
+                    help="run the workload at this head_dim instead of its own (same lengths and heads)")
     ap.add_argument("--no-peak-probes", action="store_true",
                     help="skip the measured-peak probes (a device copy and a bf16 GEMM)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
@@ -377,7 +379,12 @@ def main():
     import workloads
 
     t_gen = time.perf_counter()
-    wl = workloads.build(workloads.BENCH_WORKLOADS[args.workload])
+    spec = workloads.BENCH_WORKLOADS[args.workload]
+    if args.head_dim is not None and args.head_dim != spec.head_dim:
+        import dataclasses
+        spec = dataclasses.replace(spec, head_dim=args.head_dim,
+                                   name=spec.name.replace("D=128", f"D={args.head_dim}") + f", head_dim {args.head_dim}")
+    wl = workloads.build(spec)
     gen_s = time.perf_counter() - t_gen
     acct = accounting(wl)
 
@@ -509,7 +516,7 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(rows_gbs / HBM_PEAK_GBS, 4),
-        "traffic": None if kv8 else measured_traffic(args.workload, "rows"),
+        "traffic": None if kv8 or args.head_dim not in (None, 128) else measured_traffic(args.workload, "rows"),
         "algorithmic_bytes_per_launch": dec_bytes,
         "avg_launch_ms": round(phase_ms["rows"], 5),
         "launch_ms_p10": pct(phase_all["rows"], 10), "launch_ms_p90": pct(phase_all["rows"], 90),
@@ -527,7 +534,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None if kv8 else measured_traffic(args.workload, "prefill"),
+            "traffic": None if kv8 or args.head_dim not in (None, 128) else measured_traffic(args.workload, "prefill"),
             "algorithmic_flops_per_launch": acct["prefill_flops"],
             "avg_launch_ms": round(phase_ms["prefill"], 5),
             "launch_ms_p10": pct(phase_all["prefill"], 10), "launch_ms_p90": pct(phase_all["prefill"], 90),

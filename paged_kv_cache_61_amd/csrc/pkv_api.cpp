@@ -60,12 +60,16 @@ int num_cus() {
   return n;
 }
 
-// bf16 prefill chunks with head_dim 128 run on the MFMA tile kernel; other
-// prefill rows go through the row kernel, one query row at a time.
-bool prefill_on_mfma(int32_t dtype, int32_t head_dim) { return dtype == PKV_BF16 && head_dim == 128; }
+// Prefill chunks with bf16 q run on the MFMA tile kernel: over a bf16 cache
+// at head_dim 64 or 128, over an 8-bit cache at head_dim 128.  Other prefill
+// rows (fp32, 8-bit caches at head_dim 64) go through the row kernel, one
+// query row at a time.
+bool prefill_on_mfma(int32_t dtype, int32_t head_dim, bool kv8) {
+  return dtype == PKV_BF16 && (head_dim == 128 || (head_dim == 64 && !kv8));
+}
 
-int64_t tile_rows_for(int32_t dtype, int32_t head_dim, int32_t group) {
-  return prefill_on_mfma(dtype, head_dim) ? pkv::prefill_tile_rows(group) : 1;
+int64_t tile_rows_for(int32_t dtype, int32_t head_dim, int32_t group, bool kv8) {
+  return prefill_on_mfma(dtype, head_dim, kv8) ? pkv::prefill_tile_rows(group) : 1;
 }
 
 }  // namespace
@@ -213,7 +217,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   if (i8 && !aligned(kv_scales, 4)) return fail(PKV_ERR_ALIGN, "kv_scales needs 4-byte alignment");
 
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t tile_rows = tile_rows_for(dtype, head_dim, group);
+  const int64_t tile_rows = tile_rows_for(dtype, head_dim, group, i8);
   const pkv::WsLayout ws =
       pkv::ws_layout(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len, max_seq_len, tile_rows);
   if (workspace_bytes < ws.total)
@@ -238,7 +242,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   pp.max_seq_len = max_seq_len;
   pp.max_blocks_per_req = max_blocks_per_req;
   pp.split_decode = 1;
-  pp.mfma_prefill = prefill_on_mfma(dtype, head_dim) ? 1 : 0;
+  pp.mfma_prefill = prefill_on_mfma(dtype, head_dim, i8) ? 1 : 0;
   pp.prefill_tile_rows = (int32_t)tile_rows;
   // One 8-wave prefill workgroup per CU; the grid is a multiple of the kv
   // head count so every workgroup owns one head (slot = blockIdx / heads).
@@ -416,7 +420,7 @@ int paged_attention_noalloc(void* out, const void* q, const void* kv_cache_layer
     return fail(PKV_ERR_DIMS, "num_q_heads %lld / num_kv_heads %lld", num_q_heads, num_kv_heads);
   const size_t need = workspace_size_tiles(num_reqs, num_tokens, num_q_heads, head_dim, max_query_len,
                                            max_seq_len,
-                                           tile_rows_for(dtype, head_dim, num_q_heads / num_kv_heads));
+                                           tile_rows_for(dtype, head_dim, num_q_heads / num_kv_heads, false));
   if (need == 0) return fail(PKV_ERR_DIMS, "num_reqs %lld, num_tokens %lld, limits", num_reqs, num_tokens);
   if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
     return fail(PKV_ERR_WORKSPACE, "step needs %lld bytes of scratch; the static scratch holds %lld",

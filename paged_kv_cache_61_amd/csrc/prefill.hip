@@ -65,12 +65,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPfRows = 256;   // MFMA rows per workgroup (8 waves x 32)
 constexpr int kPfKeys = 64;    // keys per tile (4 cache blocks)
 constexpr int kPfThreads = 512;
-constexpr int kD = 128;        // head_dim handled by this kernel
-constexpr int kRowB = kD * 2;               // bytes of one key row (one kv head)
-constexpr int kHalfTile = kPfKeys * kRowB;  // K or V part of a tile: 16 KiB
-constexpr int kStage = 2 * kHalfTile;       // one ring slot: K then V
-constexpr int kStages = 4;                  // ring slots: tiles t-1 (PV), t (QK), t+1 and t+2 (in flight)
-constexpr int kKSteps = kD / 16;            // Q.K k-steps
+constexpr int kStages = 4;     // ring slots: tiles t-1 (PV), t (QK), t+1 and t+2 (in flight)
+
+// Sizes that follow from head_dim (64 or 128).
+template <int D>
+struct PfCfg {
+  static constexpr int kRowB = D * 2;               // bytes of one key row (one kv head)
+  static constexpr int kHalfTile = kPfKeys * kRowB; // K or V part of a tile: 8 or 16 KiB
+  static constexpr int kStage = 2 * kHalfTile;      // one ring slot: K then V
+  static constexpr int kKSteps = D / 16;            // Q.K k-steps
+  static constexpr int kDTiles = D / 32;            // O^T row tiles
+  static constexpr int kCopyLoads = kBlock * kRowB / 1024;  // 16-byte-per-lane loads per cache block
+};
+constexpr int kD = 128;        // head_dim of the 8-bit cache instantiations
 // 8-bit cache (INT8 or FP8 E4M3 codes): the copies bring codes (128-byte
 // rows) and per-row scales into a 4-slot ring, three tiles ahead; every
 // period the waves dequantise K(t+1) and V(t) (value * scale in float32,
@@ -82,9 +89,8 @@ constexpr int kScl = kPfKeys * 4;                 // scales of K or V of a tile
 constexpr int kStage8 = 2 * kHalf8 + 2 * kScl;    // one int8 ring slot
 constexpr int kStages8 = 4;
 constexpr int kConv = kStages8 * kStage8;         // offset of the bf16 tiles K0, K1, V0, V1
-constexpr int kLdsI8 = kConv + 4 * kHalfTile;
+constexpr int kLdsI8 = kConv + 4 * PfCfg<kD>::kHalfTile;
 static_assert(kLdsI8 + 64 <= 160 * 1024, "8-bit prefill LDS");
-constexpr int kDTiles = kD / 32;            // O^T row tiles
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define PKV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -131,10 +137,24 @@ PKV_DEV float pair_sum(float x) {
 constexpr float kRefSlack = 8.f;
 
 // Chunk-position permutation of key row r (mod 16) inside a K or V tile:
-// 16-byte chunk c of the row sits at position c ^ swz(r), swz swapping the
-// two 2-bit halves of r, so both the K operand reads and the transposed V
-// reads are free of bank conflicts.
-PKV_DEV int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 16-byte chunk c of the row sits at position c ^ swz<D>(r), so both the K
+// operand reads and the transposed V reads are free of bank conflicts.
+//  * D = 128 (256-byte rows, 16 chunks; every row starts at bank 0): swz
+//    swaps the two 2-bit halves of r.  It is a permutation of 0..15, so 16
+//    rows read at one chunk hit 16 distinct positions; and its upper two
+//    bits differ within each aligned group of 4 rows, so a transposed read
+//    (4 rows x 4 adjacent chunks) covers 16 distinct positions too.
+//  * D = 64 (128-byte rows, 8 chunks; odd rows start at the upper half of
+//    the banks): swz = 4 * bit1(r) + (r >> 2) mod 4.  Over the 8 even rows
+//    of 16 (and over the 8 odd ones) it takes every value 0..7, so 16 rows
+//    at one chunk hit 16 distinct positions; rows 4a and 4a + 2 (and 4a + 1,
+//    4a + 3) differ in bit 2, so the two rows of a bank half in a transposed
+//    read put an aligned group of 4 chunks on complementary positions.
+template <int D>
+PKV_DEV int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return ((r & 2) << 1) | ((r >> 2) & 3);
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (expcnt and lgkmcnt left alone).
@@ -213,10 +233,14 @@ PKV_DEV u32x4 buffer_desc(const void* base, uint32_t bytes) {
 
 // The metadata arrays are passed on their own as restrict pointers so their
 // wave-uniform reads become scalar loads, which never wait on the tile stream.
-template <bool I8, bool FP8>
+template <int D, bool I8, bool FP8>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     PrefillParams a, const int4* __restrict__ items, const int32_t* __restrict__ qsl,
     const int32_t* __restrict__ nct, const int32_t* __restrict__ block_table) {
+  static_assert(D == 128 || (D == 64 && !I8), "bf16 cache: head_dim 64 or 128; 8-bit cache: 128");
+  using Cf = PfCfg<D>;
+  constexpr int kRowB = Cf::kRowB, kHalfTile = Cf::kHalfTile, kStage = Cf::kStage;
+  constexpr int kKSteps = Cf::kKSteps, kDTiles = Cf::kDTiles;
   __shared__ __attribute__((aligned(16))) char lds[I8 ? kLdsI8 : kStages * kStage];
   __shared__ int tile_bad[2];
 
@@ -278,11 +302,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     voff[2] = (uint32_t)(lane & 15) * 4u;
     voff[3] = 0;
   } else {
+    // 16 lanes per row of 256 bytes (D = 128) or 8 per row of 128 bytes (D = 64)
+    constexpr int kLanesPerRow = kRowB / 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rb = 4 * j + (lane >> 4);
-      voff[j] = rb * (uint32_t)row_bytes + g * kRowB + (((lane & 15) ^ swz(rb)) << 4);
+    for (int j = 0; j < Cf::kCopyLoads; ++j) {
+      const int rb = (64 / kLanesPerRow) * j + lane / kLanesPerRow;
+      voff[j] = rb * (uint32_t)row_bytes + g * kRowB + (((lane % kLanesPerRow) ^ swz<D>(rb)) << 4);
     }
+#pragma unroll
+    for (int j = Cf::kCopyLoads; j < 4; ++j) voff[j] = 0;
   }
   const uint32_t ldst = (uint32_t)(uintptr_t)PKV_LDS(lds) + (uint32_t)ldst_half;
   const uint32_t ldsc = (uint32_t)(uintptr_t)PKV_LDS(lds) + (uint32_t)(2 * kHalf8 + (w < 4 ? 0 : kScl) + cblk * kBlock * 4);
@@ -351,8 +379,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       if (lane < kBlock) dma_dword(rss, voff[2], ldsc + slot);
     } else {
       const uint32_t m0 = ldst + (uint32_t)(tile & (kStages - 1)) * kStage;
-      static_assert(4 * kRowB == 0x400, "dma_block steps M0 by 1 KiB (4 token rows)");
-      dma_block(rs, voff, m0);
+      if constexpr (D == 128) {
+        static_assert(4 * Cf::kRowB == 0x400, "dma_block steps M0 by 1 KiB (4 token rows)");
+        dma_block(rs, voff, m0);
+      } else {
+        static_assert(8 * Cf::kRowB == 0x400, "dma_pair steps M0 by 1 KiB (8 token rows)");
+        dma_pair(rs, voff[0], voff[1], m0);
+      }
     }
   };
 
@@ -385,7 +418,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     row_ok = rho < BQ * G && pos < nrows;
     if (!row_ok) pos = nrows - 1;  // padding rows: any visible row, loaded and zeroed
     pos_abs = c + row0 + pos;
-    qrow = ((size_t)(qs + row0 + pos) * a.num_q_heads + g * G + head) * kD;
+    qrow = ((size_t)(qs + row0 + pos) * a.num_q_heads + g * G + head) * D;
     const uint32_t qmask = row_ok ? 0xffffffffu : 0u;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
@@ -406,8 +439,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // halves (reads) and opposite chunk parity (writes), so neither conflicts.
   const int cv_r = 8 * w + 4 * ((lane >> 3) & 1) + (lane >> 4);
   const int cv_rd = (cv_r ^ ((lane >> 3) & 1)) * kRowB8 + (lane & 7) * 16;
-  const int cv_w0 = cv_r * kRowB + (((2 * (lane & 7)) ^ swz(cv_r & 15)) << 4);
-  const int cv_w1 = cv_r * kRowB + (((2 * (lane & 7) + 1) ^ swz(cv_r & 15)) << 4);
+  const int cv_w0 = cv_r * kRowB + (((2 * (lane & 7)) ^ swz<D>(cv_r & 15)) << 4);
+  const int cv_w1 = cv_r * kRowB + (((2 * (lane & 7) + 1) ^ swz<D>(cv_r & 15)) << 4);
   auto dequant = [&](int tile, int kv) PKV_INLINE {  // kv 0: K, 1: V
     const char* slot = lds + (tile & (kStages8 - 1)) * kStage8;
     const u32x4 cw = *(const u32x4*)(slot + kv * kHalf8 + cv_rd);
@@ -485,17 +518,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     // tile dt reads rows 16ks + key0 (+8), chunk 4dt + (tdb >> 3), where the
     // swizzle depends only on the row mod 16, so ks and kt enter as constants.
     constexpr int kAhead = 5;
-    const int kswz = swz(lrow & 15);
+    const int kswz = swz<D>(lrow & 15);
     const int key0 = 4 * half + (ts >> 2);
-    const int vsw0 = swz(key0 & 15), vsw1 = swz((key0 + 8) & 15);
+    const int vsw0 = swz<D>(key0 & 15), vsw1 = swz<D>((key0 + 8) & 15);
     const int kbase_off = lrow * kRowB;
     const int vbase0 = key0 * kRowB + (tdb & 7) * 2, vbase1 = (key0 + 8) * kRowB + (tdb & 7) * 2;
     auto read_k = [&](const char* kl, int q) PKV_INLINE -> u32x4 {  // unit 16 + q
       const int ks = q >> 1, kt = q & 1;
       return *(const u32x4*)(kl + kbase_off + kt * 32 * kRowB + (((2 * ks + half) ^ kswz) << 4));
     };
-    auto read_v = [&](const char* vl, int u) PKV_INLINE -> u32x4 {  // unit u < 16
-      const int ks = u >> 2, c = 4 * (u & 3) + (tdb >> 3);
+    auto read_v = [&](const char* vl, int u) PKV_INLINE -> u32x4 {  // unit u < 4 * kDTiles
+      const int ks = u / kDTiles, c = 4 * (u % kDTiles) + (tdb >> 3);
       const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(vl + ks * 16 * kRowB + vbase0 + ((c ^ vsw0) << 4)));
       const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -510,13 +543,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
         // keys 16*ks + 8*jj + 4*half + 0..3, jj = 0, 1) comes from two
         // transposed reads whose source lanes point at those keys' rows.
         const char* vl = I8 ? lds + kConv + (2 + ((t - 1) & 1)) * kHalfTile : lds + ((t - 1) % kStages) * kStage + kHalfTile;
+        constexpr int kPvUnits = 4 * kDTiles;   // 4 k-steps of 16 keys x head_dim tiles
         u32x4 ring[kAhead + 1];
 #pragma unroll
         for (int j = 0; j < kAhead; ++j) ring[j] = read_v(vl, j);
-        static_for<0, 16>([&](auto uc) PKV_INLINE {
+        static_for<0, kPvUnits>([&](auto uc) PKV_INLINE {
           constexpr int u = decltype(uc)::value;
-          if constexpr (u + kAhead < 16) ring[(u + kAhead) % (kAhead + 1)] = read_v(vl, u + kAhead);
-          oacc[u & 3] = mfma32(ring[u % (kAhead + 1)], pf[u >> 2], oacc[u & 3]);
+          if constexpr (u + kAhead < kPvUnits) ring[(u + kAhead) % (kAhead + 1)] = read_v(vl, u + kAhead);
+          oacc[u % kDTiles] = mfma32(ring[u % (kAhead + 1)], pf[u / kDTiles], oacc[u % kDTiles]);
           __builtin_amdgcn_sched_barrier(0);
         });
       }
@@ -527,12 +561,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+      constexpr int kQkUnits = 2 * kKSteps;     // 2 key halves x head_dim k-steps
       u32x4 ring[kAhead + 1];
 #pragma unroll
       for (int j = 0; j < kAhead; ++j) ring[j] = read_k(kl, j);
-      static_for<0, 16>([&](auto uc) PKV_INLINE {
+      static_for<0, kQkUnits>([&](auto uc) PKV_INLINE {
         constexpr int q = decltype(uc)::value;
-        if constexpr (q + kAhead < 16) ring[(q + kAhead) % (kAhead + 1)] = read_k(kl, q + kAhead);
+        if constexpr (q + kAhead < kQkUnits) ring[(q + kAhead) % (kAhead + 1)] = read_k(kl, q + kAhead);
         sacc[q & 1] = mfma32(ring[q % (kAhead + 1)], qf[q >> 1], sacc[q & 1]);
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -606,8 +641,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
         __builtin_amdgcn_sched_barrier(0);
         return;
       }
+      // (tile t+1's copies, kCopyLoads per wave, may stay in flight)
       if (t + 1 < ntiles)
-        wait_vmem<4>();
+        wait_vmem<Cf::kCopyLoads>();
       else
         wait_vmem<0>();
       // nothing moves across the barrier or a phase boundary
@@ -698,8 +734,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
 int prefill_tile_rows(int32_t group) { return kPfRows / (group > 0 ? group : 1); }
 
 int launch_prefill(const PrefillParams& p, int32_t head_dim, int64_t grid, hipStream_t stream) {
-  if (head_dim != kD || grid <= 0) return 1;
-  auto k = !p.kv_scales ? prefill_kernel<false, false> : p.kv_fp8 ? prefill_kernel<true, true> : prefill_kernel<true, false>;
+  if (grid <= 0 || (head_dim != 128 && !(head_dim == 64 && !p.kv_scales))) return 1;
+  auto k = head_dim == 64 ? prefill_kernel<64, false, false>
+           : !p.kv_scales ? prefill_kernel<128, false, false>
+           : p.kv_fp8     ? prefill_kernel<128, true, true>
+                          : prefill_kernel<128, true, false>;
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.qsl, p.nct, p.block_table);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -263,11 +263,52 @@ def test_empty_step():
 # ---------------------------------------------------------------------------
 # prefill chunks on the MFMA path
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (12, 4), (32, 8), (64, 8), (32, 2)])
-def test_prefill_group_sizes(Hq, Hkv):
+def test_prefill_group_sizes(Hq, Hkv, D):
     reqs = [(0, 130), (37, 64), (700, 200), (5, 1), (0, 2), (1100, 77), (16, 16)]
-    wl = workloads.build(workloads.small_spec(f"prefill-{Hq}-{Hkv}", 31 + Hq, "bf16", Hq, Hkv, 128, reqs))
-    _full_step(wl, f"prefill G={Hq // Hkv}")
+    wl = workloads.build(workloads.small_spec(f"prefill-{Hq}-{Hkv}-{D}", 31 + Hq, "bf16", Hq, Hkv, D, reqs))
+    _full_step(wl, f"prefill G={Hq // Hkv} D={D}")
+
+
+def test_prefill_repeatable_across_launches():
+    # the same prefill step at head_dim 64 and 128, run several times with a
+    # launch of the other head size in between (which leaves its own tiles in
+    # the LDS of every CU): identical bits each time, so no tile is read
+    # before its copy has landed
+    steps = {}
+    for D in (64, 128):
+        reqs = [(1500, 700), (0, 900), (40, 1)]
+        wl = workloads.build(workloads.small_spec(f"prefill-rep-{D}", 71, "bf16", 16, 8, D, reqs))
+        s = upload(wl)
+        run_write(s)
+        steps[D] = s
+    first = {}
+    for it in range(6):
+        for D in (64, 128):
+            out = torch.full_like(steps[D].q, float(it))
+            run_attention(steps[D], out=out)
+            torch.cuda.synchronize()
+            b = _bits(out)
+            first.setdefault(D, b)
+            assert b == first[D], f"head_dim {D}, launch {it}: output differs from the first launch"
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (64, 4)])
+def test_prefill_head_dim_64_long_chunks(Hq, Hkv):
+    # head_dim 64 chunks of 1024+ tokens on cached prefixes, on the MFMA
+    # prefill (group sizes 1, 2, 4, 8, 16), every row against the oracle
+    reqs = [(0, 1024), (1500, 1100), (3000, 1030), (7, 1), (2100, 1)]
+    wl = workloads.build(workloads.small_spec(f"prefill-d64-{Hq}-{Hkv}", 61 + Hq, "bf16", Hq, Hkv, 64, reqs))
+    print(f"[case] head_dim 64 long chunks G={Hq // Hkv}", flush=True)
+    s = upload(wl)
+    run_write(s)
+    run_attention(s)
+    torch.cuda.synchronize()
+    assert device_error(s) == 0
+    ref_pool = oracle_pool(wl)
+    ref = oracle_rows_parallel(wl.q, ref_pool, wl, range(wl.num_tokens), wl.dtype)
+    assert_close(out_f64(s.out), ref, wl.dtype, f"head_dim 64 long chunks G={Hq // Hkv}")
 
 
 @pytest.mark.parametrize("Hq,Hkv,reqs", [
@@ -343,13 +384,14 @@ def _first_fit_decreasing(costs, W):
     return load
 
 
-def test_prefill_long_context_reads_table_per_tile():
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_long_context_reads_table_per_tile(D):
     # chunks whose keys run past 128 tiles of 64 (8192 keys): the prefill
     # kernel reads those tiles' block ids from the table per tile instead of
     # from the per-item registers
     import paged_kv_cache_61_amd as pkv
     reqs = [(9000, 70), (8150, 100), (8190, 2), (20, 1)]
-    wl = workloads.build(workloads.small_spec("long-prefill", 41, "bf16", 8, 2, 128, reqs))
+    wl = workloads.build(workloads.small_spec(f"long-prefill-{D}", 41, "bf16", 8, 2, D, reqs))
     s, good = _full_step(wl, "prefill past 8192 keys")
     # a bad id in a tile past 128 of request 0 is reported and poisons only
     # that request's rows
@@ -365,11 +407,12 @@ def test_prefill_long_context_reads_table_per_tile():
     assert np.array_equal(out[70:], ref[70:])
 
 
-def test_prefill_chunk_split_and_decode_consistency():
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_chunk_split_and_decode_consistency(D):
     # one 300-token chunk on a 100-token prefix, the same tokens as two chunks,
     # and the last token as a decode: all agree with the oracle and each other
     rng = np.random.default_rng(5)
-    wl = workloads.build(workloads.small_spec("split", 32, "bf16", 32, 8, 128,
+    wl = workloads.build(workloads.small_spec(f"split-{D}", 32, "bf16", 32, 8, D,
                                                [(100, 300), (100, 150), (250, 150), (399, 1)]))
     # make the four requests read the same cache: copy request 0's blocks
     wl.block_table[1:] = wl.block_table[0]
