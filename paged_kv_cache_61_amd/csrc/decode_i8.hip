@@ -385,10 +385,12 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
     struct Stage {
       u32x4 k[KLD];
       uint32_t v[4][VW];
-      float sk, sv;
+      f32x4_t sk, sv;
     };
     // K: token r16, bytes 64j + 16*q4 .. +15 (j < KLD); V: tokens 4*q4 + i,
-    // bytes NDT*r16 .. +NDT-1; scales of token r16.
+    // bytes NDT*r16 .. +NDT-1; the K and V scales of tokens 4*q4 .. 4*q4+3,
+    // the tokens whose scores the lane holds (one 16-byte load each: a kv
+    // head's 16 scales of a block are contiguous).
     const uint32_t koff = r16 * row_stride + g * D + 16 * q4;
     const uint32_t voff = 4 * q4 * row_stride + g * D + NDT * r16;
     auto load = [&](Stage& st, int phys) PKV_INLINE {
@@ -406,9 +408,11 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
           st.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, i * row_stride, 0);
         }
       }
-      const size_t srow = ((size_t)phys * a.num_kv_heads + g) * kBlock + r16;
-      st.sk = kv_scales[srow];
-      st.sv = kv_scales[scale_half + srow];
+      const float* srow = kv_scales + ((size_t)phys * a.num_kv_heads + g) * kBlock;
+      const __amdgpu_buffer_rsrc_t rsk = make_rsrc(srow, kBlock * 4);
+      const __amdgpu_buffer_rsrc_t rsv = make_rsrc(srow + scale_half, kBlock * 4);
+      st.sk = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsk, 16 * q4, 0, 0));
+      st.sv = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsv, 16 * q4, 0, 0));
     };
 
     auto compute = [&](const Stage& st, int jblk) PKV_INLINE {
@@ -425,15 +429,13 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
                                                        __builtin_bit_cast(bf16x8_t, qb[s]), sacc, 0, 0, 0);
       }
-      // scales of tokens 4*q4 + i from the lanes that loaded them (lane = token)
+      // the lane's tokens 4*q4 + i with their own scales
       const int tok0 = jblk * kBlock + 4 * q4;
       float sc[4], vsc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int src = 4 * (4 * q4 + i);
-        const float ks = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(st.sk)));
-        vsc[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(st.sv)));
-        sc[i] = tok0 + i < vis ? sacc[i] * (ks * sl2) : -INFINITY;
+        vsc[i] = st.sv[i];
+        sc[i] = tok0 + i < vis ? sacc[i] * (st.sk[i] * sl2) : -INFINITY;
       }
       float bmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       bmax = xmax32(xmax16(bmax));
