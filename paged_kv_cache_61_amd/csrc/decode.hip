@@ -844,14 +844,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void r
   }
 }
 
-// Persistent grid: as many 4-wave workgroups as fit on the device at once,
-// but no more than the work items need.
+// Persistent grid: as many 4-wave workgroups as fit on the device at once
+// (at most per_cu per CU), but no more than the work items need.
 // (One cached occupancy per kernel: the template argument is the kernel.  The
 // cache is the library's only process-wide state: written once per kernel
 // with the value the runtime reports, which is the same for every caller, so
 // concurrent first calls race benignly.)
 template <auto K>
-int64_t persistent_grid(int64_t bound_wgs, int cus) {
+int64_t persistent_grid(int64_t bound_wgs, int cus, int per_cu = 64) {
   static std::atomic<int> occ_cache{0};
   int occ = occ_cache.load(std::memory_order_relaxed);
   if (occ <= 0) {
@@ -859,13 +859,14 @@ int64_t persistent_grid(int64_t bound_wgs, int cus) {
       occ = 2;
     occ_cache.store(occ, std::memory_order_relaxed);
   }
-  return std::max<int64_t>(1, std::min<int64_t>(bound_wgs, (int64_t)cus * occ));
+  return std::max<int64_t>(1, std::min<int64_t>(bound_wgs, (int64_t)cus * std::min(occ, per_cu)));
 }
 
 template <bool BF16, int D, int GM>
 int launch_rows_g(const RowParams& p, int64_t bound_waves, int cus, hipStream_t s) {
   auto k = row_attn_kernel<BF16, D, GM>;
-  const int64_t grid = persistent_grid<row_attn_kernel<BF16, D, GM>>((bound_waves + 3) / 4, cus);
+  // bf16: one workgroup (one wave per SIMD) per CU streams as fast as two
+  const int64_t grid = persistent_grid<row_attn_kernel<BF16, D, GM>>((bound_waves + 3) / 4, cus, BF16 ? 1 : 64);
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
@@ -897,8 +898,8 @@ int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bou
   const bool bf16 = dtype == PKV_BF16;
   if (rows_on_mfma(dtype, p.group)) {  // the whole group in one wave (head_groups == 1)
     auto k = head_dim == 64 ? row_attn_mfma_kernel<64> : row_attn_mfma_kernel<128>;
-    const int64_t grid = head_dim == 64 ? persistent_grid<row_attn_mfma_kernel<64>>((bound_waves + 3) / 4, cus)
-                                        : persistent_grid<row_attn_mfma_kernel<128>>((bound_waves + 3) / 4, cus);
+    const int64_t grid = head_dim == 64 ? persistent_grid<row_attn_mfma_kernel<64>>((bound_waves + 3) / 4, cus, 1)
+                                        : persistent_grid<row_attn_mfma_kernel<128>>((bound_waves + 3) / 4, cus, 1);
     hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError() == hipSuccess ? 0 : 1;
   }
