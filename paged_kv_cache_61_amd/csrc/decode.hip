@@ -98,10 +98,10 @@ PKV_DEV void unpack_v(u32x2 x, float& v0, float& v1) {
 }
 
 PKV_DEV uint32_t load_v(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kCpolNT);
 }
 PKV_DEV u32x2 load_v(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, u32x2) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCpolNT);
 }
 
 PKV_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -622,9 +622,9 @@ __global__ __launch_bounds__(256, 2) void row_attn_mfma_kernel(RowParams a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (NDT == 8)
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, i * row_stride, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, i * row_stride, kCpolNT);
           else
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, kCpolNT);
         }
       };
 
@@ -865,8 +865,10 @@ int64_t persistent_grid(int64_t bound_wgs, int cus, int per_cu = 64) {
 template <bool BF16, int D, int GM>
 int launch_rows_g(const RowParams& p, int64_t bound_waves, int cus, hipStream_t s) {
   auto k = row_attn_kernel<BF16, D, GM>;
-  // bf16: one workgroup (one wave per SIMD) per CU streams as fast as two
-  const int64_t grid = persistent_grid<row_attn_kernel<BF16, D, GM>>((bound_waves + 3) / 4, cus, BF16 ? 1 : 64);
+  // bf16 at head_dim 128: one workgroup (one wave per SIMD) per CU streams
+  // as fast as two
+  const int64_t grid =
+      persistent_grid<row_attn_kernel<BF16, D, GM>>((bound_waves + 3) / 4, cus, BF16 && D == 128 ? 1 : 64);
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
@@ -898,7 +900,7 @@ int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bou
   const bool bf16 = dtype == PKV_BF16;
   if (rows_on_mfma(dtype, p.group)) {  // the whole group in one wave (head_groups == 1)
     auto k = head_dim == 64 ? row_attn_mfma_kernel<64> : row_attn_mfma_kernel<128>;
-    const int64_t grid = head_dim == 64 ? persistent_grid<row_attn_mfma_kernel<64>>((bound_waves + 3) / 4, cus, 1)
+    const int64_t grid = head_dim == 64 ? persistent_grid<row_attn_mfma_kernel<64>>((bound_waves + 3) / 4, cus)
                                         : persistent_grid<row_attn_mfma_kernel<128>>((bound_waves + 3) / 4, cus, 1);
     hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError() == hipSuccess ? 0 : 1;

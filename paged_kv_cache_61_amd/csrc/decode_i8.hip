@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_i8_kernel(RowParams a, const 
 #pragma unroll
       for (int j = 0; j < KLD; ++j) s.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 16 * j, 0, 0);
 #pragma unroll
-      for (int j = 0; j < VLD; ++j) s.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, j * TPV * row_stride, 0);
+      for (int j = 0; j < VLD; ++j) s.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, j * TPV * row_stride, kCpolNT);
       const size_t srow = ((size_t)phys * a.num_kv_heads + g) * kBlock + tk;
       s.sk = kv_scales[srow];
       s.sv = kv_scales[scale_half + srow];
@@ -401,11 +401,11 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (VW == 2) {
-          const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, 0);
+          const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, kCpolNT);
           st.v[i][0] = x.x;
           st.v[i][1] = x.y;
         } else {
-          st.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, i * row_stride, 0);
+          st.v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, i * row_stride, kCpolNT);
         }
       }
       const float* srow = kv_scales + ((size_t)phys * a.num_kv_heads + g) * kBlock;
