@@ -294,7 +294,8 @@ def row_kernel_name(wl, kv8):
         f = kv8.upper()
         return (f"row_attn_i8_mfma_kernel ({f} cache, bf16 q: decode rows + split-KV partitions)"
                 if wl.dtype == "bf16" else f"row_attn_i8_kernel ({f} cache, fp32 q: decode rows + split-KV partitions)")
-    if wl.dtype == "bf16" and wl.num_q_heads // wl.num_kv_heads > 4:
+    g = wl.num_q_heads // wl.num_kv_heads
+    if wl.dtype == "bf16" and (g > 4 or (g > 2 and wl.head_dim == 128)):
         return "row_attn_mfma_kernel (decode rows + split-KV partitions, all query heads of a kv head on MFMA)"
     return "row_attn_kernel (decode rows + split-KV partitions)"
 

@@ -888,17 +888,23 @@ int launch_rows_d(const RowParams& p, int64_t bound_waves, int cus, hipStream_t 
 
 // bf16 groups wider than kMaxGroupRegs run on row_attn_mfma_kernel, one wave
 // for the whole group (as several waves of 4 heads, each reading the blocks,
-// they measured 7% slower at G = 8); narrower groups and fp32 run on
-// row_attn_kernel, which is as fast or slightly faster there.
-bool rows_on_mfma(int32_t dtype, int32_t group) { return dtype == PKV_BF16 && group > kMaxGroupRegs; }
+// they measured 7% slower at G = 8), and so do groups of 3 or 4 at head_dim
+// 128 (measured 3-4% faster there than the 4-head VALU kernel, but 2%
+// slower at head_dim 64); one- and two-head groups and fp32 run on
+// row_attn_kernel, which is as fast or faster there.
+bool rows_on_mfma(int32_t dtype, int32_t group, int32_t head_dim) {
+  return dtype == PKV_BF16 && (group > kMaxGroupRegs || (group > 2 && head_dim == 128));
+}
 
-int max_group_regs(int32_t dtype, int32_t group) { return rows_on_mfma(dtype, group) ? 16 : kMaxGroupRegs; }
+int max_group_regs(int32_t dtype, int32_t group, int32_t head_dim) {
+  return rows_on_mfma(dtype, group, head_dim) ? 16 : kMaxGroupRegs;
+}
 
 int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bound_waves, int cus,
                 hipStream_t stream) {
   if (bound_waves <= 0) return 0;
   const bool bf16 = dtype == PKV_BF16;
-  if (rows_on_mfma(dtype, p.group)) {  // the whole group in one wave (head_groups == 1)
+  if (rows_on_mfma(dtype, p.group, head_dim)) {  // the whole group in one wave (head_groups == 1)
     auto k = head_dim == 64 ? row_attn_mfma_kernel<64> : row_attn_mfma_kernel<128>;
     const int64_t grid = head_dim == 64 ? persistent_grid<row_attn_mfma_kernel<64>>((bound_waves + 3) / 4, cus)
                                         : persistent_grid<row_attn_mfma_kernel<128>>((bound_waves + 3) / 4, cus, 1);

@@ -310,7 +310,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   rp.num_q_heads = num_q_heads;
   rp.num_kv_heads = num_kv_heads;
   rp.group = group;
-  const int gmax = i8 ? pkv::max_group_regs_i8(dtype) : pkv::max_group_regs(dtype, group);
+  const int gmax = i8 ? pkv::max_group_regs_i8(dtype) : pkv::max_group_regs(dtype, group, head_dim);
   rp.head_groups = (group + gmax - 1) / gmax;
   rp.num_blocks = num_blocks;
   rp.max_blocks_per_req = max_blocks_per_req;

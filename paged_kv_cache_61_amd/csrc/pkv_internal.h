@@ -115,7 +115,7 @@ int launch_plan(const PlanParams& p, hipStream_t stream);
 // bound_waves: upper bound on row work items (one wave each); cus: compute units.
 // Query heads of a group that one row wave handles (wider groups run as
 // head_groups waves over the same blocks).
-int max_group_regs(int32_t dtype, int32_t group);
+int max_group_regs(int32_t dtype, int32_t group, int32_t head_dim);
 int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bound_waves, int cus,
                 hipStream_t stream);
 int launch_reduce(const ReduceParams& p, int32_t dtype, int32_t head_dim, int64_t grid,
