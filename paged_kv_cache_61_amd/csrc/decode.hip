@@ -200,7 +200,7 @@ template <int GM>
 PKV_DEV RowItem fetch_item(const RowParams& a, int64_t it, int per_pair, int n_head) {
   RowItem d;
   const int64_t e = it / per_pair;
-  const int4 item = e < n_head ? a.items[e] : a.items_tail[e - n_head];
+  const int4 item = e < n_head ? load_const(a.items, e) : load_const(a.items_tail, e - n_head);
   const int rem = (int)(it % per_pair);
   d.g = rem / a.head_groups;
   const int hg = rem - d.g * a.head_groups;
@@ -212,7 +212,7 @@ PKV_DEV RowItem fetch_item(const RowParams& a, int64_t it, int per_pair, int n_h
   d.slot0 = item.w;
   d.vis = d.jb = d.je = 0;
   if (d.part != kNanRow) {
-    d.vis = a.nct[d.r] + (d.t - a.qsl[d.r]) + 1;  // keys 0 .. position
+    d.vis = load_const(a.nct, d.r) + (d.t - load_const(a.qsl, d.r)) + 1;  // keys 0 .. position
     const int nblk = (d.vis + kBlock - 1) / kBlock;
     d.je = nblk;
     if (d.part >= 0) {
@@ -577,56 +577,84 @@ __global__ __launch_bounds__(256, 2) void row_attn_mfma_kernel(RowParams a) {
   const int64_t it = item_of(0);
   if (it >= total) return;
   int64_t nx = item_of(1);
+  // Block ids outside the pool are replaced by block 0 (and reported).  Each
+  // id vector is checked right where it is fetched or where every earlier
+  // load has landed anyway, so no later use of it waits on the stream.
+  auto check_ids = [&](int& ids) __attribute__((always_inline)) -> bool {
+    const bool out = ids < 0 || ids >= a.num_blocks;
+    if (out) ids = 0;
+    return out;
+  };
   RowItem cur = fetch_item<16>(a, it, per_pair, n_head);
   int btv = fetch_ids(a, cur, 0, lane);
+  bool btv_bad = check_ids(btv);
+
+  struct Stage {
+    u32x4 k[NS];
+    VRow v[4];
+  };
+  static_assert(NST == 2, "one block computed while the next one loads");
+  // kv head g's part of a block: K token r16, elements 16*q4 + 64*s (k-step
+  // s); V tokens 4*q4 + i, elements 2*NDT*r16 .. (byte offsets)
+  auto koff_of = [&](int g) -> uint32_t { return r16 * row_stride + g * ROWB + 16 * q4; };
+  auto voff_of = [&](int g) -> uint32_t { return 4 * q4 * row_stride + g * ROWB + 2 * NDT * r16; };
+  auto load = [&](Stage& st, int phys, uint32_t koff, uint32_t voff) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)phys * blk_bytes, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)phys * blk_bytes, blk_bytes);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * s, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (NDT == 8)
+        st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, i * row_stride, kCpolNT);
+      else
+        st.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, kCpolNT);
+    }
+  };
+  // q of head r16 of an item as the B operand (k-step s: elements 32s + 8*q4
+  // .. +7, the order of the K rows).  Columns past the group read head 0's
+  // row: a column's scores, softmax state and output stay in that column of
+  // both products and are never stored, so the rows need no masking (and
+  // nothing waits for q before the block stream starts).
+  auto load_q = [&](u32x4 (&qb)[NS], const RowItem& d) __attribute__((always_inline)) {
+    const size_t row = ((size_t)d.t * a.num_q_heads + d.h0 + (r16 < d.nh ? r16 : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qb[s] = *(const u32x4*)((const uint16_t*)a.q + row + 32 * s + 8 * q4);
+  };
 
   while (true) {
     const bool has_next = nx < total;
     const int64_t nx2 = item_of(round + 2);
     RowItem nxt = cur;
     int btv_next = 0;
-    if (has_next) {  // prefetch: consumed only after this item
-      nxt = fetch_item<16>(a, nx, per_pair, n_head);
-      btv_next = fetch_ids(a, nxt, 0, lane);
-    }
+    bool btv_next_bad = false;
+    // The next item's descriptor and block ids (dependent loads: item ->
+    // request metadata -> block table) are consumed only after this item.
+    // They are requested once this item's first block is in flight, so their
+    // round trips overlap that block's instead of preceding it.
+    auto fetch_next = [&]() __attribute__((always_inline)) {
+      if (has_next) {
+        nxt = fetch_item<16>(a, nx, per_pair, n_head);
+        btv_next = fetch_ids(a, nxt, 0, lane);
+      }
+    };
     const size_t out_row = ((size_t)cur.t * a.num_q_heads + cur.h0) * D;
     if (cur.part == kNanRow) {
+      fetch_next();
+      btv_next_bad = check_ids(btv_next);
       for (int idx = lane; idx < cur.nh * D; idx += kWave) ((uint16_t*)a.out)[out_row + idx] = 0x7fc0;
     } else {
       const int g = cur.g, nh = cur.nh, vis = cur.vis;
       const bool col_ok = r16 < nh;
-      // q of head r16 (columns past the group read head 0's row, then zero it)
       u32x4 qb[NS];
-      const uint32_t qmask = col_ok ? 0xffffffffu : 0u;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        qb[s] = *(const u32x4*)((const uint16_t*)a.q + out_row + (col_ok ? r16 : 0) * D + 32 * s + 8 * q4) & qmask;
+      load_q(qb, cur);
 
       f32x4_t oacc[NDT];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       float m_ref = -INFINITY, lsum = 0.f;
-      bool bad = false;
-
-      struct Stage {
-        u32x4 k[NS];
-        VRow v[4];
-      };
-      const uint32_t koff = r16 * row_stride + g * ROWB + 16 * q4;
-      const uint32_t voff = 4 * q4 * row_stride + g * ROWB + 2 * NDT * r16;
-      auto load = [&](Stage& st, int phys) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)phys * blk_bytes, blk_bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)phys * blk_bytes, blk_bytes);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) st.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * s, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (NDT == 8)
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, i * row_stride, kCpolNT);
-          else
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, i * row_stride, kCpolNT);
-        }
-      };
+      bool bad = btv_bad;
+      const uint32_t koff = koff_of(g), voff = voff_of(g);
 
       auto compute = [&](const Stage& st, int jblk) __attribute__((always_inline)) {
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
@@ -677,30 +705,34 @@ __global__ __launch_bounds__(256, 2) void row_attn_mfma_kernel(RowParams a) {
         }
       };
 
-      // Blocks jb .. je-1, 64 ids at a time, NST - 1 blocks in flight ahead.
+      // Blocks jb .. je-1, 64 ids at a time, the next block always in flight
+      // (items of more than 64 blocks, whole rows without split-KV, fetch
+      // each further 64 ids when they reach them).
       const int n = cur.je - cur.jb;
+      Stage st[NST];
+      int btv_c = btv;
       for (int k0 = 0; k0 < n; k0 += kWave) {
-        if (k0 > 0) btv = fetch_ids(a, cur, k0, lane);
-        if (btv < 0 || btv >= a.num_blocks) {
-          btv = 0;
-          bad = true;
+        if (k0 > 0) {
+          btv_c = fetch_ids(a, cur, k0, lane);
+          bad |= check_ids(btv_c);
         }
         const int nb = min(kWave, n - k0);
         const int jfirst = cur.jb + k0;
-        Stage st[NST];
-#pragma unroll
-        for (int j = 0; j < NST - 1; ++j)
-          if (j < nb) load(st[j], __builtin_amdgcn_readlane(btv, j));
-        for (int k = 0; k < nb; k += NST) {
-#pragma unroll
-          for (int j = 0; j < NST; ++j) {
-            if (k + j < nb) {
-              if (k + j + NST - 1 < nb) load(st[(j + NST - 1) % NST], __builtin_amdgcn_readlane(btv, k + j + NST - 1));
-              compute(st[j], jfirst + k + j);
-            }
+        load(st[0], __builtin_amdgcn_readlane(btv_c, 0), koff, voff);
+        if (k0 == 0) fetch_next();
+        for (int k = 0; k < nb; k += 2) {
+          if (k + 1 < nb) load(st[1], __builtin_amdgcn_readlane(btv_c, k + 1), koff, voff);
+          compute(st[0], jfirst + k);
+          if (k + 1 < nb) {
+            if (k + 2 < nb) load(st[0], __builtin_amdgcn_readlane(btv_c, k + 2), koff, voff);
+            compute(st[1], jfirst + k + 1);
           }
         }
       }
+      if (n <= 0) fetch_next();
+      // (every load of this item has landed: checking the next ids here
+      // waits for nothing, and the next item's first loads wait for nothing)
+      btv_next_bad = check_ids(btv_next);
 
       // Finish: l over the head's four lanes; lane (r16, q4) holds O
       // elements NDT*(4*q4 + i) + dt of head r16.
@@ -742,6 +774,7 @@ __global__ __launch_bounds__(256, 2) void row_attn_mfma_kernel(RowParams a) {
     nx = nx2;
     cur = nxt;
     btv = btv_next;
+    btv_bad = btv_next_bad;
   }
 }
 

@@ -165,6 +165,21 @@ constexpr int kRsrcWord3 = 0x00020000;
 // row kernels' stream rate by 2-12% (K and V both non-temporal is slower
 // than V alone, and so is K alone on most of them).
 constexpr int kCpolNT = 2;
+// Read of step metadata (work items, query_start_loc, num_computed_tokens)
+// through the constant address space.  At a wave-uniform index it compiles to
+// a scalar load, whose completion is tracked by its own counter: waiting for
+// it does not also wait for the vector loads of the cache stream and the
+// output stores in flight, as a vector load's wait would.  Only for arrays no
+// kernel writes while the reading kernel runs.
+PKV_DEV int load_const(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+PKV_DEV int4 load_const(const int4* p, int64_t i) {
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  const i32x4_t x = ((const __attribute__((address_space(4))) i32x4_t*)p)[i];
+  return make_int4(x.x, x.y, x.z, x.w);
+}
+
 PKV_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
 }
