@@ -296,7 +296,7 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  *   With bf16 q and head_dim 128, prefill chunks run on the matrix-core
  *   prefill kernel, which dequantises each streamed tile in LDS (code *
  *   scale in float32, rounded to bf16) before both products.  Every other
- *   row (decode rows, split-KV partitions of rows past 512 tokens, and
+ *   row (decode rows, split-KV partitions of 1024 tokens, and
  *   prefill rows of other dtypes or head sizes) runs on a row kernel: with
  *   bf16 q all G query heads of a kv head share 16x16 matrix-core tiles over
  *   the exact integer codes, the scales entering in float32 (p * v_scale is

@@ -12,7 +12,7 @@
 // Decode is memory bound (same page, "Prefill vs Decode"): each K/V byte is
 // used G times and then never again, so the kernel is built to stream the
 // cache at full HBM bandwidth:
-//  * a work item is (row, kv head, partition of 512 tokens); every wave is an
+//  * a work item is (row, kv head, partition of 1024 tokens); every wave is an
 //    independent persistent worker that takes items in a fixed interleaved
 //    order and streams all blocks of its item itself (the 4 waves of a
 //    workgroup share nothing but the CU; each has its own small LDS tile);
@@ -913,7 +913,9 @@ int launch_rows_d(const RowParams& p, int64_t bound_waves, int cus, hipStream_t 
   const int gm = p.head_groups > 1 ? kMaxGroupRegs : p.group;
   if (gm <= 1) return launch_rows_g<BF16, D, 1>(p, bound_waves, cus, s);
   if (gm <= 2) return launch_rows_g<BF16, D, 2>(p, bound_waves, cus, s);
-  if (gm <= 4) return launch_rows_g<BF16, D, 4>(p, bound_waves, cus, s);
+  // (bf16 groups of 3 or 4 at head_dim 128 run on the MFMA row kernel)
+  if constexpr (!(BF16 && D == 128))
+    if (gm <= 4) return launch_rows_g<BF16, D, 4>(p, bound_waves, cus, s);
   return 1;
 }
 

@@ -10,7 +10,13 @@ namespace pkv {
 
 constexpr int kBlock = 16;        // tokens per cache block (fixed)
 constexpr int kWave = 64;         // CDNA wavefront width
-constexpr int kSplitTokens = 512; // split-KV partition length of a decode row
+// Split-KV partition length of a decode row: a constant, so a row's result
+// never depends on the rest of the batch.  Each partition is one work item of
+// a row kernel; 1024 tokens measured 4-8% faster row kernels than 512 on the
+// mixed, GQA and long-context decodes (bf16 and 8-bit caches alike: fewer,
+// longer items, fewer partials to write and merge) and unchanged or faster
+// on the Llama-7B-shaped one.
+constexpr int kSplitTokens = 1024;
 constexpr int kSplitBlocks = kSplitTokens / kBlock;
 constexpr int kMaxGroupRegs = 4;  // query heads per kv head handled by one wave
 

@@ -6,7 +6,7 @@
 // num_computed_tokens and num_tokens, with no separate prefill and decode
 // phases; one step therefore mixes single-token decodes and multi-token
 // prefill chunks.  This kernel sorts them:
-//   query_len == 1  -> decode row; split into 512-token partitions when the
+//   query_len == 1  -> decode row; split into 1024-token partitions when the
 //                      row is longer than one partition (split-KV), plus one
 //                      reduce item that merges the partitions;
 //   query_len  > 1  -> prefill tiles for the MFMA kernel (bf16), or one row

@@ -84,8 +84,9 @@ def test_workspace_size():
     small = pkv.paged_attention_workspace_size(4, 4, 8, 64, 1, 64)
     big = pkv.paged_attention_workspace_size(8, 8, 64, 128, 1, 32768)
     assert 0 < small < big
-    # 8 rows x 64 partitions x 64 heads x (128 + 2) floats of partials at least
-    assert big >= 8 * 64 * 64 * 130 * 4
+    # 8 rows x 32 partitions (1024 tokens each) x 64 heads x (128 + 2) floats
+    # of partials at least
+    assert big >= 8 * 32 * 64 * 130 * 4
     assert pkv.paged_attention_workspace_size(-1, 4, 8, 64, 1, 64) == 0
 
 

@@ -118,7 +118,7 @@ def test_int8_prefill_bad_block_id_confined_to_its_request():
     bt = wl.block_table.copy()
     bt[0, 4 * 130 + 1] = wl.num_blocks + 3
     bt[1, 5] = -2
-    bt[4, 70] = wl.num_blocks + 9     # a decode row: the third of its four 512-token partitions
+    bt[4, 70] = wl.num_blocks + 9     # a decode row: the second of its two 1024-token partitions
     out, *_ = _run(wl, "bf16", block_table=bt, expect_error=pkv.DEVERR_BLOCK_ID)
     o, gd = out_f64(out), out_f64(good)
     assert np.isnan(o[0:170]).all() and np.isnan(o[221]).all()
@@ -149,7 +149,7 @@ def test_int8_write_zero_rows_and_padding():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("n,all_rows", [(2, True), (4, False), (5, True)])
 def test_int8_workload_full_size(n, all_rows):
-    # the benchmark's decode, mixed-step and long-context (64 split-KV
+    # the benchmark's decode, mixed-step and long-context (32 split-KV
     # partitions per row) workloads at full size: every row of the decode
     # workloads, sampled rows of the mixed step
     _gpu()

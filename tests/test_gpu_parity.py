@@ -65,9 +65,10 @@ def test_small_ragged_batch(dtype, D, Hq, Hkv):
 
 
 def test_edge_lengths():
-    # context lengths around block and partition edges, one empty request
+    # context lengths around block and partition edges (split-KV partitions
+    # of 1024 tokens on these caches), one empty request
     reqs = [(0, 1), (14, 1), (15, 1), (16, 1), (511, 1), (512, 1), (1023, 1), (1024, 1),
-            (7, 0), (0, 17), (5, 16), (31, 33)]
+            (2047, 1), (2048, 1), (7, 0), (0, 17), (5, 16), (31, 33)]
     for dtype in ("f32", "bf16"):
         wl = workloads.build(workloads.small_spec(f"edges-{dtype}", 7, dtype, 8, 2, 128, reqs))
         _full_step(wl, f"edges-{dtype}")
@@ -221,7 +222,7 @@ def test_bad_metadata_sets_error_and_nan_rows(dtype, Hq, Hkv, D):
     assert device_error(s3) & pkv.DEVERR_BLOCK_ID
     assert np.isnan(out[4]).all()
     assert np.array_equal(out[[0, 1, 2, 3, 5]], good[[0, 1, 2, 3, 5]])
-    # request 3 (three 512-token partitions): a bad id in the middle one
+    # request 3 (two 1024-token partitions): a bad id in the first one
     s4 = upload(wl)
     run_write(s4)
     bt = s4.block_table.clone()
@@ -352,7 +353,7 @@ def _workspace_offsets(R, T, max_seq_len, tile_rows):
     the library documents: a 1 KiB header, then 256-byte aligned arrays)."""
     al = lambda x: (x + 255) // 256 * 256
     dec_rows = min(R, T)
-    parts = (max_seq_len + 511) // 512
+    parts = (max_seq_len + 1023) // 1024   # split-KV partitions of 1024 tokens
     cap_row = dec_rows * max(parts, 1) + T + 1
     cap_pf = T // tile_rows + R + 1
     cap_red = dec_rows + 1
