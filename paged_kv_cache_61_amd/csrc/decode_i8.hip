@@ -49,7 +49,7 @@ struct ItemI8 {
 PKV_DEV ItemI8 fetch_item_i8(const RowParams& a, int64_t it, int per_pair, int n_head, int gmax) {
   ItemI8 d;
   const int64_t e = it / per_pair;
-  const int4 item = e < n_head ? a.items[e] : a.items_tail[e - n_head];
+  const int4 item = e < n_head ? load_const(a.items, e) : load_const(a.items_tail, e - n_head);
   const int rem = (int)(it % per_pair);
   d.g = rem / a.head_groups;
   const int hg = rem - d.g * a.head_groups;
@@ -61,7 +61,7 @@ PKV_DEV ItemI8 fetch_item_i8(const RowParams& a, int64_t it, int per_pair, int n
   d.slot0 = item.w;
   d.vis = d.jb = d.je = 0;
   if (d.part != kNanRow) {
-    d.vis = a.nct[d.r] + (d.t - a.qsl[d.r]) + 1;
+    d.vis = load_const(a.nct, d.r) + (d.t - load_const(a.qsl, d.r)) + 1;
     const int nblk = (d.vis + kBlock - 1) / kBlock;
     d.je = nblk;
     if (d.part >= 0) {
