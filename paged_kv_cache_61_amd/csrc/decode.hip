@@ -239,7 +239,7 @@ PKV_DEV int fetch_ids(const RowParams& a, const RowItem& d, int k0, int lane) {
 // (A shared atomic work counter was measured slower: claims serialise on one
 // address.)
 template <bool BF16, int D, int GM>
-__global__ __launch_bounds__(256, 2) void row_attn_kernel(RowParams a) {
+__global__ __launch_bounds__(256, !BF16 && D == 128 ? 1 : 2) void row_attn_kernel(RowParams a) {
   using C = RowCfg<BF16, D>;
   using VT = typename VType<BF16>::T;
   using LN = Lanes<GM>;
