@@ -29,7 +29,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+          "-Wall", "-Wshadow", "-Wno-unused-function", "-Wno-unused-variable",
           "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 

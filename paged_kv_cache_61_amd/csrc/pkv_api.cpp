@@ -275,8 +275,6 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.kv_scales = kv_scales;
     fp.kv_fp8 = fp8 ? 1 : 0;
     fp.block_table = block_table;
-    fp.qsl = query_start_loc;
-    fp.nct = num_computed_tokens;
     fp.items = pp.prefill_items;
     fp.pf_order = pp.pf_order;
     fp.pf_slot_start = pp.pf_slot_start;

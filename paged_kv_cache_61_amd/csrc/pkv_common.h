@@ -43,8 +43,10 @@ static_assert((kHdrPrefillQueue + kMaxKvHeads) * 4 <= kHdrBytes, "header too sma
 constexpr int kWholeRow = -1;
 constexpr int kNanRow = -2;
 
-// Prefill item (int4): x = request, y = first query row of the tile
-// (relative to the request), z = rows in the tile, w = unused.
+// Prefill item (int4): x = request, y = the tile's first query token (its
+// row of q and out), z = rows in the tile, w = num_computed_tokens minus the
+// request's first query token, so y + w is the tile's first position.  The
+// prefill kernel needs no other per-request metadata than the block table.
 
 struct WsLayout {
   size_t row_items, row_items_tail, prefill_items, reduce_items, pf_order, pf_slot_start, part_ml, part_o, total;

@@ -67,9 +67,7 @@ struct PrefillParams {
   const void* q;
   const void* cache;
   const int32_t* block_table;
-  const int32_t* qsl;
-  const int32_t* nct;
-  const int4* items;
+  const int4* items;       // tiles (request, first query token, rows, computed - first token)
   int32_t* hdr;
   int32_t* err;
   const int32_t* pf_order;       // per-slot item lists, used when hdr[kHdrPrefillStatic] is 1

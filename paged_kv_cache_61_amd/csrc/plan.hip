@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
           const int rows = min(a.prefill_tile_rows, q.ql - row0);
           const int tiles = pf_bucket(q, row0, rows);
           const int pos = atomicAdd(&pf_off[tiles], 1);
-          a.prefill_items[pos] = make_int4(r, row0, rows, 0);
+          a.prefill_items[pos] = make_int4(r, q.qs + row0, rows, q.c - q.qs);
           if (pos < kPfMaxStatic) pf_tiles[pos] = tiles;
         }
       }

@@ -235,8 +235,7 @@ PKV_DEV u32x4 buffer_desc(const void* base, uint32_t bytes) {
 // wave-uniform reads become scalar loads, which never wait on the tile stream.
 template <int D, bool I8, bool FP8>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
-    PrefillParams a, const int4* __restrict__ items, const int32_t* __restrict__ qsl,
-    const int32_t* __restrict__ nct, const int32_t* __restrict__ block_table) {
+    PrefillParams a, const int4* __restrict__ items, const int32_t* __restrict__ block_table) {
   static_assert(D == 128 || (D == 64 && !I8), "bf16 cache: head_dim 64 or 128; 8-bit cache: 128");
   using Cf = PfCfg<D>;
   constexpr int kRowB = Cf::kRowB, kHalfTile = Cf::kHalfTile, kStage = Cf::kStage;
@@ -336,7 +335,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   __syncthreads();
 
   // State of the item being run, set by begin_item.
-  int r = 0, row0 = 0, nrows = 0, c = 0, qs = 0, kv_end = 0, ntiles = 0, pos_abs = 0, nxt = 0;
+  int r = 0, tpos0 = 0, nrows = 0, kv_end = 0, ntiles = 0, pos_abs = 0, nxt = 0;
   const int32_t* bt = block_table;
   int ids0 = 0, ids1 = 0;   // block ids, see begin_item
   bool bad = false, row_ok = false;
@@ -400,13 +399,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // latencies overlap that item's epilogue.
   auto begin_item = [&](int ee) PKV_INLINE {
     if (tid == 0) nxt = take();
-    const int4 item = items[ee];
+    const int4 item = items[ee];   // the one metadata read before the block ids
     r = item.x;
-    row0 = item.y;
+    const int tok0 = item.y;      // the tile's first query token
     nrows = item.z;
-    c = nct[r];
-    qs = qsl[r];
-    kv_end = c + row0 + nrows;  // keys 0 .. kv_end-1 are read
+    tpos0 = (int)((int64_t)item.y + item.w);  // its position: num_computed_tokens + first row
+    kv_end = tpos0 + nrows;       // keys 0 .. kv_end-1 are read
     ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
     bt = block_table + (size_t)r * a.max_blocks_per_req;
     const int kb0 = (kPfKeys / kBlock) * lane + cblk;
@@ -417,8 +415,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
     const int head = rho - pos * G;
     row_ok = rho < BQ * G && pos < nrows;
     if (!row_ok) pos = nrows - 1;  // padding rows: any visible row, loaded and zeroed
-    pos_abs = c + row0 + pos;
-    qrow = ((size_t)(qs + row0 + pos) * a.num_q_heads + g * G + head) * D;
+    pos_abs = tpos0 + pos;
+    qrow = ((size_t)(tok0 + pos) * a.num_q_heads + g * G + head) * D;
     const uint32_t qmask = row_ok ? 0xffffffffu : 0u;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
@@ -578,7 +576,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
       const int kv0 = t * kPfKeys;
       // Causal mask only on tiles that reach past the first row's position,
       // then the online softmax on raw dots: p = exp2(dot*|scale|*log2 e - ref).
-      if (kv0 + kPfKeys - 1 > c + row0) {
+      if (kv0 + kPfKeys - 1 > tpos0) {
         const int rel = pos_abs - kv0 - 4 * half;  // key index limit for this lane
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -739,7 +737,7 @@ int launch_prefill(const PrefillParams& p, int32_t head_dim, int64_t grid, hipSt
            : !p.kv_scales ? prefill_kernel<128, false, false>
            : p.kv_fp8     ? prefill_kernel<128, true, true>
                           : prefill_kernel<128, true, false>;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.qsl, p.nct, p.block_table);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfThreads), 0, stream, p, p.items, p.block_table);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -340,8 +340,12 @@ def test_prefill_static_item_assignment(Hq, Hkv, reqs):
     start = ws[off["pf_slot_start"]:off["pf_slot_start"] + 4 * (W + 1)].view(np.int32)
     assert sorted(order.tolist()) == list(range(n))
     assert start[0] == 0 and start[W] == n and np.all(np.diff(start) >= 0)
+    # item (request, first query token, rows, num_computed_tokens - first
+    # token of the request): first token + last field = the tile's position
+    qsl = wl.query_start_loc
     c = wl.num_computed_tokens
-    tiles = np.array([(int(c[r]) + row0 + rows + 63) // 64 for r, row0, rows, _ in items])
+    assert all(int(c[r]) - int(qsl[r]) == w for r, _, _, w in items)
+    tiles = np.array([(tok0 + w + rows + 63) // 64 for _, tok0, rows, w in items])
     assert np.all(np.diff(tiles) <= 0), "items are listed longest first"
     cost = 10 * tiles + 50
     got = sorted(int(cost[order[start[k]:start[k + 1]]].sum()) for k in range(W))
