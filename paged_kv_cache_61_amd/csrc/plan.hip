@@ -17,9 +17,19 @@
 // The partition count depends only on the row's own length, so a request's
 // result is the same whatever else is in the batch.
 //
-// One workgroup of 1024 threads walks the requests 1024 at a time and places
-// each request's items with a block-wide exclusive scan.  No host sync is
-// needed: the later kernels read the counts from the workspace header.
+// One workgroup of 1024 threads.  Requests are taken 8192 at a time; thread t
+// owns a contiguous run of up to 8 of them, loads all their metadata at once
+// and keeps it in registers, so a step of up to 8192 requests costs one
+// round trip to memory and one block-wide scan (DPP inside each wave, one
+// barrier across waves) to place every request's items in request order.
+// The longest-first lists are counting sorts: a histogram in LDS, a scan of
+// the buckets, then a scatter; the tiles of a prefill request are counted
+// and placed by all 64 lanes of its owner's wave.  The static prefill
+// assignment (first fit decreasing, the last wave) runs while the other
+// waves scatter.  The barriers order LDS only: no thread reads another's
+// work-list stores (the later kernels do), so none waits for them.  No host
+// sync is needed: the later kernels read the counts from the workspace
+// header.
 #include "pkv_common.h"
 #include "pkv_internal.h"
 
@@ -29,55 +39,74 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kReqPerThread = 8;                           // requests a thread owns per chunk
+constexpr int kChunkReqs = kPlanThreads * kReqPerThread;   // requests per chunk
 
 struct Counts {
   int rows, prefill, reduce, slots, tail;
 };
 
-// Exclusive scan of the five counters over the workgroup; returns the prefix
-// and writes the workgroup total to `total`.
-constexpr int kNC = 5;
-__device__ Counts block_exclusive_scan(Counts c, Counts* total) {
-  __shared__ int wave_tot[kPlanWaves][kNC];
-  __shared__ int wave_off[kPlanWaves][kNC];
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// makes this thread's global stores visible to the workgroup, i.e. waits
+// until every work-list store in flight has completed (a memory round trip
+// per barrier); no thread here reads another's global writes (only the
+// later kernels do), so the barriers need not wait for them.
+PKV_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Inclusive sum over the 64 lanes of a wave (every lane active): shifts by
+// 1, 2, 4 and 8 inside each row of 16 lanes, then row 0's and row 1's last
+// lanes broadcast into the rows after them (the gfx9 DPP row_bcast forms).
+// Lanes a DPP move leaves without a source keep the 0 passed as `old`.
+PKV_DEV int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Exclusive scan of N counters over the workgroup (every thread calls it):
+// ex[c] = sum of v[c] over lower threads, tot[c] = the workgroup's sum.
+// `lds` holds the wave totals; it is written before and read after the one
+// barrier, so a caller that scans again into the same array must put a
+// barrier between the two calls.
+template <int N>
+__device__ void block_scan(const int (&v)[N], int (&ex)[N], int (&tot)[N], int (*lds)[8]) {
+  static_assert(N <= 8, "at most 8 counters");
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  int v[kNC] = {c.rows, c.prefill, c.reduce, c.slots, c.tail};
-  int inc[kNC];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int inc[N];
 #pragma unroll
-  for (int j = 0; j < kNC; ++j) {
-    int x = v[j];
-    for (int off = 1; off < kWave; off <<= 1) {
-      int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    inc[j] = x;
-  }
+  for (int c = 0; c < N; ++c) inc[c] = wave_incl_sum(v[c]);
   if (lane == kWave - 1) {
 #pragma unroll
-    for (int j = 0; j < kNC; ++j) wave_tot[w][j] = inc[j];
+    for (int c = 0; c < N; ++c) lds[w][c] = inc[c];
   }
-  __syncthreads();
-  if (threadIdx.x < kNC) {
-    int run = 0;
-    for (int i = 0; i < kPlanWaves; ++i) {
-      wave_off[i][threadIdx.x] = run;
-      run += wave_tot[i][threadIdx.x];
-    }
-    wave_tot[0][threadIdx.x] = run;  // reuse row 0 for the totals
+  lds_barrier();
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    // lanes 0..15 hold the 16 wave totals; their inclusive sums inside row 0
+    int t = lane < kPlanWaves ? lds[lane][c] : 0;
+    t += __builtin_amdgcn_update_dpp(0, t, 0x111, 0xf, 0xf, false);
+    t += __builtin_amdgcn_update_dpp(0, t, 0x112, 0xf, 0xf, false);
+    t += __builtin_amdgcn_update_dpp(0, t, 0x114, 0xf, 0xf, false);
+    t += __builtin_amdgcn_update_dpp(0, t, 0x118, 0xf, 0xf, false);
+    const int before = w > 0 ? __builtin_amdgcn_readlane(t, w - 1) : 0;
+    tot[c] = __builtin_amdgcn_readlane(t, kPlanWaves - 1);
+    ex[c] = inc[c] - v[c] + before;
   }
-  __syncthreads();
-  Counts ex{inc[0] - v[0] + wave_off[w][0], inc[1] - v[1] + wave_off[w][1],
-            inc[2] - v[2] + wave_off[w][2], inc[3] - v[3] + wave_off[w][3],
-            inc[4] - v[4] + wave_off[w][4]};
-  *total = Counts{wave_tot[0][0], wave_tot[0][1], wave_tot[0][2], wave_tot[0][3], wave_tot[0][4]};
-  __syncthreads();
-  return ex;
 }
 
 // Buckets of the counting sorts that list work longest first.
 constexpr int kPfBuckets = 4096;          // prefill tiles by KV tiles to read (clamped)
-static_assert(kPfBuckets % 1024 == 0, "buckets split evenly over the plan threads");
+static_assert(kPfBuckets % kPlanThreads == 0, "buckets split evenly over the plan threads");
+constexpr int kBucketsPerThread = kPfBuckets / kPlanThreads;
 constexpr int kTailBuckets = kSplitBlocks; // partial partitions by block count
 
 struct ReqInfo {
@@ -85,14 +114,10 @@ struct ReqInfo {
   int qs, ql, L, c, nparts, err;
 };
 
-__device__ ReqInfo classify(const PlanParams& a, int r) {
-  ReqInfo q{0, 0, 0, 0, 0, 1, 0};
-  if (r >= a.num_reqs) return q;
-  q.qs = a.qsl[r];
-  const int qe = a.qsl[r + 1];
-  q.ql = qe - q.qs;
-  q.L = a.seq_lens[r];
-  q.c = a.nct[r];
+// Request r's metadata (query_start_loc[r], query_start_loc[r + 1],
+// seq_lens[r], num_computed_tokens[r]) checked and classified.
+__device__ ReqInfo classify(const PlanParams& a, int r, int qs, int qe, int L, int c) {
+  ReqInfo q{0, qs, qe - qs, L, c, 1, 0};
   const bool qsl_ok = q.qs >= 0 && q.ql >= 0 && (int64_t)qe <= a.num_tokens && (r > 0 || q.qs == 0);
   if (!qsl_ok) {
     q.err |= PKV_DEVERR_QSL;
@@ -112,10 +137,31 @@ __device__ ReqInfo classify(const PlanParams& a, int r) {
   return q;
 }
 
+// Items a request contributes: full partitions or query rows (rows), its
+// partial last partition (tail), prefill tiles, its reduce item and the
+// partial slots of its partitions.
+__device__ Counts count_items(const PlanParams& a, const ReqInfo& q) {
+  Counts m{0, 0, 0, 0, 0};
+  if (q.kind == 1) {
+    const bool partial_last = q.L % kSplitTokens != 0;
+    m.rows = q.nparts - (partial_last ? 1 : 0);
+    m.tail = partial_last ? 1 : 0;
+    if (q.nparts > 1) {
+      m.reduce = 1;
+      m.slots = q.nparts;
+    }
+  } else if (q.kind == 2) {
+    m.prefill = (q.ql + a.prefill_tile_rows - 1) / a.prefill_tile_rows;
+  } else if (q.kind == 3 || q.kind == 4) {
+    m.rows = q.ql;
+  }
+  return m;
+}
+
 // KV tiles (of 64 keys) a prefill tile starting at query row0 with `rows`
 // rows reads: its bucket in the longest-first order.
-__device__ int pf_bucket(const ReqInfo& q, int row0, int rows) {
-  const int kv_end = q.c + row0 + rows;
+__device__ int pf_bucket(int c, int row0, int rows) {
+  const int kv_end = c + row0 + rows;
   return min((kv_end + 63) / 64, kPfBuckets - 1);
 }
 
@@ -146,30 +192,50 @@ PKV_DEV int wave_max_i(int x) {
 // ballot per item instead of a wave-wide maximum.  An item costing more than
 // half the capacity fits in no slot that already holds one (those hold items
 // at least as long), so the first such items, up to W, take slots 0, 1, ...
-// directly; the rest are placed one by one.  Lane s of the calling wave holds
-// slot s's load and item count (loads stay below 2^24: at most 256 items of
-// at most 4095 tiles).  Writes slot_of[i] and the item's rank inside its
+// directly; the rest are placed one by one, in a loop whose index and item
+// cost are wave-uniform (scalar).  Lane s of the calling wave holds slot s's
+// load and item count (loads stay below 2^24: at most 256 items of at most
+// 4095 tiles); lane l also holds the costs and results of items l, l + 64,
+// l + 128 and l + 192.  Writes slot_of[i] and the item's rank inside its
 // slot, then the slot offsets (exclusive sums of the counts).
 PKV_DEV int item_cost(int tiles) { return 10 * tiles + 50; }
 
-PKV_DEV void assign_first_fit(const int* tiles, int n, int W, int* slot_of, int* rank_of, int* slot_start) {
+PKV_DEV void assign_first_fit(const int* tiles, int n_in, int W_in, int* slot_of, int* rank_of, int* slot_start) {
+  static_assert(kPfMaxStatic == 4 * kWave && kPfMaxSlots <= kWave, "four items per lane, one slot per lane");
   const int lane = threadIdx.x & (kWave - 1);
-  int total = 0, big = 0;
-  for (int i = lane; i < n; i += kWave) total += item_cost(tiles[i]);
-  for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
+  const int n = __builtin_amdgcn_readfirstlane(n_in);
+  const int W = __builtin_amdgcn_readfirstlane(W_in);
+  int cst[4], res_slot[4], res_rank[4];
+  int sum = 0, nbig = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int i = lane + kWave * s;
+    cst[s] = i < n ? item_cost(tiles[i]) : 0;
+    sum += cst[s];
+  }
+  const int total = __builtin_amdgcn_readlane(wave_incl_sum(sum), kWave - 1);
   const int cap = (total + W - 1) / W + 5;
-  for (int i = lane; i < n; i += kWave) big += 2 * item_cost(tiles[i]) > cap ? 1 : 0;
-  for (int off = 32; off > 0; off >>= 1) big += __shfl_xor(big, off);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) nbig += 2 * cst[s] > cap ? 1 : 0;
+  const int big = __builtin_amdgcn_readlane(wave_incl_sum(nbig), kWave - 1);
   const int p = min(big, W);                        // items placed directly: item i in slot i
   const bool live = lane < W;
-  int load = lane < p ? item_cost(tiles[lane]) : 0;
+  const uint64_t live_mask = __ballot(live);
+  int load = lane < p ? cst[0] : 0;
   int cnt = lane < p ? 1 : 0;
-  for (int i0 = 0; i0 < n; i0 += kWave) {
-    const int tl = i0 + lane < n ? tiles[i0 + lane] : 0;
-    int slot = i0 + lane < p ? i0 + lane : 0, rank = 0;   // for item i0 + lane
-    for (int j = max(p - i0, 0); j < kWave && i0 + j < n; ++j) {
-      const int c = item_cost(__builtin_amdgcn_readlane(tl, j));
-      const uint64_t fits = __ballot(live && load + c <= cap);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    res_slot[s] = 0;
+    res_rank[s] = 0;
+  }
+  res_slot[0] = lane < p ? lane : 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int j_end = min(n - kWave * s, kWave);
+    for (int j = max(p - kWave * s, 0); j < j_end; ++j) {   // item kWave * s + j
+      const int c = __builtin_amdgcn_readlane(cst[s], j);
+      const int room = cap - c;   // scalar: one vector compare per item
+      const uint64_t fits = __ballot(load <= room) & live_mask;
       int win;
       if (fits) {
         win = __builtin_ctzll(fits);
@@ -178,31 +244,34 @@ PKV_DEV void assign_first_fit(const int* tiles, int n, int W, int* slot_of, int*
         win = 63 - (__builtin_amdgcn_readfirstlane(m) & 63);
       }
       const int r = __builtin_amdgcn_readlane(cnt, win);
-      const bool mine = lane == win;
-      load += mine ? c : 0;
-      cnt += mine ? 1 : 0;
-      slot = lane == j ? win : slot;
-      rank = lane == j ? r : rank;
+      if (lane == win) {
+        load += c;
+        cnt += 1;
+      }
+      if (lane == j) {
+        res_slot[s] = win;
+        res_rank[s] = r;
+      }
     }
-    if (i0 + lane < n) {
-      slot_of[i0 + lane] = slot;
-      rank_of[i0 + lane] = rank;
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int i = lane + kWave * s;
+    if (i < n) {
+      slot_of[i] = res_slot[s];
+      rank_of[i] = res_rank[s];
     }
   }
   // exclusive sums of the counts (W <= 64 lanes)
-  __shared__ int cnt_lds[kPfMaxSlots];
-  cnt_lds[lane] = cnt;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int st = 0;
-  for (int j = 0; j < lane; ++j) st += cnt_lds[j];
-  if (lane < W) slot_start[lane] = st;
+  const int cl = live ? cnt : 0;
+  const int st = wave_incl_sum(cl) - cl;
+  if (live) slot_start[lane] = st;
   if (lane == 0) slot_start[W] = n;   // W may be 64: no lane W
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   __shared__ int err_acc;
+  __shared__ int scan_lds[3][kPlanWaves][8];
   __shared__ int pf_tiles[kPfMaxStatic], pf_slot_of[kPfMaxStatic], pf_rank[kPfMaxStatic];
   __shared__ int pf_start[kPfMaxSlots + 1];
   __shared__ int pf_off[kPfBuckets];
@@ -210,86 +279,134 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   for (int i = threadIdx.x; i < kPfBuckets; i += kPlanThreads) pf_off[i] = 0;
   if (threadIdx.x < kTailBuckets) tail_off[threadIdx.x] = 0;
   if (threadIdx.x == 0) err_acc = 0;
-  __syncthreads();
+  lds_barrier();
 
-  // Pass 1: check requests, place decode rows (full partitions) and reduce
-  // items, count everything, and histogram the items that are sorted.
-  Counts base{0, 0, 0, 0, 0};
-  ReqInfo first{};  // this thread's request of the first pass, reused by pass 2
-  for (int r0 = 0; r0 < a.num_reqs; r0 += kPlanThreads) {
-    const int r = r0 + threadIdx.x;
-    const ReqInfo q = classify(a, r);
-    if (r0 == 0) first = q;
-    int err = q.err;
-    const bool partial_last = q.kind == 1 && q.L % kSplitTokens != 0;
-    Counts mine{0, 0, 0, 0, 0};
-    if (q.kind == 1) {
-      mine.rows = q.nparts - (partial_last ? 1 : 0);
-      mine.tail = partial_last ? 1 : 0;
-      if (q.nparts > 1) {
-        mine.reduce = 1;
-        mine.slots = q.nparts;
-      }
-    } else if (q.kind == 2) {
-      mine.prefill = (q.ql + a.prefill_tile_rows - 1) / a.prefill_tile_rows;
-    } else if (q.kind == 3 || q.kind == 4) {
-      mine.rows = q.ql;
+  const int nreq = a.num_reqs;
+  const int nchunks = (nreq + kChunkReqs - 1) / kChunkReqs;
+  // This thread's requests of the current chunk: rbeg .. rbeg + kown - 1.
+  ReqInfo qi[kReqPerThread];
+  int rbeg = 0, kown = 0;
+  auto load_chunk = [&](int c0) {
+    const int nc = min(kChunkReqs, nreq - c0);
+    const int per = (nc + kPlanThreads - 1) / kPlanThreads;
+    rbeg = c0 + (int)threadIdx.x * per;
+    kown = max(0, min(per, c0 + nc - rbeg));
+    // Every load is issued before any is used (one round trip); indices are
+    // clamped into the arrays, and requests past this thread's run are
+    // classified as empty.
+    int qs[kReqPerThread + 1], L[kReqPerThread], c[kReqPerThread];
+#pragma unroll
+    for (int k = 0; k <= kReqPerThread; ++k) qs[k] = a.qsl[min(rbeg + k, nreq)];
+#pragma unroll
+    for (int k = 0; k < kReqPerThread; ++k) {
+      L[k] = a.seq_lens[min(rbeg + k, nreq - 1)];
+      c[k] = a.nct[min(rbeg + k, nreq - 1)];
     }
-    Counts tot;
-    Counts ex = block_exclusive_scan(mine, &tot);
-    ex.rows += base.rows;
-    ex.reduce += base.reduce;
-    ex.slots += base.slots;
-    const bool fits = ex.rows + mine.rows <= a.cap_row_items &&
-                      base.tail + tot.tail <= a.cap_row_items &&
-                      base.prefill + tot.prefill <= a.cap_prefill_items &&
-                      ex.reduce + mine.reduce <= a.cap_reduce && ex.slots + mine.slots <= a.cap_slots;
-    if (!fits) {
-      err |= PKV_DEVERR_CAPACITY;
-    } else if (q.kind == 1) {
-      const int nfull = q.nparts - (partial_last ? 1 : 0);
-      for (int p = 0; p < nfull; ++p)
-        a.row_items[ex.rows + p] =
-            make_int4(q.qs, r, q.nparts == 1 ? kWholeRow : p, q.nparts == 1 ? -1 : ex.slots);
-      if (partial_last) atomicAdd(&tail_off[(q.L % kSplitTokens + kBlock - 1) / kBlock - 1], 1);
-      if (q.nparts > 1) a.reduce_items[ex.reduce] = make_int4(q.qs, r, q.nparts, ex.slots);
-    } else if (q.kind == 2) {
-      for (int row0 = 0; row0 < q.ql; row0 += a.prefill_tile_rows)
-        atomicAdd(&pf_off[pf_bucket(q, row0, min(a.prefill_tile_rows, q.ql - row0))], 1);
-    } else if (q.kind == 3 || q.kind == 4) {
-      const int z = q.kind == 3 ? kWholeRow : kNanRow;
-      for (int i = 0; i < q.ql; ++i) a.row_items[ex.rows + i] = make_int4(q.qs + i, r, z, -1);
+#pragma unroll
+    for (int k = 0; k < kReqPerThread; ++k)
+      qi[k] = k < kown ? classify(a, rbeg + k, qs[k], qs[k + 1], L[k], c[k]) : ReqInfo{0, 0, 0, 0, 0, 1, 0};
+  };
+
+  // Pass 1: check requests, place decode rows (full partitions), reduce
+  // items and per-query rows, count everything, and histogram the items that
+  // are sorted.
+  Counts base{0, 0, 0, 0, 0};
+  int slot_first = 0;   // (single chunk) partial slot of this thread's first split row
+  for (int ch = 0; ch < nchunks; ++ch) {
+    if (ch > 0) lds_barrier();   // scan_lds[0] is read by every thread before it is rewritten
+    load_chunk(ch * kChunkReqs);
+    int own[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kReqPerThread; ++k) {
+      const Counts m = count_items(a, qi[k]);
+      own[0] += m.rows;
+      own[1] += m.prefill;
+      own[2] += m.reduce;
+      own[3] += m.slots;
+      own[4] += m.tail;
+    }
+    int ex[5], tot[5];
+    block_scan<5>(own, ex, tot, scan_lds[0]);
+    int rowpos = base.rows + ex[0], redpos = base.reduce + ex[2], slotpos = base.slots + ex[3];
+    slot_first = slotpos;
+    const bool sorted_fit = base.tail + tot[4] <= a.cap_row_items && base.prefill + tot[1] <= a.cap_prefill_items;
+    int err = 0;
+    bool pf_req[kReqPerThread];   // prefill requests whose tiles go into the histogram
+#pragma unroll
+    for (int k = 0; k < kReqPerThread; ++k) {
+      pf_req[k] = false;
+      if (k >= kown) continue;
+      const ReqInfo q = qi[k];
+      const int r = rbeg + k;
+      const Counts m = count_items(a, q);
+      err |= q.err;
+      const bool fits = sorted_fit && rowpos + m.rows <= a.cap_row_items && redpos + m.reduce <= a.cap_reduce &&
+                        slotpos + m.slots <= a.cap_slots;
+      if (!fits) {
+        err |= PKV_DEVERR_CAPACITY;
+      } else if (q.kind == 1) {
+        for (int p = 0; p < m.rows; ++p)
+          a.row_items[rowpos + p] = make_int4(q.qs, r, q.nparts == 1 ? kWholeRow : p, q.nparts == 1 ? -1 : slotpos);
+        if (m.tail) atomicAdd(&tail_off[(q.L % kSplitTokens + kBlock - 1) / kBlock - 1], 1);
+        if (m.reduce) a.reduce_items[redpos] = make_int4(q.qs, r, q.nparts, slotpos);
+      } else if (q.kind == 2) {
+        pf_req[k] = true;
+      } else if (q.kind == 3 || q.kind == 4) {
+        const int z = q.kind == 3 ? kWholeRow : kNanRow;
+        for (int i = 0; i < q.ql; ++i) a.row_items[rowpos + i] = make_int4(q.qs + i, r, z, -1);
+      }
+      rowpos += m.rows;
+      redpos += m.reduce;
+      slotpos += m.slots;
+    }
+    // A prefill request's tiles are histogrammed by the whole wave, one tile
+    // per lane (a request may have thousands; its owner alone would count
+    // them one by one).
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 0; k < kReqPerThread; ++k) {
+      for (uint64_t m = __ballot(pf_req[k]); m; m &= m - 1) {
+        const int src = __builtin_ctzll(m);
+        const int ql = __builtin_amdgcn_readlane(qi[k].ql, src), c = __builtin_amdgcn_readlane(qi[k].c, src);
+        const int tr = a.prefill_tile_rows;
+        for (int row0 = lane * tr; row0 < ql; row0 += kWave * tr)
+          atomicAdd(&pf_off[pf_bucket(c, row0, min(tr, ql - row0))], 1);
+      }
     }
     if (err) atomicOr(&err_acc, err);
-    base.rows += tot.rows;
-    base.prefill += tot.prefill;
-    base.reduce += tot.reduce;
-    base.slots += tot.slots;
-    base.tail += tot.tail;
+    base.rows += tot[0];
+    base.prefill += tot[1];
+    base.reduce += tot[2];
+    base.slots += tot[3];
+    base.tail += tot[4];
   }
-  __syncthreads();
   const bool over = base.rows > a.cap_row_items || base.tail > a.cap_row_items ||
                     base.prefill > a.cap_prefill_items || base.reduce > a.cap_reduce ||
                     base.slots > a.cap_slots;
   // Bucket offsets, longest bucket first: thread t owns the 4 buckets at
-  // descending positions 4t .. 4t+3 of the prefill list; thread 0 also does
-  // the 32 tail buckets.  (Skipped, like pass 2, when nothing is sorted:
+  // descending positions 4t .. 4t+3 of the prefill list and writes the tile
+  // count of each of their positions below kPfMaxStatic (the first-fit
+  // input: items of one bucket cost the same, so the assignment does not
+  // depend on which of them the scatter puts where); thread 0 also does the
+  // 32 tail buckets.  (Skipped, like the scatter, when nothing is sorted:
   // base is the same in every thread.)
   const bool sorted_work = base.prefill > 0 || base.tail > 0;
+  lds_barrier();   // the histograms are complete
   if (sorted_work) {
-    constexpr int kPer = kPfBuckets / kPlanThreads;
-    int n[kPer], local = 0;
+    int n[kBucketsPerThread], local[1] = {0}, run[1], tot[1];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      n[i] = pf_off[kPfBuckets - 1 - (kPer * threadIdx.x + i)];
-      local += n[i];
+    for (int i = 0; i < kBucketsPerThread; ++i) {
+      n[i] = pf_off[kPfBuckets - 1 - (kBucketsPerThread * threadIdx.x + i)];
+      local[0] += n[i];
     }
-    Counts tot;
-    int run = block_exclusive_scan(Counts{local, 0, 0, 0, 0}, &tot).rows;
+    block_scan<1>(local, run, tot, scan_lds[1]);
+    int off = run[0];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      pf_off[kPfBuckets - 1 - (kPer * threadIdx.x + i)] = run;
-      run += n[i];
+    for (int i = 0; i < kBucketsPerThread; ++i) {
+      const int b = kPfBuckets - 1 - (kBucketsPerThread * threadIdx.x + i);
+      pf_off[b] = off;
+      for (int q = off; q < min(off + n[i], kPfMaxStatic); ++q) pf_tiles[q] = b;
+      off += n[i];
     }
     if (threadIdx.x == 0) {
       int trun = 0;
@@ -300,44 +417,62 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // Pass 2: scatter the sorted items (order inside a bucket is irrelevant:
-  // an item's result does not depend on which worker computes it).
-  if (!over && sorted_work) {
-    int slot_base = 0;  // the split rows' partial slots, recomputed as in pass 1
-    for (int r0 = 0; r0 < a.num_reqs; r0 += kPlanThreads) {
-      const int r = r0 + threadIdx.x;
-      const ReqInfo q = r0 == 0 ? first : classify(a, r);
-      Counts mine{0, 0, 0, 0, 0};
-      if (q.kind == 1 && q.nparts > 1) mine.slots = q.nparts;
-      Counts tot;
-      const int slot0 = block_exclusive_scan(mine, &tot).slots + slot_base;
-      slot_base += tot.slots;
-      if (q.kind == 1 && q.L % kSplitTokens != 0) {
-        const int nb = (q.L % kSplitTokens + kBlock - 1) / kBlock;
-        const int pos = atomicAdd(&tail_off[nb - 1], 1);
-        a.row_items_tail[pos] = q.nparts == 1 ? make_int4(q.qs, r, kWholeRow, -1)
-                                              : make_int4(q.qs, r, q.nparts - 1, slot0);
-      } else if (q.kind == 2) {
-        for (int row0 = 0; row0 < q.ql; row0 += a.prefill_tile_rows) {
-          const int rows = min(a.prefill_tile_rows, q.ql - row0);
-          const int tiles = pf_bucket(q, row0, rows);
-          const int pos = atomicAdd(&pf_off[tiles], 1);
-          a.prefill_items[pos] = make_int4(r, q.qs + row0, rows, q.c - q.qs);
-          if (pos < kPfMaxStatic) pf_tiles[pos] = tiles;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // Static prefill assignment when it is small enough to build here (one
-  // wave); otherwise the prefill kernel takes items from per-head queues.
+  // Static prefill assignment when it is small enough to build here (the last
+// wave, whose threads own the last requests and usually none);
+  // otherwise the prefill kernel takes items from per-head queues.
   const int npf = base.prefill;
   const bool pf_static = !over && npf > 0 && npf <= kPfMaxStatic && a.prefill_slots > 0 &&
                          a.prefill_slots <= kPfMaxSlots;
-  if (pf_static && threadIdx.x < kWave) assign_first_fit(pf_tiles, npf, a.prefill_slots, pf_slot_of, pf_rank, pf_start);
-  __syncthreads();
+  if (pf_static && threadIdx.x >= kPlanThreads - kWave) assign_first_fit(pf_tiles, npf, a.prefill_slots, pf_slot_of, pf_rank, pf_start);
+
+  // Pass 2: scatter the sorted items (order inside a bucket is irrelevant:
+  // an item's result does not depend on which worker computes it).  With one
+  // chunk every thread still holds its requests and the partial slot of its
+  // first split row; otherwise each chunk is loaded and scanned again.
+  if (!over && sorted_work) {
+    int slot_base = 0;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      int sp = slot_first;
+      if (nchunks > 1) {
+        if (ch > 0) lds_barrier();   // scan_lds[2] is read by every thread before it is rewritten
+        load_chunk(ch * kChunkReqs);
+        int own[1] = {0}, ex[1], tot[1];
+#pragma unroll
+        for (int k = 0; k < kReqPerThread; ++k) own[0] += count_items(a, qi[k]).slots;
+        block_scan<1>(own, ex, tot, scan_lds[2]);
+        sp = slot_base + ex[0];
+        slot_base += tot[0];
+      }
+      const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+      for (int k = 0; k < kReqPerThread; ++k) {
+        const ReqInfo q = qi[k];   // empty past this thread's run
+        const int r = rbeg + k;
+        if (q.kind == 1 && q.L % kSplitTokens != 0) {
+          const int nb = (q.L % kSplitTokens + kBlock - 1) / kBlock;
+          const int pos = atomicAdd(&tail_off[nb - 1], 1);
+          a.row_items_tail[pos] = q.nparts == 1 ? make_int4(q.qs, r, kWholeRow, -1)
+                                                : make_int4(q.qs, r, q.nparts - 1, sp);
+        }
+        // a prefill request's tiles are placed by the whole wave, one per lane
+        for (uint64_t m = __ballot(q.kind == 2); m; m &= m - 1) {
+          const int src = __builtin_ctzll(m);
+          const int qs = __builtin_amdgcn_readlane(q.qs, src), ql = __builtin_amdgcn_readlane(q.ql, src);
+          const int c = __builtin_amdgcn_readlane(q.c, src), rq = __builtin_amdgcn_readlane(r, src);
+          const int tr = a.prefill_tile_rows;
+          for (int row0 = lane * tr; row0 < ql; row0 += kWave * tr) {
+            const int rows = min(tr, ql - row0);
+            const int pos = atomicAdd(&pf_off[pf_bucket(c, row0, rows)], 1);
+            a.prefill_items[pos] = make_int4(rq, qs + row0, rows, c - qs);
+          }
+        }
+        if (q.kind == 1 && q.nparts > 1) sp += q.nparts;
+      }
+    }
+  }
+  lds_barrier();
   if (pf_static) {
     for (int i = threadIdx.x; i < npf; i += blockDim.x) a.pf_order[pf_start[pf_slot_of[i]] + pf_rank[i]] = i;
     for (int i = threadIdx.x; i <= a.prefill_slots; i += blockDim.x) a.pf_slot_start[i] = pf_start[i];
