@@ -234,6 +234,42 @@ def test_bad_metadata_sets_error_and_nan_rows(dtype, Hq, Hkv, D):
     assert np.array_equal(out[:5], good[:5])
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 128), (32, 8, 128), (16, 4, 64)])
+def test_prefill_bad_block_id_poisons_its_items(Hq, Hkv, D):
+    # a block id outside the pool in a prefill request's table is reported,
+    # replaced by block 0, and turns exactly the rows of the prefill items
+    # that read that block into NaN; other items and requests are unchanged
+    import paged_kv_cache_61_amd as pkv
+    G = Hq // Hkv
+    tile_rows = 256 // G
+    c, ql = 100, 3 * tile_rows + 5
+    reqs = [(40, 1), (c, ql), (300, 1), (7, 20)]
+    wl = workloads.build(workloads.small_spec(f"prefill-bad-{Hq}-{D}", 29, "bf16", Hq, Hkv, D, reqs))
+    s = upload(wl)
+    run_write(s)
+    good = out_f64(run_attention(s))
+    hdr = s.workspace[:1024].cpu().numpy().view(np.int32)
+    assert hdr[6] == 1, "the static item lists are in use"
+    qs = int(wl.query_start_loc[1])
+    for kb in (2, (c + tile_rows + 10) // 16):   # in the cached prefix; inside the chunk's second tile
+        print(f"[case] prefill bad block id G={G} D={D} block {kb}", flush=True)
+        s2 = upload(wl)
+        run_write(s2)
+        bt = s2.block_table.clone()
+        bt[1, kb] = wl.num_blocks + 5
+        s2.block_table = bt
+        out = out_f64(run_attention(s2))
+        assert device_error(s2) & pkv.DEVERR_BLOCK_ID
+        nan_rows = np.zeros(wl.num_tokens, dtype=bool)
+        for row0 in range(0, ql, tile_rows):
+            rows = min(tile_rows, ql - row0)
+            if 16 * kb < c + row0 + rows:   # the item reads block kb
+                nan_rows[qs + row0:qs + row0 + rows] = True
+        assert nan_rows.any() and not nan_rows.all()
+        assert np.isnan(out[nan_rows]).all()
+        assert np.array_equal(out[~nan_rows], good[~nan_rows])
+
+
 def test_write_skips_padding_and_bad_slots():
     import paged_kv_cache_61_amd as pkv
     wl = workloads.build(workloads.small_spec("w", 26, "bf16", 8, 2, 128, [(5, 6), (0, 3)]))
