@@ -17,9 +17,9 @@
 // The partition count depends only on the row's own length, so a request's
 // result is the same whatever else is in the batch.
 //
-// One workgroup of 1024 threads.  Requests are taken 8192 at a time; thread t
-// owns a contiguous run of up to 8 of them, loads all their metadata at once
-// and keeps it in registers, so a step of up to 8192 requests costs one
+// One workgroup of 1024 threads.  Requests are taken 4096 at a time; thread t
+// owns a contiguous run of up to 4 of them, loads all their metadata at once
+// and keeps it in registers, so a step of up to 4096 requests costs one
 // round trip to memory and one block-wide scan (DPP inside each wave, one
 // barrier across waves) to place every request's items in request order.
 // The longest-first lists are counting sorts: a histogram in LDS, a scan of
@@ -39,7 +39,7 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / kWave;
-constexpr int kReqPerThread = 8;                           // requests a thread owns per chunk
+constexpr int kReqPerThread = 4;                           // requests a thread owns per chunk
 constexpr int kChunkReqs = kPlanThreads * kReqPerThread;   // requests per chunk
 
 struct Counts {
@@ -291,16 +291,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     const int per = (nc + kPlanThreads - 1) / kPlanThreads;
     rbeg = c0 + (int)threadIdx.x * per;
     kown = max(0, min(per, c0 + nc - rbeg));
-    // Every load is issued before any is used (one round trip); indices are
-    // clamped into the arrays, and requests past this thread's run are
-    // classified as empty.
+    // Every load is issued before any is used (one round trip); a thread
+    // loads only its own requests (rbeg + kown <= nreq), and requests past
+    // its run are classified as empty.
     int qs[kReqPerThread + 1], L[kReqPerThread], c[kReqPerThread];
 #pragma unroll
-    for (int k = 0; k <= kReqPerThread; ++k) qs[k] = a.qsl[min(rbeg + k, nreq)];
+    for (int k = 0; k <= kReqPerThread; ++k) qs[k] = k <= kown && kown > 0 ? a.qsl[rbeg + k] : 0;
 #pragma unroll
     for (int k = 0; k < kReqPerThread; ++k) {
-      L[k] = a.seq_lens[min(rbeg + k, nreq - 1)];
-      c[k] = a.nct[min(rbeg + k, nreq - 1)];
+      L[k] = k < kown ? a.seq_lens[rbeg + k] : 0;
+      c[k] = k < kown ? a.nct[rbeg + k] : 0;
     }
 #pragma unroll
     for (int k = 0; k < kReqPerThread; ++k)
