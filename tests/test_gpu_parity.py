@@ -107,6 +107,35 @@ def test_workload4_mixed_step_every_row():
     assert_close(out_f64(s.out), ref, wl.dtype, what + " (every row)")
 
 
+@pytest.mark.timeout(600)
+def test_plan_more_requests_than_one_chunk():
+    """A step of 4500 requests (the planner takes 4096 per chunk): decodes of
+    1 to 160 tokens, some of 1025 to 1300 (two split-KV partitions), and
+    prefill chunks at both ends and across the chunk boundary; every row
+    against the oracle, the static prefill lists checked as a permutation."""
+    g = np.random.default_rng(4500)
+    reqs = []
+    for i in range(4500):
+        if i in (0, 4095, 4096, 4499):
+            reqs.append((int(g.integers(0, 300)), int(g.integers(2, 90))))
+        elif i % 37 == 0:
+            reqs.append((int(g.integers(1024, 1300)), 1))
+        else:
+            reqs.append((int(g.integers(0, 160)), 1))
+    # 8 kv heads: 32 prefill workgroups per head, so the static lists are built
+    wl = workloads.build(workloads.small_spec("plan-4500", 4500, "bf16", 16, 8, 64, reqs))
+    s, _ = _full_step(wl, "4500 requests over two planner chunks")
+    ws = s.workspace.cpu().numpy()
+    hdr = ws[:1024].view(np.int32)
+    assert hdr[0] == 0 and hdr[6] == 1
+    n_pf = int(hdr[2])
+    tile_rows = 256 // 2
+    assert n_pf == sum((ql + tile_rows - 1) // tile_rows for _, ql in reqs if ql > 1)
+    off = _workspace_offsets(wl.num_reqs, wl.num_tokens, wl.max_seq_len, tile_rows)
+    order = ws[off["pf_order"]:off["pf_order"] + 4 * n_pf].view(np.int32)
+    assert sorted(order.tolist()) == list(range(n_pf))
+
+
 # ---------------------------------------------------------------------------
 # invariants on the GPU
 
