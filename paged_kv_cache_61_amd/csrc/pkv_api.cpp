@@ -250,6 +250,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   const int64_t pf_per_head =
       std::max<int64_t>(1, std::min<int64_t>(ws.cap_prefill_items, (int64_t)cus / num_kv_heads));
   pp.prefill_slots = (int32_t)pf_per_head;
+  pp.reduce_short_parts = pkv::reduce_short_parts(head_dim);
   pp.hdr = hdr;
   pp.row_items = (int4*)(wsb + ws.row_items);
   pp.row_items_tail = (int4*)(wsb + ws.row_items_tail);
@@ -329,6 +330,7 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     rd.part_o = rp.part_o;
     rd.part_ml = rp.part_ml;
     rd.num_q_heads = num_q_heads;
+    rd.cap_reduce = ws.cap_reduce;
     const int64_t bound = (ws.cap_reduce * num_q_heads + 3) / 4;
     const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 8);
     if (pkv::launch_reduce(rd, dtype, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "reduce launch failed");

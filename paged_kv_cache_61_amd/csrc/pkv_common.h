@@ -29,6 +29,7 @@ enum HdrWord {
   kHdrSlots = 4,
   kHdrRowHead = 5,      // row items in the first region (the rest are in the tail region)
   kHdrPrefillStatic = 6,  // 1: prefill items come from per-slot lists (pf_order), 0: from the queues
+  kHdrReduceShort = 7,  // reduce items of short rows, listed first (the rest fill the list from its end)
   kHdrPrefillQueue = 16,  // one prefill work-queue counter per kv head (zeroed by the plan kernel)
 };
 constexpr int kMaxKvHeads = 240;  // kv heads with a prefill queue counter in the header
@@ -36,6 +37,11 @@ constexpr int kPfMaxSlots = 64;   // static prefill assignment: at most this man
 constexpr int kPfMaxStatic = 256; // ... and at most this many prefill items
 constexpr size_t kHdrBytes = 1024;
 static_assert((kHdrPrefillQueue + kMaxKvHeads) * 4 <= kHdrBytes, "header too small");
+
+// Reduce item (int4): x = query row, y = request, z = partitions, w = first
+// partial slot.  Rows of at most PlanParams::reduce_short_parts partitions
+// are listed from the front of the list, longer rows from its end (position
+// cap - 1 - i), so the merge can batch the short ones.
 
 // Row item (int4): x = query row, y = request, z = partition (kWholeRow: all
 // visible keys, kNanRow: metadata was bad, write NaN), w = first partial slot

@@ -26,6 +26,7 @@ struct PlanParams {
   int32_t mfma_prefill;      // query_len > 1 requests go to the prefill kernel
   int32_t prefill_tile_rows; // query rows per prefill tile
   int32_t prefill_slots;     // prefill workgroups per kv head (the prefill grid / num_kv_heads)
+  int32_t reduce_short_parts;  // split rows of at most this many partitions are "short" reduce items
   int32_t* hdr;
   int4* row_items;
   int4* row_items_tail;
@@ -55,11 +56,12 @@ struct RowParams {
 
 struct ReduceParams {
   void* out;
-  const int4* items;
+  const int4* items;       // short rows from the front, long rows from position cap_reduce - 1 down
   const int32_t* hdr;
   const float* part_o;
   const float2* part_ml;
   int32_t num_q_heads;
+  int64_t cap_reduce;
 };
 
 struct PrefillParams {
@@ -118,6 +120,9 @@ int launch_rows(const RowParams& p, int32_t dtype, int32_t head_dim, int64_t bou
                 hipStream_t stream);
 int launch_reduce(const ReduceParams& p, int32_t dtype, int32_t head_dim, int64_t grid,
                   hipStream_t stream);
+// Partitions of the longest row the merge takes as a "short" row (four query
+// heads per wave and pass).
+int reduce_short_parts(int32_t head_dim);
 int prefill_tile_rows(int32_t group);
 int launch_prefill(const PrefillParams& p, int32_t head_dim, int64_t grid, hipStream_t stream);
 

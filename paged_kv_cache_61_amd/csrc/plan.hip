@@ -43,7 +43,7 @@ constexpr int kReqPerThread = 4;                           // requests a thread 
 constexpr int kChunkReqs = kPlanThreads * kReqPerThread;   // requests per chunk
 
 struct Counts {
-  int rows, prefill, reduce, slots, tail;
+  int rows, prefill, reduce, slots, tail, reduce_long;
 };
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
@@ -138,16 +138,19 @@ __device__ ReqInfo classify(const PlanParams& a, int r, int qs, int qe, int L, i
 }
 
 // Items a request contributes: full partitions or query rows (rows), its
-// partial last partition (tail), prefill tiles, its reduce item and the
-// partial slots of its partitions.
+// partial last partition (tail), prefill tiles, its reduce item (a short or
+// a long row's) and the partial slots of its partitions.
 __device__ Counts count_items(const PlanParams& a, const ReqInfo& q) {
-  Counts m{0, 0, 0, 0, 0};
+  Counts m{0, 0, 0, 0, 0, 0};
   if (q.kind == 1) {
     const bool partial_last = q.L % kSplitTokens != 0;
     m.rows = q.nparts - (partial_last ? 1 : 0);
     m.tail = partial_last ? 1 : 0;
     if (q.nparts > 1) {
-      m.reduce = 1;
+      if (q.nparts <= a.reduce_short_parts)
+        m.reduce = 1;
+      else
+        m.reduce_long = 1;
       m.slots = q.nparts;
     }
   } else if (q.kind == 2) {
@@ -310,12 +313,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   // Pass 1: check requests, place decode rows (full partitions), reduce
   // items and per-query rows, count everything, and histogram the items that
   // are sorted.
-  Counts base{0, 0, 0, 0, 0};
+  Counts base{0, 0, 0, 0, 0, 0};
   int slot_first = 0;   // (single chunk) partial slot of this thread's first split row
   for (int ch = 0; ch < nchunks; ++ch) {
     if (ch > 0) lds_barrier();   // scan_lds[0] is read by every thread before it is rewritten
     load_chunk(ch * kChunkReqs);
-    int own[5] = {0, 0, 0, 0, 0};
+    int own[6] = {0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < kReqPerThread; ++k) {
       const Counts m = count_items(a, qi[k]);
@@ -324,10 +327,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
       own[2] += m.reduce;
       own[3] += m.slots;
       own[4] += m.tail;
+      own[5] += m.reduce_long;
     }
-    int ex[5], tot[5];
-    block_scan<5>(own, ex, tot, scan_lds[0]);
+    int ex[6], tot[6];
+    block_scan<6>(own, ex, tot, scan_lds[0]);
     int rowpos = base.rows + ex[0], redpos = base.reduce + ex[2], slotpos = base.slots + ex[3];
+    int redpos_l = base.reduce_long + ex[5];   // long rows: from the end of the list
     slot_first = slotpos;
     const bool sorted_fit = base.tail + tot[4] <= a.cap_row_items && base.prefill + tot[1] <= a.cap_prefill_items;
     int err = 0;
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
       const Counts m = count_items(a, q);
       err |= q.err;
       const bool fits = sorted_fit && rowpos + m.rows <= a.cap_row_items && redpos + m.reduce <= a.cap_reduce &&
-                        slotpos + m.slots <= a.cap_slots;
+                        redpos_l + m.reduce_long <= a.cap_reduce && slotpos + m.slots <= a.cap_slots;
       if (!fits) {
         err |= PKV_DEVERR_CAPACITY;
       } else if (q.kind == 1) {
@@ -349,6 +354,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
           a.row_items[rowpos + p] = make_int4(q.qs, r, q.nparts == 1 ? kWholeRow : p, q.nparts == 1 ? -1 : slotpos);
         if (m.tail) atomicAdd(&tail_off[(q.L % kSplitTokens + kBlock - 1) / kBlock - 1], 1);
         if (m.reduce) a.reduce_items[redpos] = make_int4(q.qs, r, q.nparts, slotpos);
+        if (m.reduce_long) a.reduce_items[a.cap_reduce - 1 - redpos_l] = make_int4(q.qs, r, q.nparts, slotpos);
       } else if (q.kind == 2) {
         pf_req[k] = true;
       } else if (q.kind == 3 || q.kind == 4) {
@@ -357,6 +363,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
       }
       rowpos += m.rows;
       redpos += m.reduce;
+      redpos_l += m.reduce_long;
       slotpos += m.slots;
     }
     // A prefill request's tiles are histogrammed by the whole wave, one tile
@@ -379,9 +386,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     base.reduce += tot[2];
     base.slots += tot[3];
     base.tail += tot[4];
+    base.reduce_long += tot[5];
   }
   const bool over = base.rows > a.cap_row_items || base.tail > a.cap_row_items ||
-                    base.prefill > a.cap_prefill_items || base.reduce > a.cap_reduce ||
+                    base.prefill > a.cap_prefill_items || base.reduce + base.reduce_long > a.cap_reduce ||
                     base.slots > a.cap_slots;
   // Bucket offsets, longest bucket first: thread t owns the 4 buckets at
   // descending positions 4t .. 4t+3 of the prefill list and writes the tile
@@ -485,7 +493,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     a.hdr[kHdrRowHead] = over ? 0 : base.rows;
     a.hdr[kHdrPrefillItems] = over ? 0 : base.prefill;
     a.hdr[kHdrPrefillStatic] = pf_static ? 1 : 0;
-    a.hdr[kHdrReduceItems] = over ? 0 : base.reduce;
+    a.hdr[kHdrReduceItems] = over ? 0 : base.reduce + base.reduce_long;
+    a.hdr[kHdrReduceShort] = over ? 0 : base.reduce;
     a.hdr[kHdrSlots] = over ? 0 : base.slots;
   }
 }
