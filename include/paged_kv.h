@@ -34,13 +34,14 @@
  *    takes at most 240 kv heads.
  *  - stream is a hipStream_t (NULL = the legacy default stream).  Work is only
  *    enqueued: the calls return before the GPU finishes, never synchronise,
- *    never allocate and never free.  The caller keeps every buffer alive until
+ *    never allocate or free device memory.  The caller keeps every buffer alive until
  *    the stream reaches that point.
  *  - The calls may be made from several host threads at once.  The only
  *    process-wide state is a per-kernel cache of the occupancy the HIP runtime
- *    reports (filled on first use with the same value by every caller) and the
- *    per-thread error detail string.  Two calls that share a workspace must be
- *    ordered on one stream.
+ *    reports (filled on first use with the same value by every caller), one
+ *    library stream per device (created on first use, default priority; see
+ *    paged_attention_int8) and the per-thread error detail string.  Two calls
+ *    that share a workspace must be ordered on one stream.
  *  - Errors are returned as a pkv_status, never thrown.  Argument errors are
  *    detected on the host before anything is enqueued.  Bad *contents* of
  *    device metadata (inconsistent lengths, out-of-range block ids or slots)
@@ -301,7 +302,12 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  *   bf16 q all G query heads of a kv head share 16x16 matrix-core tiles over
  *   the exact integer codes, the scales entering in float32 (p * v_scale is
  *   rounded to bf16); with fp32 q a VALU kernel works in float32.
- *   phase_events as for paged_attention_profiled, or NULL.
+ *   phase_events as for paged_attention_profiled, or NULL.  With NULL the
+ *   prefill kernel of a step that has prefill chunks runs on a library stream
+ *   beside `stream` (which waits for it through events created and released
+ *   by the call, so `stream` still orders everything): the row kernels take
+ *   the CUs that the prefill's last workgroups leave free.  With phase events
+ *   every kernel runs on `stream`, one after the other.
  * Other arguments, the workspace and the error conventions are those of
  * paged_kv_write / paged_attention.
  */
