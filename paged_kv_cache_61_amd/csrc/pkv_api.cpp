@@ -400,7 +400,8 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     rd.part_ml = rp.part_ml;
     rd.num_q_heads = num_q_heads;
     rd.cap_reduce = ws.cap_reduce;
-    const int64_t bound = (ws.cap_reduce * num_q_heads + 3) / 4;
+    // (a workgroup per (long row, head) at most; short rows need a quarter of that)
+    const int64_t bound = ws.cap_reduce * num_q_heads;
     const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 8);
     if (pkv::launch_reduce(rd, dtype, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "reduce launch failed");
   }

@@ -30,6 +30,7 @@ enum HdrWord {
   kHdrRowHead = 5,      // row items in the first region (the rest are in the tail region)
   kHdrPrefillStatic = 6,  // 1: prefill items come from per-slot lists (pf_order), 0: from the queues
   kHdrReduceShort = 7,  // reduce items of short rows, listed first (the rest fill the list from its end)
+  kHdrReduceSplit = 8,  // of the rest, rows of more than 2 * PlanParams::reduce_short_parts partitions
   kHdrPrefillQueue = 16,  // one prefill work-queue counter per kv head (zeroed by the plan kernel)
 };
 constexpr int kMaxKvHeads = 240;  // kv heads with a prefill queue counter in the header

@@ -273,7 +273,7 @@ PKV_DEV void assign_first_fit(const int* tiles, int n_in, int W_in, int* slot_of
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
-  __shared__ int err_acc;
+  __shared__ int err_acc, split_rows;
   __shared__ int scan_lds[3][kPlanWaves][8];
   __shared__ int pf_tiles[kPfMaxStatic], pf_slot_of[kPfMaxStatic], pf_rank[kPfMaxStatic];
   __shared__ int pf_start[kPfMaxSlots + 1];
@@ -281,7 +281,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   __shared__ int tail_off[kTailBuckets];
   for (int i = threadIdx.x; i < kPfBuckets; i += kPlanThreads) pf_off[i] = 0;
   if (threadIdx.x < kTailBuckets) tail_off[threadIdx.x] = 0;
-  if (threadIdx.x == 0) err_acc = 0;
+  if (threadIdx.x == 0) {
+    err_acc = 0;
+    split_rows = 0;
+  }
   lds_barrier();
 
   const int nreq = a.num_reqs;
@@ -354,7 +357,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
           a.row_items[rowpos + p] = make_int4(q.qs, r, q.nparts == 1 ? kWholeRow : p, q.nparts == 1 ? -1 : slotpos);
         if (m.tail) atomicAdd(&tail_off[(q.L % kSplitTokens + kBlock - 1) / kBlock - 1], 1);
         if (m.reduce) a.reduce_items[redpos] = make_int4(q.qs, r, q.nparts, slotpos);
-        if (m.reduce_long) a.reduce_items[a.cap_reduce - 1 - redpos_l] = make_int4(q.qs, r, q.nparts, slotpos);
+        if (m.reduce_long) {
+          a.reduce_items[a.cap_reduce - 1 - redpos_l] = make_int4(q.qs, r, q.nparts, slotpos);
+          if (q.nparts > 2 * a.reduce_short_parts) atomicAdd(&split_rows, 1);
+        }
       } else if (q.kind == 2) {
         pf_req[k] = true;
       } else if (q.kind == 3 || q.kind == 4) {
@@ -495,6 +501,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     a.hdr[kHdrPrefillStatic] = pf_static ? 1 : 0;
     a.hdr[kHdrReduceItems] = over ? 0 : base.reduce + base.reduce_long;
     a.hdr[kHdrReduceShort] = over ? 0 : base.reduce;
+    a.hdr[kHdrReduceSplit] = over ? 0 : split_rows;
     a.hdr[kHdrSlots] = over ? 0 : base.slots;
   }
 }

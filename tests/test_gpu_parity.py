@@ -107,6 +107,19 @@ def test_workload4_mixed_step_every_row():
     assert_close(out_f64(s.out), ref, wl.dtype, what + " (every row)")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_split_kv_merge_classes(dtype, D):
+    # decode rows of 1 to 33 split-KV partitions in one step: the merge takes
+    # rows of up to 2 * (256 / D) partitions four heads per wave, rows of up
+    # to 4 * (256 / D) one head per wave, and longer ones one head per
+    # workgroup (each wave a quarter of the partitions); every row against
+    # the oracle
+    ctx = [1000, 2000, 2500, 4500, 8000, 8500, 16500, 33000]
+    reqs = [(c, 1) for c in ctx] + [(300, 40)]
+    wl = workloads.build(workloads.small_spec(f"merge-classes-{dtype}-{D}", 77 + D, dtype, 8, 2, D, reqs))
+    _full_step(wl, f"split-KV merge classes {dtype} D={D}")
+
+
 @pytest.mark.timeout(600)
 def test_plan_more_requests_than_one_chunk():
     """A step of 4500 requests (the planner takes 4096 per chunk): decodes of
