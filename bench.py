@@ -53,6 +53,8 @@ def parse():
                     help="INT8 KV cache (paged_kv_write_int8 + paged_attention_int8)")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="FP8 (E4M3) KV cache (paged_kv_write_fp8 + paged_attention_fp8)")
+    ap.add_argument("--no-staging", action="store_true",
+                    help="8-bit caches: no staging area (the prefill dequantises every tile it streams)")
     ap.add_argument("--rope", action="store_true",
                     help="write the step's tokens with paged_kv_write_rope (RoPE on K, and on q in place)")
     ap.add_argument("--head-dim", type=int, choices=(64, 128), default=None,
@@ -403,9 +405,16 @@ def main():
     slot_mapping = torch.from_numpy(wl.slot_mapping).to(dev)
     bt, sl, qsl, nct = (i32(wl.block_table), i32(wl.seq_lens), i32(wl.query_start_loc),
                         i32(wl.num_computed_tokens))
-    ws = torch.empty(max(256, pkv.paged_attention_workspace_size(
-        wl.num_reqs, wl.num_tokens, wl.num_q_heads, wl.head_dim, wl.max_query_len,
-        wl.max_seq_len)), dtype=torch.uint8, device=dev)
+    ws_bytes = pkv.paged_attention_workspace_size(wl.num_reqs, wl.num_tokens, wl.num_q_heads, wl.head_dim,
+                                                  wl.max_query_len, wl.max_seq_len)
+    stage_blocks = 0
+    if kv8 and not args.no_staging:
+        # 8-bit cache: room to stage the step's prefill blocks (dequantised once per step)
+        ql = wl.query_lens
+        stage_blocks = int(sum((int(wl.seq_lens[r]) + 15) // 16 for r in np.nonzero(ql > 1)[0]))
+        ws_bytes += pkv.paged_attention_staging_bytes(wl.num_reqs, wl.block_table.shape[1], wl.num_kv_heads,
+                                                      wl.head_dim, stage_blocks)
+    ws = torch.empty(max(256, ws_bytes), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
 
     nph = pkv.NUM_PHASES
@@ -566,6 +575,7 @@ def main():
             "head_dim": wl.head_dim, "block_size": 16, "num_blocks": wl.num_blocks,
             "decode_kv_tokens": acct["decode_kv_tokens"], "max_seq_len": wl.max_seq_len,
             "kv_cache": (f"{kv8} codes + float32 scale per (token, kv head)" if kv8 else wl.dtype),
+            **({"prefill_staging_blocks": stage_blocks} if kv8 else {}),
         },
         "roofline": roof_pf if dominant_is_pf else roof_rows,
         "rooflines": {"decode_rows": roof_rows, **({"prefill": roof_pf} if roof_pf else {})},

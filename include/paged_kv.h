@@ -302,6 +302,14 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  *   bf16 q all G query heads of a kv head share 16x16 matrix-core tiles over
  *   the exact integer codes, the scales entering in float32 (p * v_scale is
  *   rounded to bf16); with fp32 q a VALU kernel works in float32.
+ *   workspace_bytes beyond paged_attention_workspace_size() is a staging
+ *   area: when the step's prefill chunks (bf16 q, head_dim 128) read at most
+ *   as many cache blocks as fit there (paged_attention_staging_bytes), each
+ *   of those blocks is dequantised once into a bf16 block of the staging area
+ *   (code * scale in float32, rounded to bf16: the values the prefill kernel
+ *   forms in LDS, so results are the same bit for bit) and the prefill reads
+ *   the staged blocks instead of dequantising every tile it streams.  With no
+ *   extra workspace, or a step that does not fit, nothing changes.
  *   phase_events as for paged_attention_profiled, or NULL.  With NULL the
  *   prefill kernel of a step that has prefill chunks runs on a library stream
  *   beside `stream` (which waits for it through events created and released
@@ -311,6 +319,16 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  * Other arguments, the workspace and the error conventions are those of
  * paged_kv_write / paged_attention.
  */
+/*
+ * paged_attention_staging_bytes — workspace bytes to add to
+ * paged_attention_workspace_size() so that paged_attention_int8 / _fp8 stage
+ * the prefill of any step whose prefill requests read at most prefill_blocks
+ * cache blocks in all (the sum over the prefill requests of
+ * ceil(seq_len / 16)); num_reqs and max_blocks_per_req as in the call.
+ * Returns 0 for prefill_blocks == 0 or invalid sizes.  Pure host function.
+ */
+size_t paged_attention_staging_bytes(int32_t num_reqs, int32_t max_blocks_per_req, int32_t num_kv_heads,
+                                     int32_t head_dim, int64_t prefill_blocks);
 int paged_kv_write_int8(const void* k, const void* v, const int64_t* slot_mapping, void* kv_cache_layer,
                         float* kv_scales, int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
                         int32_t head_dim, int32_t dtype, int32_t* device_error, void* stream);

@@ -35,7 +35,7 @@ __all__ = [
     "DEVERR_SEQ_LEN", "DEVERR_LIMITS", "DEVERR_QSL", "DEVERR_BLOCK_ID", "DEVERR_SLOT",
     "DEVERR_CAPACITY", "DEVERR_POSITION", "BLOCK_SIZE", "paged_kv_copy_blocks", "paged_kv_write_rope",
     "paged_kv_write_int8", "paged_attention_int8", "paged_kv_write_fp8", "paged_attention_fp8",
-    "BlockManager", "Step", "paged_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "BlockManager", "Step", "paged_attention_noalloc", "NOALLOC_SCRATCH_BYTES", "paged_attention_staging_bytes",
 ]
 
 BLOCK_SIZE = 16
@@ -94,6 +94,8 @@ def load_library() -> ctypes.CDLL:
     lib.paged_attention_noalloc.restype = ctypes.c_int
     lib.paged_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.paged_attention_workspace_size.restype = sz
+    lib.paged_attention_staging_bytes.argtypes = [i32, i32, i32, i32, i64]
+    lib.paged_attention_staging_bytes.restype = sz
     lib.pkv_read_device_error.argtypes = [vp, vp]
     lib.pkv_read_device_error.restype = i32
     lib.pkv_validate_metadata_host.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32]
@@ -224,6 +226,15 @@ def paged_attention_workspace_size(num_reqs: int, num_tokens: int, num_q_heads: 
                                    head_dim: int, max_query_len: int, max_seq_len: int) -> int:
     return int(_lib.paged_attention_workspace_size(num_reqs, num_tokens, num_q_heads, head_dim,
                                                    max_query_len, max_seq_len))
+
+
+def paged_attention_staging_bytes(num_reqs: int, max_blocks_per_req: int, num_kv_heads: int,
+                                  head_dim: int, prefill_blocks: int) -> int:
+    """Extra workspace with which ``paged_attention_int8`` / ``_fp8`` dequantise
+    a step's prefill blocks once (steps whose prefill requests read at most
+    ``prefill_blocks`` cache blocks in all)."""
+    return int(_lib.paged_attention_staging_bytes(num_reqs, max_blocks_per_req, num_kv_heads, head_dim,
+                                                  prefill_blocks))
 
 
 def paged_attention(q: torch.Tensor, kv_cache_layer: torch.Tensor, block_table: torch.Tensor,
@@ -439,7 +450,10 @@ def paged_attention_int8(q: torch.Tensor, kv_cache_layer: torch.Tensor, kv_scale
                          workspace: Optional[torch.Tensor] = None, stream=None,
                          phase_events=None) -> torch.Tensor:
     """``paged_attention`` over an INT8 cache (``kv_cache_layer`` int8 codes,
-    ``kv_scales`` float32 per (token, kv head)); ``q`` / ``out`` bf16 or fp32."""
+    ``kv_scales`` float32 per (token, kv head)); ``q`` / ``out`` bf16 or fp32.
+    A ``workspace`` larger than ``paged_attention_workspace_size`` (by
+    ``paged_attention_staging_bytes``) lets the prefill read blocks
+    dequantised once per step."""
     return _attention_8bit("int8", q, kv_cache_layer, kv_scales, block_table, seq_lens, query_start_loc,
                            num_computed_tokens, scale, max_query_len, max_seq_len, out, workspace, stream,
                            phase_events)
@@ -453,7 +467,8 @@ def paged_attention_fp8(q: torch.Tensor, kv_cache_layer: torch.Tensor, kv_scales
                         phase_events=None) -> torch.Tensor:
     """``paged_attention`` over an FP8 cache (``kv_cache_layer`` E4M3 codes as
     uint8 or float8_e4m3fn, ``kv_scales`` float32 per (token, kv head));
-    ``q`` / ``out`` bf16 or fp32."""
+    ``q`` / ``out`` bf16 or fp32.  Workspace and staging as for
+    ``paged_attention_int8``."""
     return _attention_8bit("fp8", q, kv_cache_layer, kv_scales, block_table, seq_lens, query_start_loc,
                            num_computed_tokens, scale, max_query_len, max_seq_len, out, workspace, stream,
                            phase_events)

@@ -244,6 +244,18 @@ size_t paged_attention_workspace_size(int32_t num_reqs, int64_t num_tokens, int3
                                            max_query_len, max_seq_len, 1);
 }
 
+size_t paged_attention_staging_bytes(int32_t num_reqs, int32_t max_blocks_per_req, int32_t num_kv_heads,
+                                     int32_t head_dim, int64_t prefill_blocks) {
+  if (num_reqs < 0 || max_blocks_per_req < 0 || num_kv_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
+      prefill_blocks < 0)
+    return 0;
+  if (prefill_blocks == 0) return 0;
+  // covers the alignments stage_layout() applies after the workspace's own size
+  return 256 + pkv::align_up(sizeof(int32_t) * (size_t)num_reqs * (size_t)max_blocks_per_req, 256) +
+         pkv::align_up(sizeof(int32_t) * (size_t)prefill_blocks, 256) +
+         (size_t)prefill_blocks * (size_t)pkv::stage_block_bytes(num_kv_heads, head_dim) + 1024;
+}
+
 static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
                           const int32_t* block_table, const int32_t* seq_lens,
                           const int32_t* query_start_loc, const int32_t* num_computed_tokens,
@@ -314,6 +326,17 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
       std::max<int64_t>(1, std::min<int64_t>(ws.cap_prefill_items, (int64_t)cus / num_kv_heads));
   pp.prefill_slots = (int32_t)pf_per_head;
   pp.reduce_short_parts = pkv::reduce_short_parts(head_dim);
+  pp.block_table = block_table;
+  pp.num_blocks = num_blocks;
+  // 8-bit cache, prefill on the matrix cores: workspace past ws.total stages
+  // the step's prefill blocks in bf16 when they fit (see stage.hip).
+  const pkv::StageLayout stl =
+      i8 && pp.mfma_prefill ? pkv::stage_layout(ws.total, workspace_bytes, num_reqs, max_blocks_per_req,
+                                                num_kv_heads, head_dim)
+                            : pkv::StageLayout{};
+  pp.stage_capacity = stl.capacity;
+  pp.stage_bt = stl.capacity > 0 ? (int32_t*)(wsb + stl.bt) : nullptr;
+  pp.stage_src = stl.capacity > 0 ? (int32_t*)(wsb + stl.src) : nullptr;
   pp.hdr = hdr;
   pp.row_items = (int4*)(wsb + ws.row_items);
   pp.row_items_tail = (int4*)(wsb + ws.row_items_tail);
@@ -357,6 +380,32 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.num_blocks = num_blocks;
     fp.max_blocks_per_req = max_blocks_per_req;
     const int64_t grid = pf_per_head * num_kv_heads;
+    if (stl.capacity > 0) {
+      // staged: the blocks dequantised once, then the bf16 kernel over them
+      // (both no-ops unless the plan staged this step)
+      pkv::StageParams sp{};
+      sp.cache = kv_cache_layer;
+      sp.kv_scales = kv_scales;
+      sp.src = pp.stage_src;
+      sp.staged = wsb + stl.blocks;
+      sp.hdr = hdr;
+      sp.capacity = stl.capacity;
+      sp.num_blocks = num_blocks;
+      sp.num_kv_heads = num_kv_heads;
+      sp.head_dim = head_dim;
+      sp.fp8 = fp8 ? 1 : 0;
+      if (pkv::launch_stage(sp, std::min<int64_t>(2 * stl.capacity, (int64_t)cus * 8), ps))
+        return fail(PKV_ERR_LAUNCH, "stage launch failed");
+      pkv::PrefillParams sf = fp;
+      sf.cache = wsb + stl.blocks;
+      sf.kv_scales = nullptr;
+      sf.kv_fp8 = 0;
+      sf.block_table = pp.stage_bt;
+      sf.num_blocks = (int32_t)stl.capacity;
+      sf.staged = 1;
+      if (pkv::launch_prefill(sf, head_dim, grid, ps)) return fail(PKV_ERR_LAUNCH, "prefill launch failed");
+    }
+    fp.staged = 0;
     if (pkv::launch_prefill(fp, head_dim, grid, ps)) return fail(PKV_ERR_LAUNCH, "prefill launch failed");
   }
 

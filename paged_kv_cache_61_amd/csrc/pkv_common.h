@@ -31,6 +31,8 @@ enum HdrWord {
   kHdrPrefillStatic = 6,  // 1: prefill items come from per-slot lists (pf_order), 0: from the queues
   kHdrReduceShort = 7,  // reduce items of short rows, listed first (the rest fill the list from its end)
   kHdrReduceSplit = 8,  // of the rest, rows of more than 2 * PlanParams::reduce_short_parts partitions
+  kHdrPrefillStaged = 9,   // 1: the prefill reads bf16 blocks dequantised once into the staging area
+  kHdrStagedBlocks = 10,   // blocks in the staging area this step (0 when not staged)
   kHdrPrefillQueue = 16,  // one prefill work-queue counter per kv head (zeroed by the plan kernel)
 };
 constexpr int kMaxKvHeads = 240;  // kv heads with a prefill queue counter in the header
@@ -61,6 +63,36 @@ struct WsLayout {
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Staging area of an 8-bit cache's prefill: the workspace bytes past
+// WsLayout::total.  A bf16 block table of the same shape as the step's
+// ([num_reqs][max_blocks_per_req] int32), the source block of each staged
+// block (int32 [capacity]), then the staged blocks, laid out as a bf16 cache
+// of `capacity` blocks ([2][capacity][16][num_kv_heads][head_dim]).
+struct StageLayout {
+  size_t bt, src, blocks;   // byte offsets from the workspace start
+  int64_t capacity;         // staged blocks that fit (0: no staging)
+};
+inline int64_t stage_block_bytes(int64_t num_kv_heads, int64_t head_dim) {
+  return 2 * 16 * num_kv_heads * head_dim * 2;   // K and V halves of one block, bf16
+}
+inline StageLayout stage_layout(size_t ws_total, size_t workspace_bytes, int64_t num_reqs,
+                                int64_t max_blocks_per_req, int64_t num_kv_heads, int64_t head_dim) {
+  StageLayout s{};
+  s.bt = align_up(ws_total, 256);
+  s.src = align_up(s.bt + sizeof(int32_t) * (size_t)(num_reqs * max_blocks_per_req), 256);
+  if (workspace_bytes <= s.src + 512) return s;
+  const int64_t per = stage_block_bytes(num_kv_heads, head_dim) + (int64_t)sizeof(int32_t);
+  int64_t cap = (int64_t)(workspace_bytes - s.src - 512) / per;
+  if (cap > ((int64_t)1 << 30)) cap = (int64_t)1 << 30;
+  s.blocks = align_up(s.src + sizeof(int32_t) * (size_t)cap, 256);
+  while (cap > 0 && s.blocks + (size_t)cap * (size_t)stage_block_bytes(num_kv_heads, head_dim) > workspace_bytes) {
+    --cap;
+    s.blocks = align_up(s.src + sizeof(int32_t) * (size_t)cap, 256);
+  }
+  s.capacity = cap;
+  return s;
+}
 
 // Capacities are upper bounds that hold for any metadata that passes the
 // device checks (query_len <= max_query_len, seq_len <= max_seq_len).

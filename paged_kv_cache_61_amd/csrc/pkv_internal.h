@@ -27,6 +27,15 @@ struct PlanParams {
   int32_t prefill_tile_rows; // query rows per prefill tile
   int32_t prefill_slots;     // prefill workgroups per kv head (the prefill grid / num_kv_heads)
   int32_t reduce_short_parts;  // split rows of at most this many partitions are "short" reduce items
+  // 8-bit cache, prefill on the matrix cores: staging of the prefill blocks
+  // (stage_capacity 0: none).  stage_bt gets block_table's shape; the rows of
+  // prefill requests are written (kb -> staged block, -1 for an id outside
+  // the pool), stage_src[staged block] = the cache block it copies.
+  int64_t stage_capacity;
+  int32_t* stage_bt;
+  int32_t* stage_src;
+  const int32_t* block_table;
+  int32_t num_blocks;
   int32_t* hdr;
   int4* row_items;
   int4* row_items_tail;
@@ -76,6 +85,7 @@ struct PrefillParams {
   const int32_t* pf_slot_start;
   const float* kv_scales;  // 8-bit cache: [2][num_blocks][num_kv_heads][16] scales; else nullptr
   int32_t kv_fp8;          // 8-bit cache codes: 0 INT8, 1 OCP E4M3
+  int32_t staged;          // runs only if hdr[kHdrPrefillStaged] equals this (1: over the staging area)
   float scale_log2;
   int32_t num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_req;
 };
@@ -112,6 +122,18 @@ int launch_kv_copy_blocks(void* cache, const int32_t* copies, int32_t num_copies
                           int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, int32_t* device_error,
                           hipStream_t stream);
 int launch_plan(const PlanParams& p, hipStream_t stream);
+// Dequantise the step's prefill blocks into the staging area (a no-op unless
+// the plan staged them).
+struct StageParams {
+  const void* cache;        // 8-bit cache layer: K codes then V codes
+  const float* kv_scales;   // [2][num_blocks][num_kv_heads][16]
+  const int32_t* src;       // stage_src
+  void* staged;             // bf16 [2][capacity][16][num_kv_heads][head_dim]
+  const int32_t* hdr;
+  int64_t capacity;
+  int32_t num_blocks, num_kv_heads, head_dim, fp8;
+};
+int launch_stage(const StageParams& p, int64_t grid, hipStream_t stream);
 // bound_waves: upper bound on row work items (one wave each); cus: compute units.
 // Query heads of a group that one row wave handles (wider groups run as
 // head_groups waves over the same blocks).

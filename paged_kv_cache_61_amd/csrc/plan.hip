@@ -43,7 +43,7 @@ constexpr int kReqPerThread = 4;                           // requests a thread 
 constexpr int kChunkReqs = kPlanThreads * kReqPerThread;   // requests per chunk
 
 struct Counts {
-  int rows, prefill, reduce, slots, tail, reduce_long;
+  int rows, prefill, reduce, slots, tail, reduce_long, stage;
 };
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
@@ -141,7 +141,7 @@ __device__ ReqInfo classify(const PlanParams& a, int r, int qs, int qe, int L, i
 // partial last partition (tail), prefill tiles, its reduce item (a short or
 // a long row's) and the partial slots of its partitions.
 __device__ Counts count_items(const PlanParams& a, const ReqInfo& q) {
-  Counts m{0, 0, 0, 0, 0, 0};
+  Counts m{0, 0, 0, 0, 0, 0, 0};
   if (q.kind == 1) {
     const bool partial_last = q.L % kSplitTokens != 0;
     m.rows = q.nparts - (partial_last ? 1 : 0);
@@ -155,6 +155,7 @@ __device__ Counts count_items(const PlanParams& a, const ReqInfo& q) {
     }
   } else if (q.kind == 2) {
     m.prefill = (q.ql + a.prefill_tile_rows - 1) / a.prefill_tile_rows;
+    if (a.stage_capacity > 0) m.stage = (q.L + kBlock - 1) / kBlock;   // blocks its tiles read
   } else if (q.kind == 3 || q.kind == 4) {
     m.rows = q.ql;
   }
@@ -316,12 +317,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   // Pass 1: check requests, place decode rows (full partitions), reduce
   // items and per-query rows, count everything, and histogram the items that
   // are sorted.
-  Counts base{0, 0, 0, 0, 0, 0};
+  Counts base{0, 0, 0, 0, 0, 0, 0};
   int slot_first = 0;   // (single chunk) partial slot of this thread's first split row
+  int stage_first = 0;  // (single chunk) first staged block of this thread's first prefill request
   for (int ch = 0; ch < nchunks; ++ch) {
     if (ch > 0) lds_barrier();   // scan_lds[0] is read by every thread before it is rewritten
     load_chunk(ch * kChunkReqs);
-    int own[6] = {0, 0, 0, 0, 0, 0};
+    int own[7] = {0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < kReqPerThread; ++k) {
       const Counts m = count_items(a, qi[k]);
@@ -331,9 +333,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
       own[3] += m.slots;
       own[4] += m.tail;
       own[5] += m.reduce_long;
+      own[6] += m.stage;
     }
-    int ex[6], tot[6];
-    block_scan<6>(own, ex, tot, scan_lds[0]);
+    int ex[7], tot[7];
+    block_scan<7>(own, ex, tot, scan_lds[0]);
+    stage_first = base.stage + ex[6];
     int rowpos = base.rows + ex[0], redpos = base.reduce + ex[2], slotpos = base.slots + ex[3];
     int redpos_l = base.reduce_long + ex[5];   // long rows: from the end of the list
     slot_first = slotpos;
@@ -393,10 +397,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     base.slots += tot[3];
     base.tail += tot[4];
     base.reduce_long += tot[5];
+    base.stage += tot[6];
   }
   const bool over = base.rows > a.cap_row_items || base.tail > a.cap_row_items ||
                     base.prefill > a.cap_prefill_items || base.reduce + base.reduce_long > a.cap_reduce ||
                     base.slots > a.cap_slots;
+  // 8-bit cache: the prefill reads its blocks from the staging area when they
+  // all fit there (each is dequantised once, instead of once per prefill tile
+  // that reads it)
+  const bool staged = !over && base.stage > 0 && base.stage <= a.stage_capacity;
   // Bucket offsets, longest bucket first: thread t owns the 4 buckets at
   // descending positions 4t .. 4t+3 of the prefill list and writes the tile
   // count of each of their positions below kPfMaxStatic (the first-fit
@@ -446,18 +455,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
   // chunk every thread still holds its requests and the partial slot of its
   // first split row; otherwise each chunk is loaded and scanned again.
   if (!over && sorted_work) {
-    int slot_base = 0;
+    int slot_base = 0, stage_base = 0;
     for (int ch = 0; ch < nchunks; ++ch) {
-      int sp = slot_first;
+      int sp = slot_first, stp = stage_first;
       if (nchunks > 1) {
         if (ch > 0) lds_barrier();   // scan_lds[2] is read by every thread before it is rewritten
         load_chunk(ch * kChunkReqs);
-        int own[1] = {0}, ex[1], tot[1];
+        int own[2] = {0, 0}, ex[2], tot[2];
 #pragma unroll
-        for (int k = 0; k < kReqPerThread; ++k) own[0] += count_items(a, qi[k]).slots;
-        block_scan<1>(own, ex, tot, scan_lds[2]);
+        for (int k = 0; k < kReqPerThread; ++k) {
+          const Counts m = count_items(a, qi[k]);
+          own[0] += m.slots;
+          own[1] += m.stage;
+        }
+        block_scan<2>(own, ex, tot, scan_lds[2]);
         sp = slot_base + ex[0];
         slot_base += tot[0];
+        stp = stage_base + ex[1];
+        stage_base += tot[1];
       }
       const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
@@ -481,8 +496,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
             const int pos = atomicAdd(&pf_off[pf_bucket(c, row0, rows)], 1);
             a.prefill_items[pos] = make_int4(rq, qs + row0, rows, c - qs);
           }
+          if (staged) {   // its staging: block kb -> staged block sb0 + kb, sources checked
+            const int sb0 = __builtin_amdgcn_readlane(stp, src);
+            const int nb = (__builtin_amdgcn_readlane(q.L, src) + kBlock - 1) / kBlock;
+            const size_t row = (size_t)rq * a.max_blocks_per_req;
+            for (int kb = lane; kb < nb; kb += kWave) {
+              const int id = a.block_table[row + kb];
+              const bool ok = id >= 0 && id < a.num_blocks;
+              a.stage_src[sb0 + kb] = ok ? id : 0;
+              a.stage_bt[row + kb] = ok ? sb0 + kb : -1;
+            }
+          }
         }
         if (q.kind == 1 && q.nparts > 1) sp += q.nparts;
+        if (q.kind == 2) stp += count_items(a, q).stage;
       }
     }
   }
@@ -502,6 +529,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams a) {
     a.hdr[kHdrReduceItems] = over ? 0 : base.reduce + base.reduce_long;
     a.hdr[kHdrReduceShort] = over ? 0 : base.reduce;
     a.hdr[kHdrReduceSplit] = over ? 0 : split_rows;
+    a.hdr[kHdrPrefillStaged] = staged ? 1 : 0;
+    a.hdr[kHdrStagedBlocks] = staged ? base.stage : 0;
     a.hdr[kHdrSlots] = over ? 0 : base.slots;
   }
 }

@@ -276,6 +276,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(
   // order, each as soon as it is free, so the longest tiles are spread first
   // and the work per workgroup evens out.  The next index is fetched while
   // the current tile runs.
+  // An 8-bit cache's step launches this kernel twice, over the staging area
+  // (bf16, staged = 1) and over the cache (staged = 0); the plan's decision
+  // picks the one that runs.
+  if (a.hdr[kHdrPrefillStaged] != a.staged) return;
   const int n_entries = a.hdr[kHdrPrefillItems];
   const int g = blockIdx.x % Hkv;
   // (8-bit cache) scales [2][num_blocks][Hkv][16] fp32: this wave's K or V
