@@ -353,14 +353,27 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
   mark(PKV_PHASE_PLAN, 1);
 
   const float scale_log2 = scale * 1.4426950408889634f;
-  mark(PKV_PHASE_PREFILL, 0);
-  // With `overlap` (8-bit caches, no phase events) the prefill kernel runs on
-  // the side stream while the row kernels run on the caller's; the caller's
-  // stream waits for both at the end.
-  Fork fork;
+  // The kernels after the plan, as launchers on a stream.  Staging (a no-op
+  // unless the plan staged this step) dequantises the prefill blocks; of the
+  // two prefill launches of a staged call only the one the plan picked runs.
   const bool prefill_mfma = pp.mfma_prefill && max_query_len > 1;
-  const hipStream_t ps = prefill_mfma && overlap && fork.begin(s) ? fork.side : s;
-  if (prefill_mfma) {
+  auto stage_on = [&](hipStream_t st) -> int {
+    pkv::StageParams sp{};
+    sp.cache = kv_cache_layer;
+    sp.kv_scales = kv_scales;
+    sp.src = pp.stage_src;
+    sp.staged = wsb + stl.blocks;
+    sp.hdr = hdr;
+    sp.capacity = stl.capacity;
+    sp.num_blocks = num_blocks;
+    sp.num_kv_heads = num_kv_heads;
+    sp.head_dim = head_dim;
+    sp.fp8 = fp8 ? 1 : 0;
+    return pkv::launch_stage(sp, std::min<int64_t>(2 * stl.capacity, (int64_t)cus * 8), st)
+               ? fail(PKV_ERR_LAUNCH, "stage launch failed")
+               : PKV_OK;
+  };
+  auto prefill_on = [&](hipStream_t ps) -> int {
     pkv::PrefillParams fp{};
     fp.out = out;
     fp.q = q;
@@ -381,21 +394,8 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     fp.max_blocks_per_req = max_blocks_per_req;
     const int64_t grid = pf_per_head * num_kv_heads;
     if (stl.capacity > 0) {
-      // staged: the blocks dequantised once, then the bf16 kernel over them
-      // (both no-ops unless the plan staged this step)
-      pkv::StageParams sp{};
-      sp.cache = kv_cache_layer;
-      sp.kv_scales = kv_scales;
-      sp.src = pp.stage_src;
-      sp.staged = wsb + stl.blocks;
-      sp.hdr = hdr;
-      sp.capacity = stl.capacity;
-      sp.num_blocks = num_blocks;
-      sp.num_kv_heads = num_kv_heads;
-      sp.head_dim = head_dim;
-      sp.fp8 = fp8 ? 1 : 0;
-      if (pkv::launch_stage(sp, std::min<int64_t>(2 * stl.capacity, (int64_t)cus * 8), ps))
-        return fail(PKV_ERR_LAUNCH, "stage launch failed");
+      // staged: the bf16 kernel over the staged blocks (a no-op unless the
+      // plan staged this step)
       pkv::PrefillParams sf = fp;
       sf.cache = wsb + stl.blocks;
       sf.kv_scales = nullptr;
@@ -407,54 +407,71 @@ static int attention_impl(void* out, const void* q, const void* kv_cache_layer,
     }
     fp.staged = 0;
     if (pkv::launch_prefill(fp, head_dim, grid, ps)) return fail(PKV_ERR_LAUNCH, "prefill launch failed");
-  }
-
-  mark(PKV_PHASE_PREFILL, 1);
+    return PKV_OK;
+  };
   pkv::RowParams rp{};
-  rp.out = out;
-  rp.q = q;
-  rp.cache = kv_cache_layer;
-  rp.block_table = block_table;
-  rp.qsl = query_start_loc;
-  rp.nct = num_computed_tokens;
-  rp.items = pp.row_items;
-  rp.items_tail = pp.row_items_tail;
-  rp.hdr = hdr;
-  rp.part_o = (float*)(wsb + ws.part_o);
-  rp.part_ml = (float2*)(wsb + ws.part_ml);
-  rp.err = hdr + pkv::kHdrError;
-  rp.scale_log2 = scale_log2;
-  rp.num_q_heads = num_q_heads;
-  rp.num_kv_heads = num_kv_heads;
-  rp.group = group;
-  const int gmax = i8 ? pkv::max_group_regs_i8(dtype) : pkv::max_group_regs(dtype, group, head_dim);
-  rp.head_groups = (group + gmax - 1) / gmax;
-  rp.num_blocks = num_blocks;
-  rp.max_blocks_per_req = max_blocks_per_req;
-  {
-    const int64_t bound_waves = ws.cap_row_items * num_kv_heads * rp.head_groups;
-    mark(PKV_PHASE_ROWS, 0);
-    if (i8 ? pkv::launch_rows_i8(rp, kv_scales, dtype, head_dim, fp8, bound_waves, cus, s)
-           : pkv::launch_rows(rp, dtype, head_dim, bound_waves, cus, s))
-      return fail(PKV_ERR_LAUNCH, "row launch failed");
-    mark(PKV_PHASE_ROWS, 1);
-  }
-  mark(PKV_PHASE_REDUCE, 0);
-  if (max_seq_len > pkv::kSplitTokens) {
-    pkv::ReduceParams rd{};
-    rd.out = out;
-    rd.items = pp.reduce_items;
-    rd.hdr = hdr;
-    rd.part_o = rp.part_o;
-    rd.part_ml = rp.part_ml;
-    rd.num_q_heads = num_q_heads;
-    rd.cap_reduce = ws.cap_reduce;
-    // (a workgroup per (long row, head) at most; short rows need a quarter of that)
-    const int64_t bound = ws.cap_reduce * num_q_heads;
-    const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 8);
-    if (pkv::launch_reduce(rd, dtype, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "reduce launch failed");
-  }
-  mark(PKV_PHASE_REDUCE, 1);
+  auto rows_and_merge = [&]() -> int {
+    rp.out = out;
+    rp.q = q;
+    rp.cache = kv_cache_layer;
+    rp.block_table = block_table;
+    rp.qsl = query_start_loc;
+    rp.nct = num_computed_tokens;
+    rp.items = pp.row_items;
+    rp.items_tail = pp.row_items_tail;
+    rp.hdr = hdr;
+    rp.part_o = (float*)(wsb + ws.part_o);
+    rp.part_ml = (float2*)(wsb + ws.part_ml);
+    rp.err = hdr + pkv::kHdrError;
+    rp.scale_log2 = scale_log2;
+    rp.num_q_heads = num_q_heads;
+    rp.num_kv_heads = num_kv_heads;
+    rp.group = group;
+    const int gmax = i8 ? pkv::max_group_regs_i8(dtype) : pkv::max_group_regs(dtype, group, head_dim);
+    rp.head_groups = (group + gmax - 1) / gmax;
+    rp.num_blocks = num_blocks;
+    rp.max_blocks_per_req = max_blocks_per_req;
+    {
+      const int64_t bound_waves = ws.cap_row_items * num_kv_heads * rp.head_groups;
+      mark(PKV_PHASE_ROWS, 0);
+      if (i8 ? pkv::launch_rows_i8(rp, kv_scales, dtype, head_dim, fp8, bound_waves, cus, s)
+             : pkv::launch_rows(rp, dtype, head_dim, bound_waves, cus, s))
+        return fail(PKV_ERR_LAUNCH, "row launch failed");
+      mark(PKV_PHASE_ROWS, 1);
+    }
+    mark(PKV_PHASE_REDUCE, 0);
+    if (max_seq_len > pkv::kSplitTokens) {
+      pkv::ReduceParams rd{};
+      rd.out = out;
+      rd.items = pp.reduce_items;
+      rd.hdr = hdr;
+      rd.part_o = rp.part_o;
+      rd.part_ml = rp.part_ml;
+      rd.num_q_heads = num_q_heads;
+      rd.cap_reduce = ws.cap_reduce;
+      // (a workgroup per (long row, head) at most; short rows need a quarter of that)
+      const int64_t bound = ws.cap_reduce * num_q_heads;
+      const int64_t grid = std::min<int64_t>(bound, (int64_t)cus * 8);
+      if (pkv::launch_reduce(rd, dtype, head_dim, grid, s)) return fail(PKV_ERR_LAUNCH, "reduce launch failed");
+    }
+    mark(PKV_PHASE_REDUCE, 1);
+    return PKV_OK;
+  };
+  // With `overlap` (8-bit caches, no phase events) and no staging area the
+  // prefill kernel (dequantising its tiles) runs on a second stream beside
+  // the row kernels, which take the CUs its last workgroups leave free; the
+  // caller's stream waits for it at the end (Fork).  With a staging area the
+  // step runs in order on the caller's stream: the bf16 prefill beside the
+  // rows measured no faster than after them (as with a bf16 cache), and the
+  // staging kernel beside the FP8 row kernel slowed it.
+  Fork fork;
+  int rc = PKV_OK;
+  mark(PKV_PHASE_PREFILL, 0);
+  if (prefill_mfma && stl.capacity > 0 && (rc = stage_on(s)) != PKV_OK) return rc;
+  const hipStream_t ps = prefill_mfma && overlap && stl.capacity == 0 && fork.begin(s) ? fork.side : s;
+  if (prefill_mfma && (rc = prefill_on(ps)) != PKV_OK) return rc;
+  mark(PKV_PHASE_PREFILL, 1);
+  if ((rc = rows_and_merge()) != PKV_OK) return rc;
   if (fork.join()) return fail(PKV_ERR_LAUNCH, "joining the prefill stream failed");
   return ok();
 }
