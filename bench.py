@@ -538,7 +538,8 @@ def main():
         tf = acct["prefill_flops"] / (phase_ms["prefill"] * 1e-3) / 1e12
         roof_pf = {
             "kernel": "prefill_kernel (chunked prefill on bf16 MFMA"
-                      + (f", {kv8} cache dequantised in LDS)" if kv8 else ")"),
+                      + ((f", {kv8} cache dequantised once into a bf16 staging area; the phase includes the "
+                          "staging kernel)" if stage_blocks else f", {kv8} cache dequantised in LDS)") if kv8 else ")"),
             "bound": "mfma",
             "achieved": round(tf, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,

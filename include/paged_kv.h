@@ -310,12 +310,13 @@ int paged_kv_write_rope(void* q, const void* k, const void* v, const int64_t* po
  *   forms in LDS, so results are the same bit for bit) and the prefill reads
  *   the staged blocks instead of dequantising every tile it streams.  With no
  *   extra workspace, or a step that does not fit, nothing changes.
- *   phase_events as for paged_attention_profiled, or NULL.  With NULL the
- *   prefill kernel of a step that has prefill chunks runs on a library stream
- *   beside `stream` (which waits for it through events created and released
- *   by the call, so `stream` still orders everything): the row kernels take
- *   the CUs that the prefill's last workgroups leave free.  With phase events
- *   every kernel runs on `stream`, one after the other.
+ *   phase_events as for paged_attention_profiled, or NULL.  With NULL and
+ *   no staging area, the prefill kernel of a step that has prefill chunks
+ *   runs on a library stream beside `stream` (which waits for it through
+ *   events created and released by the call, so `stream` still orders
+ *   everything): the row kernels take the CUs that the prefill's last
+ *   workgroups leave free.  With a staging area, or with phase events, every
+ *   kernel runs on `stream`, one after the other.
  * Other arguments, the workspace and the error conventions are those of
  * paged_kv_write / paged_attention.
  */
