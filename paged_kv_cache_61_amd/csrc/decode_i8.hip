@@ -353,7 +353,16 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void row_attn_i8_mfma_kernel
   const size_t scale_half = (size_t)a.num_blocks * kBlock * a.num_kv_heads;
   const float sl2 = a.scale_log2;
 
-  for (int64_t it = (int64_t)blockIdx.x * 4 + w; it < total; it += (int64_t)gridDim.x * 4) {
+  // Round k of a wave takes item k*NW + gw, or k*NW + NW-1-gw in odd rounds
+  // (NW waves, gw this wave's index; items are listed longest first), so a
+  // wave that drew a long item in one round draws a short one in the next.
+  // (Requesting the next item's descriptor and block ids while streaming the
+  // current item, as the bf16 MFMA row kernel does, measured slower here.)
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + w;
+  for (int64_t k = 0;; ++k) {
+    const int64_t it = k * nw + ((k & 1) ? nw - 1 - gw : gw);
+    if (it >= total) break;
     const ItemI8 cur = fetch_item_i8(a, it, per_pair, n_head, 16);
     const size_t out_row = ((size_t)cur.t * a.num_q_heads + cur.h0) * D;
     if (cur.part == kNanRow) {
