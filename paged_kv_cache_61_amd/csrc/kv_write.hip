@@ -10,6 +10,8 @@
 // One thread moves one 16-byte chunk; consecutive threads move consecutive
 // chunks of a token row, so both the read of k/v and the write into the
 // cache are fully coalesced.  The copy is bit-exact.
+#include <algorithm>
+
 #include "pkv_common.h"
 #include "pkv_internal.h"
 
@@ -179,60 +181,95 @@ PKV_DEV uint32_t e4m3_code(float y) {
 //         [-127, 127];
 //   FP8:  scale = max|x| / 448, code = e4m3_code(x / scale);
 // an all-zero row gets scale 0 and codes 0.  Both divisions are IEEE float32
-// so the codes are reproducible.  One wave per row: each lane holds
-// head_dim / 64 values, the row max is a wave reduction, lane 0 stores the
+// so the codes are reproducible.  A row is spread over D/8 lanes, 8 values
+// each (one 16-byte load of bf16), so a wave holds a set of 64/(D/8) rows;
+// wave w of NW takes row sets w, w + NW, ... (up to kI8WPasses of them per
+// round) and issues all their loads before the first quantisation.  The row
+// max is a reduction over the row's lanes; the row's first lane stores the
 // scale.
+constexpr int kI8WPasses = 4;
+
+// max over aligned groups of N lanes (N = 8 or 16)
+template <int N>
+PKV_DEV float group_max(float x) {
+#pragma unroll
+  for (int m = 1; m < N; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, N));
+  return x;
+}
+
 template <bool BF16, int D, bool FP8>
 __global__ __launch_bounds__(256) void kv_write_i8_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                           const int64_t* __restrict__ slot_mapping,
                                                           int8_t* __restrict__ cache, float* __restrict__ scales,
                                                           int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
                                                           int32_t* __restrict__ device_error) {
-  constexpr int E = D / kWave;  // values per lane
+  constexpr int VPL = 8;               // values per lane
+  constexpr int LPR = D / VPL;         // lanes per row
+  constexpr int RPW = kWave / LPR;     // rows per wave and pass
+  static_assert(LPR == 8 || LPR == 16, "head_dim 64 or 128");
   const int lane = threadIdx.x & (kWave - 1);
+  const int sub = lane / LPR, li = lane % LPR;
   const int64_t rows = num_tokens * 2 * num_kv_heads;
   const int64_t num_slots = (int64_t)num_blocks * kBlock;
-  for (int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave; row < rows;
-       row += (int64_t)gridDim.x * blockDim.x / kWave) {
-    const int64_t t = row / (2 * num_kv_heads);
-    const int rem = (int)(row - t * 2 * num_kv_heads);
-    const int kv = rem / num_kv_heads, h = rem - kv * num_kv_heads;
-    const int64_t slot = slot_mapping[t];
-    if (slot == -1) continue;
-    if (slot < 0 || slot >= num_slots) {
-      if (device_error != nullptr && lane == 0 && kv == 0 && h == 0) atomicOr(device_error, PKV_DEVERR_SLOT);
-      continue;
-    }
-    const size_t src = ((size_t)t * num_kv_heads + h) * D + lane * E;
-    float x[E];
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  const int64_t sets = (rows + RPW - 1) / RPW;
+  for (int64_t base = wave; base < sets; base += nwaves * kI8WPasses) {
+    float x[kI8WPasses][VPL];
+    int64_t slot[kI8WPasses];
+    int kvh[kI8WPasses];   // kv * num_kv_heads + h
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if constexpr (BF16)
-        x[e] = __uint_as_float((uint32_t)((const uint16_t*)(kv ? v : k))[src + e] << 16);
-      else
-        x[e] = ((const float*)(kv ? v : k))[src + e];
-    }
-    float amax = 0.f;
+    for (int u = 0; u < kI8WPasses; ++u) {
+      const int64_t row = (base + u * nwaves) * RPW + sub;
+      const bool in = row < rows;
+      const int64_t t = in ? row / (2 * num_kv_heads) : 0;
+      kvh[u] = in ? (int)(row - t * 2 * num_kv_heads) : 0;
+      const int kv = kvh[u] / num_kv_heads, h = kvh[u] - kv * num_kv_heads;
+      slot[u] = in ? slot_mapping[t] : -1;
+      const size_t src = ((size_t)t * num_kv_heads + h) * D + li * VPL;
+      if constexpr (BF16) {
+        const u32x4 w = in ? *(const u32x4*)((const uint16_t*)(kv ? v : k) + src) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    amax = wave_max(amax);
-    const float scale = amax / (FP8 ? 448.f : 127.f);
-    int8_t c[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if constexpr (FP8)
-        c[e] = scale > 0.f ? (int8_t)e4m3_code(x[e] / scale) : 0;
-      else
-        c[e] = scale > 0.f ? (int8_t)fminf(fmaxf(rintf(x[e] / scale), -127.f), 127.f) : 0;
+        for (int e = 0; e < 4; ++e) {
+          x[u][2 * e] = __uint_as_float(w[e] << 16);
+          x[u][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+        const float* f = (const float*)(kv ? v : k) + src;
+        const float4 w0 = in ? *(const float4*)f : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 w1 = in ? *(const float4*)(f + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[u][0] = w0.x; x[u][1] = w0.y; x[u][2] = w0.z; x[u][3] = w0.w;
+        x[u][4] = w1.x; x[u][5] = w1.y; x[u][6] = w1.z; x[u][7] = w1.w;
+      }
     }
-    int8_t* dst = cache + ((size_t)kv * num_slots + slot) * num_kv_heads * D + (size_t)h * D + lane * E;
-    if constexpr (E == 2)
-      *(uint16_t*)dst = (uint16_t)((uint8_t)c[0] | ((uint16_t)(uint8_t)c[1] << 8));
-    else
-      dst[0] = c[0];
-    // scales [2][num_blocks][num_kv_heads][16]: a head's 16 scales of a block are contiguous
-    if (lane == 0)
-      scales[(((size_t)kv * num_blocks + slot / kBlock) * num_kv_heads + h) * kBlock + slot % kBlock] = scale;
+#pragma unroll
+    for (int u = 0; u < kI8WPasses; ++u) {
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
+      amax = group_max<LPR>(amax);
+      const int64_t sl = slot[u];
+      if (sl == -1) continue;
+      const int kv = kvh[u] / num_kv_heads, h = kvh[u] - kv * num_kv_heads;
+      if (sl < 0 || sl >= num_slots) {
+        if (device_error != nullptr && li == 0 && kvh[u] == 0) atomicOr(device_error, PKV_DEVERR_SLOT);
+        continue;
+      }
+      const float scale = amax / (FP8 ? 448.f : 127.f);
+      uint32_t c[VPL];
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) {
+        if constexpr (FP8)
+          c[e] = scale > 0.f ? e4m3_code(x[u][e] / scale) : 0u;
+        else
+          c[e] = scale > 0.f ? (uint32_t)(uint8_t)(int8_t)fminf(fmaxf(rintf(x[u][e] / scale), -127.f), 127.f) : 0u;
+      }
+      int8_t* dst = cache + ((size_t)kv * num_slots + sl) * num_kv_heads * D + (size_t)h * D + li * VPL;
+      *(u32x2*)dst = u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+      // scales [2][num_blocks][num_kv_heads][16]: a head's 16 scales of a block are contiguous
+      if (li == 0)
+        scales[(((size_t)kv * num_blocks + sl / kBlock) * num_kv_heads + h) * kBlock + sl % kBlock] = scale;
+    }
   }
 }
 
@@ -241,7 +278,11 @@ int launch_kv_write_i8(const void* k, const void* v, const int64_t* slot_mapping
                        bool fp8, int32_t* device_error, hipStream_t stream) {
   if (num_tokens == 0) return 0;
   const int64_t rows = num_tokens * 2 * num_kv_heads;
-  int64_t grid = (rows + 3) / 4;
+  // enough waves for kI8WPasses row sets each, and at least 2048 (a round
+  // over the whole chip) when there are that many sets
+  const int64_t sets = (rows + kWave / (head_dim / 8) - 1) / (kWave / (head_dim / 8));
+  const int64_t waves = std::max((sets + kI8WPasses - 1) / kI8WPasses, std::min<int64_t>(sets, 2048));
+  int64_t grid = (waves + 3) / 4;   // 4 waves per 256-thread workgroup
   if (grid > 65536) grid = 65536;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, k, v, slot_mapping, (int8_t*)cache,
