@@ -146,6 +146,47 @@ def test_int8_write_zero_rows_and_padding():
     assert rs[0, 1, 1].tolist() == [0.0, 0.0]
 
 
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+@pytest.mark.parametrize("dtype,D,Hkv,T", [("bf16", 64, 3, 37), ("bf16", 128, 3, 1000), ("f32", 128, 1, 7),
+                                           ("f32", 64, 5, 513)])
+def test_8bit_write_ragged_rows_and_bad_slots(fmt, dtype, D, Hkv, T):
+    # the write kernel spreads a row over head_dim/8 lanes and takes row sets
+    # of 64/(head_dim/8) rows, several per wave: row counts that leave the
+    # last set partly empty, a padding token and two out-of-range slots (not
+    # written, reported), everything else bit for bit as the oracle
+    _gpu()
+    import paged_kv_cache_61_amd as pkv
+    NB = (T + 15) // 16 + 3
+    print(f"[case] 8-bit write {fmt} {dtype} D={D} Hkv={Hkv} T={T}", flush=True)
+    g = torch.Generator().manual_seed(T * 7 + D)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kt = torch.randn((T, Hkv, D), generator=g).to(tdt)
+    vt = torch.randn((T, Hkv, D), generator=g).to(tdt)
+    k, v = kt.float().numpy(), vt.float().numpy()   # the stored values, exactly
+    rng = np.random.default_rng(T + D)
+    slots = rng.permutation(NB * 16)[:T].astype(np.int64)
+    slots[T // 2] = -1                               # padding token
+    bad = [T - 1, 0] if T > 2 else [T - 1]
+    slots[bad[0]] = NB * 16 + 5                      # past the pool
+    if len(bad) > 1:
+        slots[bad[1]] = -7                           # negative, not -1
+    cdt = np.int8 if fmt == "int8" else np.uint8
+    codes = np.full((2, NB, 16, Hkv, D), 7, cdt)
+    scales = np.full((2, NB, 16, Hkv), 5.0, np.float32)
+    d_codes, d_scales = torch.from_numpy(codes).cuda(), scales_to_dev(scales)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    write = pkv.paged_kv_write_int8 if fmt == "int8" else pkv.paged_kv_write_fp8
+    write(kt.cuda(), vt.cuda(), torch.from_numpy(slots).cuda(), d_codes, d_scales, device_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & pkv.DEVERR_SLOT
+    ok_slots = slots.copy()
+    ok_slots[bad] = -1                               # the oracle skips them
+    quant = oracle.kv_write_int8 if fmt == "int8" else oracle.kv_write_fp8
+    rc, rs = quant(codes, scales, k, v, ok_slots, "f32")
+    assert np.array_equal(d_codes.cpu().numpy(), rc)
+    assert scales_from_dev(d_scales).tobytes() == rs.tobytes()
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("n,all_rows", [(2, True), (4, False), (5, True)])
 def test_int8_workload_full_size(n, all_rows):
